@@ -1,0 +1,231 @@
+/*
+ * latentmoe_oracle.c -- plain fp64 CPU reference of the LatentMoE layer forward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load or call this file.  It shares no code,
+ * header, table or helper with the HIP library, and the HIP library never
+ * calls it.
+ *
+ * What it computes (one token at a time, in the order the pages give):
+ *   1. z = W_down x: the token of width d is projected to the latent width l
+ *      (qingkeai.online LatentMoE article, section "LatentMoE 具体怎么做",
+ *      first bullet; zhichai.net "LatentMoE: How MoE Made a Key Paradigm Leap
+ *      in 2026", section 2, step 1; 10100.com article section 2.2, Figure 3b).
+ *   2. Router logits from x at the full width d: the gate is one of the parts
+ *      that stay at d (qingkeai.online article, closing paragraph of
+ *      "LatentMoE 具体怎么做"; zhichai.net section 2, last paragraph).  Other
+ *      sentences of the same pages say routing happens in l; the full-d
+ *      reading is the one taken here.
+ *   3. Softmax over all N logits, keep the K largest (ties: lower expert index
+ *      first), renormalise the kept probabilities to sum 1.  The pages name
+ *      top-K counts (512/top-22, 896/top-16: zhichai.net section 4) but not
+ *      the gate function; this is the reading taken.
+ *   4. Each selected expert runs in the latent space: h = W1[e] z,
+ *      a = max(h, 0)^2, y = W2[e] a; its weights are l x m instead of d x m
+ *      (qingkeai.online article, "LatentMoE 具体怎么做", second bullet and the
+ *      paragraph after it).  The squared-ReLU activation is a reading: the
+ *      pages do not name one.
+ *   5. s = sum_k g_k y_k in rank order, aggregated in l before projecting back
+ *      (10100.com article section 2.2: aggregate, then up-project).
+ *   6. out = x + W_up s (third bullet of the same qingkeai.online section).
+ *      The residual add is a reading: the pages do not state one.
+ * Standard mode (no projections, l == d): z = x and out = x + s, the plain
+ * MoE of 10100.com Figure 3a.
+ *
+ * Storage (row-major; the reduction index is the fastest one):
+ *   x [T,d]  W_down [l,d]  W_router [N,d]  W1 [N,m,l]  W2 [N,l,m]  W_up [d,l]
+ *   bias [N] float32 or NULL.
+ * Element type of x and the weights: float32 (dtype 0) or bfloat16 bit
+ * patterns (dtype 1).  Each element is widened to double at use; every sum is
+ * accumulated in double in index order.
+ *
+ * Parity pins: see tests/test_oracle_pins.py.  Every output here is pinned by
+ * at least one check that does not re-run this code's formulas: brute-force
+ * subset enumeration for the routing, numpy float64 matmuls for the dense
+ * reductions, identity and zero-weight special cases, and exact scalings.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+typedef struct {
+    int32_t T, d, l, N, K, m;
+    int32_t dtype;    /* 0: float32 arrays, 1: bfloat16 bit patterns */
+    int32_t standard; /* 1: no projections (requires l == d) */
+} oracle_dims;
+
+static double widen(const void* base, int dtype, size_t i) {
+    if (dtype == 0) return (double)((const float*)base)[i];
+    uint32_t bits = ((uint32_t)((const uint16_t*)base)[i]) << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/* logit order: a outranks b if its logit is larger, or equal with a lower index */
+static int outranks(const double* logit, int a, int b) {
+    return logit[a] > logit[b] || (logit[a] == logit[b] && a < b);
+}
+
+/*
+ * One token.  `forced` (K ids or NULL) replaces the token's own selection:
+ * used when a caller wants this token evaluated with another routing (the
+ * gates still come from this token's own fp64 logits).
+ */
+static void one_token(const oracle_dims* D, int t, const void* x, const void* Wd,
+                      const void* Wr, const void* W1, const void* W2, const void* Wu,
+                      const float* bias, const int32_t* forced, double* out_t,
+                      int32_t* ids_t, double* gates_t, double* logits_t, double* gap_t,
+                      double* work) {
+    const int d = D->d, l = D->l, N = D->N, K = D->K, m = D->m, dt = D->dtype;
+    double* xt = work;            /* [d] */
+    double* z = xt + d;           /* [l] */
+    double* p = z + l;            /* [N] */
+    double* h = p + N;            /* [m] */
+    double* s = h + m;            /* [l] */
+    char* chosen = (char*)(s + l);/* [N] */
+
+    for (int i = 0; i < d; ++i) xt[i] = widen(x, dt, (size_t)t * d + i);
+
+    /* step 1: z = W_down x */
+    if (D->standard) {
+        for (int i = 0; i < l; ++i) z[i] = xt[i];
+    } else {
+        for (int j = 0; j < l; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < d; ++i) acc += widen(Wd, dt, (size_t)j * d + i) * xt[i];
+            z[j] = acc;
+        }
+    }
+
+    /* step 2: router logits at full d */
+    for (int e = 0; e < N; ++e) {
+        double acc = 0.0;
+        for (int i = 0; i < d; ++i) acc += widen(Wr, dt, (size_t)e * d + i) * xt[i];
+        if (bias) acc += (double)bias[e];
+        logits_t[e] = acc;
+    }
+
+    /* step 3a: softmax over all N, max subtracted */
+    double mx = logits_t[0];
+    for (int e = 1; e < N; ++e) if (logits_t[e] > mx) mx = logits_t[e];
+    double den = 0.0;
+    for (int e = 0; e < N; ++e) { p[e] = exp(logits_t[e] - mx); den += p[e]; }
+    for (int e = 0; e < N; ++e) p[e] /= den;
+
+    /* step 3b: the K best experts in rank order (largest logit, then lowest index) */
+    memset(chosen, 0, (size_t)N);
+    for (int k = 0; k < K; ++k) {
+        int best = -1;
+        for (int e = 0; e < N; ++e)
+            if (!chosen[e] && (best < 0 || outranks(logits_t, e, best))) best = e;
+        chosen[best] = 1;
+        ids_t[k] = best;
+    }
+    if (K < N) {
+        int next = -1;
+        for (int e = 0; e < N; ++e)
+            if (!chosen[e] && (next < 0 || outranks(logits_t, e, next))) next = e;
+        *gap_t = logits_t[ids_t[K - 1]] - logits_t[next];
+    } else {
+        *gap_t = INFINITY;
+    }
+    if (forced) for (int k = 0; k < K; ++k) ids_t[k] = forced[k];
+
+    /* step 3c: renormalise the kept probabilities */
+    double kept = 0.0;
+    for (int k = 0; k < K; ++k) kept += p[ids_t[k]];
+    for (int k = 0; k < K; ++k) gates_t[k] = p[ids_t[k]] / kept;
+
+    /* steps 4-5: experts in latent space, gate-weighted sum in rank order */
+    for (int i = 0; i < l; ++i) s[i] = 0.0;
+    for (int k = 0; k < K; ++k) {
+        const size_t e = (size_t)ids_t[k];
+        for (int j = 0; j < m; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < l; ++i) acc += widen(W1, dt, (e * m + j) * l + i) * z[i];
+            double a = acc > 0.0 ? acc : 0.0;
+            h[j] = a * a;
+        }
+        for (int i = 0; i < l; ++i) {
+            double acc = 0.0;
+            for (int j = 0; j < m; ++j) acc += widen(W2, dt, (e * l + i) * m + j) * h[j];
+            s[i] += gates_t[k] * acc;
+        }
+    }
+
+    /* step 6: project back to d and add the residual */
+    for (int n = 0; n < d; ++n) {
+        double acc;
+        if (D->standard) {
+            acc = s[n];
+        } else {
+            acc = 0.0;
+            for (int i = 0; i < l; ++i) acc += widen(Wu, dt, (size_t)n * l + i) * s[i];
+        }
+        out_t[n] = xt[n] + acc;
+    }
+}
+
+/*
+ * oracle_forward: evaluate `n_sel` tokens (token indices in `sel`, or the
+ * first n_sel tokens when sel is NULL).  Outputs are indexed by position in
+ * the selection:  out [n_sel,d]  ids [n_sel,K]  gates [n_sel,K]
+ * logits [n_sel,N]  gap [n_sel]  (gap = K-th minus (K+1)-th largest logit).
+ * forced_ids [n_sel,K] or NULL.  Returns 0, or -1 on bad arguments.
+ */
+int oracle_forward(const oracle_dims* D, const void* x, const void* Wd, const void* Wr,
+                   const void* W1, const void* W2, const void* Wu, const float* bias,
+                   const int32_t* sel, int32_t n_sel, const int32_t* forced_ids,
+                   double* out, int32_t* ids, double* gates, double* logits, double* gap) {
+    if (!D || !x || !Wr || !W1 || !W2 || !out || !ids || !gates || !logits || !gap) return -1;
+    if (D->K < 1 || D->K > D->N || D->T < 0 || n_sel < 0) return -1;
+    if (D->standard ? (D->l != D->d) : (!Wd || !Wu)) return -1;
+    for (int q = 0; q < n_sel; ++q) {
+        int t = sel ? sel[q] : q;
+        if (t < 0 || t >= D->T) return -1;
+    }
+    const size_t work_doubles = (size_t)D->d + 2 * (size_t)D->l + D->N + D->m + (D->N + 7) / 8 + 1;
+    int bad = 0;
+#pragma omp parallel
+    {
+        double* work = (double*)malloc(work_doubles * sizeof(double));
+        if (!work) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int q = 0; q < n_sel; ++q) {
+                int t = sel ? sel[q] : q;
+                one_token(D, t, x, Wd, Wr, W1, W2, Wu, bias,
+                          forced_ids ? forced_ids + (size_t)q * D->K : NULL,
+                          out + (size_t)q * D->d, ids + (size_t)q * D->K,
+                          gates + (size_t)q * D->K, logits + (size_t)q * D->N, gap + q, work);
+            }
+            free(work);
+        }
+    }
+    return bad ? -1 : 0;
+}
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* number of threads the next oracle_forward call will use */
+int oracle_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}

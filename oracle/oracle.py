@@ -1,0 +1,134 @@
+"""Python access to the fp64 CPU oracle of the LatentMoE layer forward.
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the
+benchmark's CPU-baseline leg are the only callers.  Nothing here imports the
+HIP library or its package, and the HIP library never calls this.
+
+`build()` compiles latentmoe_oracle.c with gcc (OpenMP, no fast-math, no FP
+contraction, so every sum is the plain double-precision sum in index order).
+`forward()` runs it on numpy arrays holding the exact values the GPU gets
+(float32, or bfloat16 bit patterns as uint16).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "latentmoe_oracle.c")
+LIB = os.path.join(HERE, "liblatentmoe_oracle.so")
+
+CFLAGS = ["-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared", "-std=c11"]
+
+
+class _Dims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("T", "d", "l", "N", "K", "m", "dtype", "standard")]
+
+
+def build(src: str = SRC, out: str = LIB, extra: Sequence[str] = ()) -> str:
+    """Compile the oracle (or a variant source) into a shared library."""
+    cmd = ["gcc", *CFLAGS, *extra, src, "-o", out + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+class Oracle:
+    """Handle on one compiled oracle library."""
+
+    def __init__(self, path: str = LIB):
+        if not os.path.exists(path):
+            build(out=path) if path == LIB else None
+        self.lib = ctypes.CDLL(path)
+        f = self.lib.oracle_forward
+        f.restype = ctypes.c_int
+        P = ctypes.c_void_p
+        f.argtypes = [ctypes.POINTER(_Dims), P, P, P, P, P, P, P, P, ctypes.c_int32, P, P, P, P, P, P]
+        self.lib.oracle_threads.restype = ctypes.c_int
+        self.lib.oracle_set_threads.argtypes = [ctypes.c_int]
+
+    def threads(self) -> int:
+        return int(self.lib.oracle_threads())
+
+    def set_threads(self, n: int) -> None:
+        self.lib.oracle_set_threads(int(n))
+
+    def forward(self, x, W_down, W_router, W1, W2, W_up, K: int, *, bias=None,
+                standard: bool = False, sel: Optional[Sequence[int]] = None,
+                forced_ids=None):
+        """Evaluate the layer for the tokens in `sel` (all tokens if None).
+
+        Arrays: numpy float32, or uint16 holding bfloat16 bits, in the
+        storage layout x [T,d], W_down [l,d], W_router [N,d], W1 [N,m,l],
+        W2 [N,l,m], W_up [d,l]; bias float32 [N] or None.
+        Returns dict(out [n,d] f64, ids [n,K] i32, gates [n,K] f64,
+        logits [n,N] f64, gap [n] f64).
+        """
+        x = np.ascontiguousarray(x)
+        dtype = 0 if x.dtype == np.float32 else 1
+        if dtype == 1 and x.dtype != np.uint16:
+            raise TypeError("x must be float32 or uint16 (bf16 bits)")
+        T, d = x.shape
+        N = W_router.shape[0]
+        m = W1.shape[1]
+        l = W1.shape[2]
+        arrs = [x, W_down, W_router, W1, W2, W_up]
+        for a in arrs:
+            if a is not None and a.dtype != x.dtype:
+                raise TypeError("all of x and the weights must share one dtype")
+        arrs = [None if a is None else np.ascontiguousarray(a) for a in arrs]
+        x, W_down, W_router, W1, W2, W_up = arrs
+        if bias is not None:
+            bias = np.ascontiguousarray(bias, dtype=np.float32)
+        if sel is None:
+            sel_arr = None
+            n = T
+        else:
+            sel_arr = np.ascontiguousarray(np.asarray(sel, dtype=np.int32))
+            n = int(sel_arr.shape[0])
+        if forced_ids is not None:
+            forced_ids = np.ascontiguousarray(np.asarray(forced_ids, dtype=np.int32))
+            assert forced_ids.shape == (n, K)
+        D = _Dims(T, d, l, N, K, m, dtype, 1 if standard else 0)
+        out = np.empty((n, d), np.float64)
+        ids = np.empty((n, K), np.int32)
+        gates = np.empty((n, K), np.float64)
+        logits = np.empty((n, N), np.float64)
+        gap = np.empty((n,), np.float64)
+
+        def p(a):
+            return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+        rc = self.lib.oracle_forward(ctypes.byref(D), p(x), p(W_down), p(W_router), p(W1), p(W2),
+                                     p(W_up), p(bias), p(sel_arr), n, p(forced_ids),
+                                     p(out), p(ids), p(gates), p(logits), p(gap))
+        if rc != 0:
+            raise ValueError("oracle_forward rejected its arguments")
+        return {"out": out, "ids": ids, "gates": gates, "logits": logits, "gap": gap}
+
+
+_default: Optional[Oracle] = None
+
+
+def default() -> Oracle:
+    global _default
+    if _default is None:
+        if not os.path.exists(LIB):
+            build()
+        _default = Oracle(LIB)
+    return _default
+
+
+def forward(*args, **kw):
+    return default().forward(*args, **kw)
+
+
+def bf16_bits_to_f64(a: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns (uint16) or float32 to float64, exactly."""
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)

@@ -1,0 +1,142 @@
+"""Seeded synthetic inputs for the LatentMoE layer forward.
+
+This module is shared by the HIP path's tests and benchmark and by the
+oracle's tests.  It only draws random numbers and casts them; it holds none
+of the layer's arithmetic.
+
+Shapes follow the pages' workloads:
+  * Nemotron 3 Super: 512 experts, top-22, latent width l = 1024 = d/4
+    (zhichai.net "LatentMoE: How MoE Made a Key Paradigm Leap in 2026",
+    section 4 "Two Teams, Two Practices").
+  * The Table-1 comparison: a standard MoE with d = 4096, 128 experts, top-6
+    against a LatentMoE with l = 1024, 512 experts, top-22 (10100.com article,
+    section 2.3 "评估", Table 1).
+  * Kimi K3: 896 experts, top-16 (same zhichai.net page, section 4).
+The expert width m and, for the Kimi-like shape, l are not on the pages; the
+values below are choices of this library's workload set.
+
+Storage layout (chosen for MFMA: the reduction index is contiguous for both
+operands of every product):
+  x        [T, d]
+  W_down   [l, d]        z_j   = sum_i W_down[j, i] x_i
+  W_router [N, d]        logit_e = sum_i W_router[e, i] x_i (+ bias_e)
+  W1       [N, m, l]     h_j   = sum_i W1[e, j, i] z_i
+  W2       [N, l, m]     y_i   = sum_j W2[e, i, j] a_j
+  W_up     [d, l]        out_n = x_n + sum_i W_up[n, i] s_i
+  bias     [N] float32 (skewed workload only)
+
+Recipe: one CPU torch.Generator seeded with `seed`; draws in the order x,
+W_down, W_router, W1 (one draw of [m, l] per expert, expert 0 first), W2 (one
+[l, m] draw per expert), W_up, bias.  Every draw is float32 N(0, 1); weights
+are multiplied by 1/sqrt(fan_in) in float32; for bf16 workloads every array
+except the bias is then rounded to bfloat16 (round-to-nearest-even).
+x ~ N(0, 1) throughout, so routing is near uniform except where the fixed
+logit bias ~ N(0, 1) skews the expert loads.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, Optional
+
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    T: int
+    d: int
+    l: int
+    N: int
+    K: int
+    m: int
+    dtype: str            # "f32" or "bf16"
+    standard: bool = False  # no projections: l == d, z = x, out = x + s
+    bias: bool = False      # fixed per-expert logit bias ~ N(0, 1)
+
+    def replace(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+    @property
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+    @property
+    def elem_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+
+# The five workloads (the standard-MoE one at two token counts).
+WORKLOADS: Dict[str, Workload] = {
+    "tiny_f32": Workload("tiny_f32", T=64, d=256, l=64, N=32, K=4, m=128, dtype="f32"),
+    "decode": Workload("decode", T=32, d=4096, l=1024, N=512, K=22, m=768, dtype="bf16"),
+    "prefill": Workload("prefill", T=16384, d=4096, l=1024, N=512, K=22, m=768, dtype="bf16"),
+    "standard_decode": Workload("standard_decode", T=32, d=4096, l=4096, N=128, K=6, m=768,
+                                dtype="bf16", standard=True),
+    "standard_prefill": Workload("standard_prefill", T=16384, d=4096, l=4096, N=128, K=6, m=768,
+                                 dtype="bf16", standard=True),
+    "skewed": Workload("skewed", T=8192, d=7168, l=1792, N=896, K=16, m=512, dtype="bf16",
+                       bias=True),
+}
+
+
+def _draw(gen: torch.Generator, shape, scale: Optional[float]) -> torch.Tensor:
+    t = torch.randn(*shape, generator=gen, dtype=torch.float32)
+    if scale is not None:
+        t.mul_(scale)
+    return t
+
+
+def make_inputs(w: Workload, seed: int = 0, *, x_only_seed: Optional[int] = None) -> Dict[str, torch.Tensor]:
+    """Draw the inputs of workload `w` on the CPU.
+
+    Returns a dict with keys x, W_down, W_router, W1, W2, W_up, bias (None
+    where the workload has no such array).  Arrays are contiguous CPU tensors
+    in the workload's storage dtype; bias stays float32.
+    """
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(seed)
+    dt = w.torch_dtype
+    out: Dict[str, Optional[torch.Tensor]] = {}
+    out["x"] = _draw(gen, (w.T, w.d), None).to(dt)
+    if w.standard:
+        out["W_down"] = None
+    else:
+        out["W_down"] = _draw(gen, (w.l, w.d), 1.0 / math.sqrt(w.d)).to(dt)
+    out["W_router"] = _draw(gen, (w.N, w.d), 1.0 / math.sqrt(w.d)).to(dt)
+    W1 = torch.empty((w.N, w.m, w.l), dtype=dt)
+    for e in range(w.N):
+        W1[e] = _draw(gen, (w.m, w.l), 1.0 / math.sqrt(w.l)).to(dt)
+    out["W1"] = W1
+    W2 = torch.empty((w.N, w.l, w.m), dtype=dt)
+    for e in range(w.N):
+        W2[e] = _draw(gen, (w.l, w.m), 1.0 / math.sqrt(w.m)).to(dt)
+    out["W2"] = W2
+    if w.standard:
+        out["W_up"] = None
+    else:
+        out["W_up"] = _draw(gen, (w.d, w.l), 1.0 / math.sqrt(w.l)).to(dt)
+    out["bias"] = _draw(gen, (w.N,), None) if w.bias else None
+    if x_only_seed is not None:
+        g2 = torch.Generator(device="cpu")
+        g2.manual_seed(x_only_seed)
+        out["x"] = _draw(g2, (w.T, w.d), None).to(dt)
+    return out
+
+
+def draw_x(w: Workload, seed: int) -> torch.Tensor:
+    """A fresh batch of tokens x ~ N(0, 1) for workload `w` from its own seed."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(seed)
+    return _draw(gen, (w.T, w.d), None).to(w.torch_dtype)
+
+
+def as_numpy_bits(t: Optional[torch.Tensor]):
+    """CPU tensor -> numpy array holding the same bits (bf16 as uint16)."""
+    if t is None:
+        return None
+    t = t.contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view("uint16")
+    return t.numpy()

@@ -1,0 +1,77 @@
+"""The fp64 oracle against its pins, and every planted mistake against them.
+
+The mutation test copies the oracle's C source into a temporary folder,
+replaces one snippet with a plausible mistake (a dropped term, a wrong sign or
+index, a transposed operand, a wrong tie rule ...), compiles the copy, and
+requires at least one pin to fail on it.
+"""
+import os
+import shutil
+
+import pytest
+
+from oracle import oracle
+from tests import oracle_pins as P
+
+
+@pytest.fixture(scope="module")
+def real():
+    oracle.build()
+    return oracle.Oracle(oracle.LIB)
+
+
+@pytest.mark.parametrize("pin", P.ALL_PINS, ids=lambda f: f.__name__)
+def test_pin_holds(real, pin):
+    pin(real)
+
+
+def test_routing_bruteforce_tiny_workload_shape(real):
+    P.pin_routing_bruteforce_tiny_workload(real)
+
+
+MUTANTS = {
+    "drop_residual": ("out_t[n] = xt[n] + acc;", "out_t[n] = acc;"),
+    "residual_sign": ("out_t[n] = xt[n] + acc;", "out_t[n] = xt[n] - acc;"),
+    "relu_not_squared": ("h[j] = a * a;", "h[j] = a;"),
+    "relu_of_square": ("double a = acc > 0.0 ? acc : 0.0;", "double a = acc;"),
+    "transposed_W_down": ("widen(Wd, dt, (size_t)j * d + i)", "widen(Wd, dt, (size_t)i * l + j)"),
+    "transposed_W1": ("widen(W1, dt, (e * m + j) * l + i)", "widen(W1, dt, e * m * l + (size_t)i * m + j)"),
+    "transposed_W2": ("widen(W2, dt, (e * l + i) * m + j)", "widen(W2, dt, e * l * m + (size_t)j * l + i)"),
+    "transposed_W_up": ("widen(Wu, dt, (size_t)n * l + i)", "widen(Wu, dt, (size_t)i * d + n)"),
+    "router_from_latent": ("acc += widen(Wr, dt, (size_t)e * d + i) * xt[i];",
+                           "acc += widen(Wr, dt, (size_t)e * d + i) * (i < l ? z[i] : 0.0);"),
+    "bias_ignored": ("if (bias) acc += (double)bias[e];", "(void)bias;"),
+    "tie_to_higher_index": ("(logit[a] == logit[b] && a < b)", "(logit[a] == logit[b] && a > b)"),
+    "smallest_k": ("return logit[a] > logit[b] ||", "return logit[a] < logit[b] ||"),
+    "gates_not_renormalised": ("gates_t[k] = p[ids_t[k]] / kept;", "gates_t[k] = p[ids_t[k]];"),
+    "gate_dropped": ("s[i] += gates_t[k] * acc;", "s[i] += acc;"),
+    "gate_wrong_index": ("s[i] += gates_t[k] * acc;", "s[i] += gates_t[0] * acc;"),
+    "kept_sum_drops_first": ("for (int k = 0; k < K; ++k) kept += p[ids_t[k]];",
+                             "for (int k = 1; k < K; ++k) kept += p[ids_t[k]];"),
+    "last_expert_dropped": ("for (int k = 0; k < K; ++k) {\n        const size_t e",
+                            "for (int k = 0; k < K - 1; ++k) {\n        const size_t e"),
+    "softmax_temperature": ("p[e] = exp(logits_t[e] - mx);", "p[e] = exp(2.0 * (logits_t[e] - mx));"),
+    "gap_from_top": ("*gap_t = logits_t[ids_t[K - 1]] - logits_t[next];",
+                     "*gap_t = logits_t[ids_t[0]] - logits_t[next];"),
+    "standard_mode_projects": ("            acc = s[n];\n", "            acc = 0.5 * s[n];\n"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(tmp_path, name):
+    src = open(oracle.SRC).read()
+    old, new = MUTANTS[name]
+    assert src.count(old) == 1, f"snippet for {name} must occur once in the oracle"
+    mpath = os.path.join(tmp_path, "mutant.c")
+    with open(mpath, "w") as f:
+        f.write(src.replace(old, new))
+    lib = oracle.build(src=mpath, out=os.path.join(tmp_path, "libmutant.so"))
+    o = oracle.Oracle(lib)
+    caught = []
+    for pin in P.ALL_PINS:
+        try:
+            pin(o)
+        except (AssertionError, ValueError, FloatingPointError):
+            caught.append(pin.__name__)
+            break
+    assert caught, f"no pin fails on the planted mistake {name}"
