@@ -1,0 +1,250 @@
+"""Benchmark of the LatentMoE layer forward on one MI355X.
+
+Default workload: the decode-shaped layer (T=32 tokens, d=4096, l=1024,
+512 experts, top-22, m=768, bf16 with fp32 accumulation).  One step is one
+full forward through the C ABI: projection + router, top-K, dispatch, expert
+FFN, combine, projection back with the residual.  Inputs are resident in HBM
+before timing starts.  Two independent weight sets (seeds 0 and 1) alternate
+between steps so that the 256 MB Infinity Cache cannot serve one step's
+expert weights to the next.
+
+Prints ONE JSON line.  `roofline` is for the dominant kernel (the expert FFN):
+its algorithmic bytes (weights of the experts that received rows, read once)
+or flops per launch over its mean duration measured with HIP events recorded
+on the launch stream around that kernel in every timed step.  `cpu_baseline`
+times the fp64 CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "LatentMoE fwd tokens/s (d4096 ℓ1024 E512 top22); % of HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="decode")
+    ap.add_argument("--path", type=int, default=0, help="0 auto, 1 streaming FFN, 2 tiled FFN")
+    ap.add_argument("--weight-sets", type=int, default=2)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget; 0 skips it")
+    ap.add_argument("--no-events", action="store_true", help="time without stage events")
+    return ap.parse_args()
+
+
+class Hip:
+    """The few HIP runtime calls the stage timing needs (events)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        ev = ctypes.c_void_p()
+        rc = self.lib.hipEventCreate(ctypes.byref(ev))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed: {rc}")
+        return ev.value
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        rc = self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return float(ms.value)
+
+
+def algorithmic(w, A: float):
+    """Whole-layer algorithmic bytes and flops (A = experts that got rows)."""
+    B = w.elem_bytes
+    lat = 0 if w.standard else 1
+    nbytes = B * (2 * w.T * w.d + lat * 2 * w.d * w.l + w.d * w.N + A * 2 * w.l * w.m) + (4 * w.N if w.bias else 0)
+    flops = lat * 4 * w.T * w.d * w.l + 2 * w.T * w.d * w.N + 4 * w.T * w.K * w.l * w.m
+    return nbytes, flops
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the layer is not sharded "
+                                   "across GPUs (see DESIGN.md for how it would shard)",
+                          "n_gpus_requested": max(args.gpus, world)}), flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from sparse_moe_layer_gemm_amd import binding as B
+    from sparse_moe_layer_gemm_amd.inputs import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B.lib()
+    sets = []
+    for s in range(max(1, args.weight_sets)):
+        inp = make_inputs(w, seed=s)
+        sets.append((inp, {k: (None if v is None else v.to(dev)) for k, v in inp.items()}))
+    dims = B.dims_for(sets[0][1], w.K, args.path)
+    path = B.latentmoe_resolved_path(dims, w.K)
+    ws = B.alloc_workspace(dims, w.K, dev)
+    out = torch.empty_like(sets[0][1]["x"])
+    stream = torch.cuda.current_stream()
+    hip = Hip()
+    nst = B.LMOE_N_STAGE_EVENTS
+
+    def step(i, events=None):
+        d = sets[i % len(sets)][1]
+        B.latentmoe_forward(d["x"], d["W_down"], d["W_router"], d["W1"], d["W2"], d["W_up"], w.K, out, dims,
+                            router_bias=d["bias"], workspace=ws, stream=stream, events=events)
+
+    # active experts per weight set (for the algorithmic byte count)
+    lay = B.latentmoe_workspace_layout(dims, w.K)
+    active = []
+    for i in range(len(sets)):
+        step(i)
+        torch.cuda.synchronize()
+        active.append(int(ws[lay.n_active:lay.n_active + 4].cpu().numpy().view(np.int32)[0]))
+    A = float(np.mean(active))
+
+    for i in range(args.warmup):
+        step(i)
+    # Timed region: the whole forward, with HIP events recorded on the launch
+    # stream only around the expert FFN (the dominant kernel).
+    ffn_end = 4 if path == B.LMOE_PATH_STREAM else 5
+    ev_ffn = None
+    if not args.no_events:
+        ev_ffn = []
+        for _ in range(args.steps):
+            arr = (ctypes.c_void_p * nst)()
+            arr[3], arr[ffn_end] = hip.event(), hip.event()
+            ev_ffn.append(arr)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, ev_ffn[i] if ev_ffn else None)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+    tok_s = w.T / (ms * 1e-3)
+    ffn_us = float("nan")
+    if ev_ffn:
+        ffn_us = float(np.mean([hip.elapsed_ms(ev[3], ev[ffn_end]) for ev in ev_ffn])) * 1e3
+
+    # Stage breakdown (a separate pass with an event at every stage boundary).
+    stages = {}
+    if not args.no_events:
+        ev_all = [(ctypes.c_void_p * nst)(*[hip.event() for _ in range(nst)]) for _ in range(args.steps)]
+        for i in range(args.steps):
+            step(i, ev_all[i])
+        torch.cuda.synchronize()
+        for si, name in enumerate(B.STAGES):
+            stages[name] = float(np.mean([hip.elapsed_ms(ev[si], ev[si + 1]) for ev in ev_all])) * 1e3
+    copy_gbs = copy_bandwidth(torch, dev)
+    lay_bytes, lay_flops = algorithmic(w, A)
+
+    # dominant kernel: the expert FFN
+    if path == B.LMOE_PATH_STREAM:
+        ffn_bytes = A * 2 * w.l * w.m * w.elem_bytes
+        roof = {"kernel": "ffn_stream_kernel", "bound": "hbm", "achieved": ffn_bytes / (ffn_us * 1e-6) / 1e9,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": None}
+    else:
+        ffn_flops = 4.0 * w.T * w.K * w.l * w.m
+        roof = {"kernel": "gemm_mfma_kernel<Ffn1>+<Ffn2>", "bound": "mfma",
+                "achieved": ffn_flops / (ffn_us * 1e-6) / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "traffic": None}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["kernel_us"] = ffn_us
+    roof["copy_GBps_measured"] = copy_gbs
+    layer_frac = max(lay_bytes / (HBM_PEAK_GBS * 1e9), lay_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)) / (ms * 1e-3)
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(w, sets[0][0], args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "T": w.T, "d": w.d, "l": w.l, "N": w.N, "K": w.K, "m": w.m,
+                   "standard": w.standard, "bias": w.bias, "weight_sets": len(sets),
+                   "ffn_path": "stream" if path == B.LMOE_PATH_STREAM else "tiled",
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "layer": {"algorithmic_bytes": lay_bytes, "algorithmic_flops": lay_flops, "active_experts": A,
+                  "roofline_frac": layer_frac, "stage_us": stages},
+    }
+    print(json.dumps(line), flush=True)
+
+
+def copy_bandwidth(torch, dev, nbytes: int = 1 << 30, reps: int = 10) -> float:
+    """In-run HBM reference: a device-to-device copy, (read + write) bytes / s."""
+    src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    gbs = 2 * nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, dst
+    return gbs
+
+
+def cpu_baseline(w, inp, budget_s: float):
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+
+    from oracle import oracle as O
+    from sparse_moe_layer_gemm_amd.inputs import as_numpy_bits
+
+    arr = {k: (None if v is None else (v.numpy() if k == "bias" else as_numpy_bits(v))) for k, v in inp.items()}
+    orc = O.default()
+    n = 0
+    t0 = time.perf_counter()
+    chunk = min(w.T, 64)
+    passes = 0
+    while True:
+        sel = np.arange(n % w.T, n % w.T + chunk, dtype=np.int32) % w.T
+        orc.forward(arr["x"], arr["W_down"], arr["W_router"], arr["W1"], arr["W2"], arr["W_up"], w.K,
+                    bias=arr["bias"], standard=w.standard, sel=sel)
+        n += chunk
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": n / el, "unit": "tokens/s", "cores": orc.threads(), "kind": "oracle",
+            "sample": f"{n} tokens ({passes} calls of {chunk} tokens) of the {w.name} workload, weight set 0, "
+                      f"{el:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,153 @@
+/*
+ * latentmoe.h -- C ABI of the MI355X (gfx950) LatentMoE layer forward.
+ *
+ * The operation (the pages' three steps, with the readings this library
+ * takes where the pages are silent):
+ *   z      = W_down x                     x of width d -> latent width l
+ *            (qingkeai.online LatentMoE article, section "LatentMoE 具体怎么做",
+ *            first bullet; zhichai.net "LatentMoE: How MoE Made a Key Paradigm
+ *            Leap in 2026", section 2, step 1)
+ *   logit  = W_router x (+ bias)          router at the full width d: the gate
+ *            stays at d (same qingkeai.online section, last paragraph;
+ *            zhichai.net section 2, last paragraph)
+ *   S, g   = top-K of softmax(logit), ties to the lower expert index, kept
+ *            probabilities renormalised to sum 1 (gate function: a reading)
+ *   s      = sum_k g_k W2[S_k] relu(W1[S_k] z)^2   experts in the latent space,
+ *            their weights l x m instead of d x m (qingkeai.online, same
+ *            section, second bullet); outputs aggregated in l before the
+ *            projection back (10100.com article, section 2.2, Figure 3b)
+ *   out    = x + W_up s                   back to width d (third bullet),
+ *            plus the residual (a reading)
+ * Standard mode (W_down == W_up == NULL, l == d): z = x and out = x + s, the
+ * plain MoE of 10100.com Figure 3a, run through the same kernels.
+ *
+ * Layout: every array is dense and row-major, with the reduction index
+ * fastest (the PyTorch nn.Linear [out, in] convention), so both operands of
+ * every matrix product are contiguous along the reduction:
+ *   x        [T, d]            out      [T, d]
+ *   W_down   [l, d]            W_router [N, d]
+ *   W1       [N, m, l]  (expert e at W1 + e*m*l)
+ *   W2       [N, l, m]  (expert e at W2 + e*l*m)
+ *   W_up     [d, l]
+ *   router_bias [N] float32, topk_ids [T, K] int32, topk_gates [T, K] float32
+ * One element type covers x, the weights and out: float32 or bfloat16.
+ * Accumulation is float32; router logits and gates are float32 throughout.
+ *
+ * Memory: all tensor pointers are DEVICE pointers owned by the caller.  The
+ * library allocates nothing in latentmoe_forward, keeps no pointer after it
+ * returns, and writes only `out`, `topk_ids`, `topk_gates` and `workspace`.
+ * The call enqueues work on `stream` (a hipStream_t; NULL = the default
+ * stream) and returns without synchronising: buffers must stay alive until
+ * the stream has finished.  It never synchronises the host and so can be
+ * captured into a HIP graph.
+ *
+ * Errors: arguments are checked before anything is enqueued; on a check
+ * failure nothing is written and a negative lmoe_status is returned.
+ * latentmoe_last_error() gives a thread-local text for the last failure.
+ */
+#ifndef LATENTMOE_H
+#define LATENTMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LMOE_OK = 0,
+    LMOE_EINVAL = -1,        /* a NULL pointer, a bad size or a bad combination */
+    LMOE_EUNSUPPORTED = -2,  /* legal arguments outside what the kernels cover */
+    LMOE_EWORKSPACE = -3,    /* workspace NULL or smaller than latentmoe_workspace_bytes */
+    LMOE_EHIP = -4           /* a HIP launch failed; see latentmoe_last_error() */
+} lmoe_status;
+
+typedef enum { LMOE_F32 = 0, LMOE_BF16 = 1 } lmoe_dtype;
+
+/* Which kernel family runs the expert FFN (bf16 only; float32 always uses
+ * the float32 kernels).  AUTO picks STREAM when the mean number of rows per
+ * expert, T*K/N, is at most 16, else TILED.  STREAM streams each active
+ * expert's weights once per 16 routed rows (decode shapes); TILED runs
+ * LDS-tiled grouped GEMMs (prefill shapes).  Both give results within the
+ * same tolerance of the exact layer. */
+typedef enum { LMOE_PATH_AUTO = 0, LMOE_PATH_STREAM = 1, LMOE_PATH_TILED = 2 } lmoe_path;
+
+typedef struct {
+    int32_t T;      /* tokens, >= 1 */
+    int32_t d;      /* model width, multiple of 64 */
+    int32_t l;      /* latent width, multiple of 64; == d in standard mode */
+    int32_t N;      /* experts, 1 .. 2048 */
+    int32_t m;      /* expert hidden width, multiple of 64 */
+    int32_t dtype;  /* lmoe_dtype */
+    int32_t path;   /* lmoe_path */
+} lmoe_dims;
+
+/* Bytes of device workspace latentmoe_forward needs for these dims and K
+ * (0 when the arguments are invalid).  The size depends on the resolved path. */
+size_t latentmoe_workspace_bytes(const lmoe_dims* dims, int32_t K);
+
+/*
+ * The layer forward.  K: experts per token, 1 <= K <= min(N, 64).
+ * router_bias: NULL or [N] float32 added to the logits before the softmax
+ * (it changes both the selection and the gates).
+ * topk_ids / topk_gates: NULL, or caller buffers that receive the selected
+ * experts in rank order (largest logit first) and their gates.
+ * out must not alias x or any weight.
+ */
+int latentmoe_forward(const void* x, const void* W_down, const void* W_router,
+                      const void* W1, const void* W2, const void* W_up, int32_t K,
+                      void* out, const lmoe_dims* dims, const float* router_bias,
+                      int32_t* topk_ids, float* topk_gates,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * latentmoe_forward with stage timing, for benchmarks and profilers.
+ * events: an array of LMOE_N_STAGE_EVENTS hipEvent_t handles created by
+ * the caller; NULL entries are skipped.  Event i is recorded on `stream` at
+ * the start of stage i, the last one after the final stage.  Stages: 0 projection + router logits, 1 top-K gates,
+ * 2 dispatch, 3 expert FFN first kernel (the whole FFN on the streaming path),
+ * 4 expert FFN second kernel (empty on the streaming path), 5 combine,
+ * 6 projection back to d (empty in standard mode).  The computation is the
+ * same as latentmoe_forward's.
+ */
+#define LMOE_N_STAGE_EVENTS 8
+int latentmoe_forward_timed(const void* x, const void* W_down, const void* W_router,
+                            const void* W1, const void* W2, const void* W_up, int32_t K,
+                            void* out, const lmoe_dims* dims, const float* router_bias,
+                            int32_t* topk_ids, float* topk_gates,
+                            void* workspace, size_t workspace_bytes, void* stream,
+                            void* const* events);
+
+/* Static text for a status code. */
+const char* latentmoe_status_string(int status);
+
+/* Thread-local detail of the last failure in this thread ("" if none). */
+const char* latentmoe_last_error(void);
+
+/* The path latentmoe_forward resolves for these dims and K
+ * (LMOE_PATH_STREAM or LMOE_PATH_TILED), or a negative status. */
+int latentmoe_resolved_path(const lmoe_dims* dims, int32_t K);
+
+/*
+ * Where the dispatch arrays live inside the workspace after a forward (byte
+ * offsets from the workspace base), so that callers and tests can inspect the
+ * token -> expert permutation:
+ *   counts   [N]      int32  rows routed to each expert
+ *   offsets  [N + 1]  int32  exclusive prefix sum of counts
+ *   perm     [T*K]    int32  slot -> flat pair index t*K + k; the slots of one
+ *                            expert are contiguous and in increasing pair order
+ *   slot_of  [T*K]    int32  flat pair index -> slot (the inverse of perm)
+ *   n_active [1]      int32  experts with at least one row
+ */
+typedef struct {
+    size_t counts, offsets, perm, slot_of, n_active;
+} lmoe_ws_layout;
+
+int latentmoe_workspace_layout(const lmoe_dims* dims, int32_t K, lmoe_ws_layout* layout);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LATENTMOE_H */

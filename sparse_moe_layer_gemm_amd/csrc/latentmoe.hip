@@ -1,0 +1,395 @@
+// latentmoe.hip -- the C ABI (include/latentmoe.h) and the launch plan.
+//
+// One forward enqueues, on the caller's stream:
+//   1. z = W_down x and the router logits   (skinny / tiled MFMA / SIMT GEMM)
+//   2. top-K + softmax renormalisation      (one wavefront per token)
+//   3. dispatch: counting sort by expert    (1 or 3 launches)
+//   4. expert FFN                           (streaming kernel, or two grouped
+//                                            GEMMs with ReLU^2 and the gate
+//                                            fused into their epilogues)
+//   5. gate-weighted combine                (+ residual in standard mode)
+//   6. out = x + W_up s                     (latent mode)
+// No host synchronisation and no allocation happen inside a forward.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <string>
+
+#include "../../include/latentmoe.h"
+#include "combine.h"
+#include "common.h"
+#include "gemm.h"
+#include "layer.h"
+#include "route.h"
+#include "stream.h"
+
+using namespace lmoe;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// mean rows per expert at or below which the streaming FFN is chosen
+constexpr int kStreamMaxMeanRows = 16;
+
+struct Plan {
+    int status = LMOE_OK;
+    bool bf16 = false;
+    int path = LMOE_PATH_TILED;   // resolved: STREAM or TILED
+    bool skinny = false;          // projections on the skinny kernel
+    int tile_rows = kTileM;
+    int ms = 128;                 // streaming FFN m-slice
+    int nsplit = 1;
+    int nblk = 1;                 // dispatch blocks
+    long long max_tiles = 0;
+    size_t es = 2;
+    size_t z, logits, ids, gates, counts, offsets, perm, slot_of, blk_counts, blk_offsets, tiles, n_tiles,
+        active, n_active, abuf, ybuf, s, total;
+};
+
+bool mult64(int v) { return v > 0 && v % 64 == 0; }
+
+Plan make_plan(const lmoe_dims* dm, int32_t K) {
+    Plan p;
+    if (!dm) {
+        p.status = fail(LMOE_EINVAL, "dims is NULL");
+        return p;
+    }
+    const lmoe_dims& d = *dm;
+    if (d.T < 1 || d.T > (1 << 24)) {
+        p.status = fail(LMOE_EINVAL, "T=%d must be in [1, 2^24]", d.T);
+        return p;
+    }
+    if (!mult64(d.d) || !mult64(d.l) || !mult64(d.m)) {
+        p.status = fail(LMOE_EINVAL, "d=%d, l=%d, m=%d must be positive multiples of 64", d.d, d.l, d.m);
+        return p;
+    }
+    if (d.N < 1 || d.N > kMaxExperts) {
+        p.status = fail(LMOE_EINVAL, "N=%d must be in [1, %d]", d.N, kMaxExperts);
+        return p;
+    }
+    if (K < 1 || K > d.N || K > kMaxK) {
+        p.status = fail(LMOE_EINVAL, "K=%d must be in [1, min(N=%d, %d)]", K, d.N, kMaxK);
+        return p;
+    }
+    if ((long long)d.T * K > (1ll << 30)) {
+        p.status = fail(LMOE_EUNSUPPORTED, "T*K=%lld exceeds 2^30", (long long)d.T * K);
+        return p;
+    }
+    if (d.dtype != LMOE_F32 && d.dtype != LMOE_BF16) {
+        p.status = fail(LMOE_EINVAL, "dtype=%d is not LMOE_F32 or LMOE_BF16", d.dtype);
+        return p;
+    }
+    if (d.path != LMOE_PATH_AUTO && d.path != LMOE_PATH_STREAM && d.path != LMOE_PATH_TILED) {
+        p.status = fail(LMOE_EINVAL, "path=%d is not a lmoe_path", d.path);
+        return p;
+    }
+    p.bf16 = d.dtype == LMOE_BF16;
+    p.es = p.bf16 ? 2 : 4;
+    const long long TK = (long long)d.T * K;
+    if (!p.bf16) {
+        if (d.path == LMOE_PATH_STREAM) {
+            p.status = fail(LMOE_EUNSUPPORTED, "the streaming FFN is bf16 only");
+            return p;
+        }
+        p.path = LMOE_PATH_TILED;
+        p.tile_rows = kSimtM;
+    } else {
+        if (d.path == LMOE_PATH_AUTO)
+            p.path = (TK <= (long long)kStreamMaxMeanRows * d.N) ? LMOE_PATH_STREAM : LMOE_PATH_TILED;
+        else
+            p.path = d.path;
+        p.tile_rows = kTileM;
+        p.skinny = p.path == LMOE_PATH_STREAM && d.T <= kSkinnyMaxRows;
+        p.ms = (d.m % 128 == 0) ? 128 : 64;
+        p.nsplit = p.path == LMOE_PATH_STREAM ? d.m / p.ms : 1;
+    }
+    p.nblk = cdiv(d.T, kRouteTok);
+    p.max_tiles = TK / p.tile_rows + std::min<long long>(d.N, TK);
+
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o = align_up(o + bytes);
+        return at;
+    };
+    p.z = take((size_t)d.T * d.l * p.es);
+    p.logits = take((size_t)d.T * d.N * 4);
+    p.ids = take((size_t)TK * 4);
+    p.gates = take((size_t)TK * 4);
+    p.counts = take((size_t)d.N * 4);
+    p.offsets = take((size_t)(d.N + 1) * 4);
+    p.perm = take((size_t)TK * 4);
+    p.slot_of = take((size_t)TK * 4);
+    p.blk_counts = take((size_t)p.nblk * d.N * 4);
+    p.blk_offsets = take((size_t)p.nblk * d.N * 4);
+    p.tiles = take((size_t)p.max_tiles * 8);
+    p.n_tiles = take(4);
+    p.active = take((size_t)d.N * 4);
+    p.n_active = take(4);
+    if (p.path == LMOE_PATH_STREAM) {
+        p.abuf = take(0);
+        p.ybuf = take((size_t)p.nsplit * TK * d.l * 4);
+    } else {
+        p.abuf = take((size_t)TK * d.m * p.es);
+        p.ybuf = take((size_t)TK * d.l * p.es);
+    }
+    p.s = take((size_t)d.T * d.l * p.es);
+    p.total = o;
+    return p;
+}
+
+size_t dispatch_lds_bytes(int N) { return (size_t)N * 32 + (size_t)N * 12 + 17 * 4; }
+
+void init_once() {
+    static std::once_flag flag;
+    std::call_once(flag, [] {
+        const int bytes = (int)dispatch_lds_bytes(kMaxExperts);
+        hipFuncSetAttribute((const void*)dispatch_one_block_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+        hipFuncSetAttribute((const void*)dispatch_count_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+        hipFuncSetAttribute((const void*)dispatch_scan_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+        hipFuncSetAttribute((const void*)dispatch_scatter_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+        (void)hipGetLastError();
+    });
+}
+
+template <class E, class YT>
+void launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* events) {
+    auto mark = [&](int i) {
+        if (events && events[i]) hipEventRecord(static_cast<hipEvent_t>(events[i]), st);
+    };
+    const dim3 b256(256), b1024(1024);
+    const int ncols_pr = (a.standard ? 0 : a.l) + a.N;
+    // 1. projection + router logits
+    mark(0);
+    if constexpr (sizeof(E) == 2) {
+        if (p.skinny) {
+            skinny_kernel<ProjRouter<bf16>><<<cdiv(ncols_pr, 16), b1024, 0, st>>>(a);
+        } else {
+            gemm_mfma_kernel<ProjRouter<bf16>><<<dim3(cdiv(a.T, kTileM), cdiv(ncols_pr, kTileN)), b256, 0, st>>>(a);
+        }
+    } else {
+        gemm_simt_kernel<ProjRouter<float>><<<dim3(cdiv(a.T, kSimtM), cdiv(ncols_pr, kSimtN)), b256, 0, st>>>(a);
+    }
+    // 2. top-K gates
+    mark(1);
+    {
+        const dim3 g(cdiv(a.T, 4));
+        if (a.N <= 256)
+            topk_kernel<4><<<g, b256, 0, st>>>(a);
+        else if (a.N <= 512)
+            topk_kernel<8><<<g, b256, 0, st>>>(a);
+        else if (a.N <= 1024)
+            topk_kernel<16><<<g, b256, 0, st>>>(a);
+        else
+            topk_kernel<32><<<g, b256, 0, st>>>(a);
+    }
+    // 3. dispatch
+    mark(2);
+    const size_t lds = dispatch_lds_bytes(a.N);
+    if (p.nblk == 1) {
+        dispatch_one_block_kernel<<<1, b1024, lds, st>>>(a);
+    } else {
+        dispatch_count_kernel<<<p.nblk, b1024, lds, st>>>(a);
+        dispatch_scan_kernel<<<1, b1024, lds, st>>>(a, p.nblk);
+        dispatch_scatter_kernel<<<p.nblk, b1024, lds, st>>>(a);
+    }
+    // 4. expert FFN
+    mark(3);
+    const unsigned mt = (unsigned)p.max_tiles;
+    if constexpr (sizeof(E) == 2) {
+        if (p.path == LMOE_PATH_STREAM) {
+            const dim3 g(a.N, p.nsplit);
+            if (p.ms == 128)
+                ffn_stream_kernel<128><<<g, b256, 0, st>>>(a);
+            else
+                ffn_stream_kernel<64><<<g, b256, 0, st>>>(a);
+            mark(4);
+        } else {
+            gemm_mfma_kernel<Ffn1<bf16>><<<dim3(mt, cdiv(a.m, kTileN)), b256, 0, st>>>(a);
+            mark(4);
+            gemm_mfma_kernel<Ffn2<bf16, YT>><<<dim3(mt, cdiv(a.l, kTileN)), b256, 0, st>>>(a);
+        }
+    } else {
+        gemm_simt_kernel<Ffn1<float>><<<dim3(mt, cdiv(a.m, kSimtN)), b256, 0, st>>>(a);
+        mark(4);
+        gemm_simt_kernel<Ffn2<float, float>><<<dim3(mt, cdiv(a.l, kSimtN)), b256, 0, st>>>(a);
+    }
+    // 5. combine
+    mark(5);
+    const dim3 gc((unsigned)a.T * cdiv(a.l, 256));
+    if (p.path == LMOE_PATH_STREAM)
+        combine_kernel<E, float><<<gc, b256, 0, st>>>(a, p.nsplit, 1);
+    else
+        combine_kernel<E, YT><<<gc, b256, 0, st>>>(a, 1, 0);
+    // 6. back to d with the residual
+    mark(6);
+    if (!a.standard) {
+        if constexpr (sizeof(E) == 2) {
+            if (p.skinny)
+                skinny_kernel<Up<bf16>><<<cdiv(a.d, 16), b1024, 0, st>>>(a);
+            else
+                gemm_mfma_kernel<Up<bf16>><<<dim3(cdiv(a.T, kTileM), cdiv(a.d, kTileN)), b256, 0, st>>>(a);
+        } else {
+            gemm_simt_kernel<Up<float>><<<dim3(cdiv(a.T, kSimtM), cdiv(a.d, kSimtN)), b256, 0, st>>>(a);
+        }
+    }
+    mark(7);
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const char* pa = static_cast<const char*>(a);
+    const char* pb = static_cast<const char*>(b);
+    return pa < pb + nb && pb < pa + na;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t latentmoe_workspace_bytes(const lmoe_dims* dims, int32_t K) {
+    const Plan p = make_plan(dims, K);
+    return p.status == LMOE_OK ? p.total : 0;
+}
+
+int latentmoe_resolved_path(const lmoe_dims* dims, int32_t K) {
+    const Plan p = make_plan(dims, K);
+    return p.status == LMOE_OK ? p.path : p.status;
+}
+
+int latentmoe_workspace_layout(const lmoe_dims* dims, int32_t K, lmoe_ws_layout* layout) {
+    if (!layout) return fail(LMOE_EINVAL, "layout is NULL");
+    const Plan p = make_plan(dims, K);
+    if (p.status != LMOE_OK) return p.status;
+    layout->counts = p.counts;
+    layout->offsets = p.offsets;
+    layout->perm = p.perm;
+    layout->slot_of = p.slot_of;
+    layout->n_active = p.n_active;
+    return LMOE_OK;
+}
+
+static int forward_impl(const void* x, const void* W_down, const void* W_router, const void* W1, const void* W2,
+                        const void* W_up, int32_t K, void* out, const lmoe_dims* dims, const float* router_bias,
+                        int32_t* topk_ids, float* topk_gates, void* workspace, size_t workspace_bytes,
+                        void* stream, void* const* events) {
+    g_last_error.clear();
+    const Plan p = make_plan(dims, K);
+    if (p.status != LMOE_OK) return p.status;
+    const lmoe_dims& d = *dims;
+    if (!x || !W_router || !W1 || !W2 || !out)
+        return fail(LMOE_EINVAL, "x, W_router, W1, W2 and out must be non-NULL");
+    if ((W_down == nullptr) != (W_up == nullptr))
+        return fail(LMOE_EINVAL, "W_down and W_up must be both NULL (standard MoE) or both set");
+    const bool standard = W_down == nullptr;
+    if (standard && d.l != d.d) return fail(LMOE_EINVAL, "standard mode (no projections) needs l == d");
+    if (!workspace) return fail(LMOE_EWORKSPACE, "workspace is NULL");
+    if (workspace_bytes < p.total)
+        return fail(LMOE_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, p.total);
+    const size_t xbytes = (size_t)d.T * d.d * p.es;
+    if (overlaps(out, xbytes, x, xbytes)) return fail(LMOE_EINVAL, "out must not alias x");
+    if (overlaps(out, xbytes, workspace, p.total)) return fail(LMOE_EINVAL, "out must not alias the workspace");
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+        return fail(LMOE_EINVAL, "workspace must be 256-byte aligned");
+    const void* ptrs[] = {x, W_down, W_router, W1, W2, W_up, out};
+    for (const void* q : ptrs)
+        if (q && (reinterpret_cast<uintptr_t>(q) & 15) != 0)
+            return fail(LMOE_EINVAL, "tensor pointers must be 16-byte aligned");
+
+    init_once();
+    char* ws = static_cast<char*>(workspace);
+    LayerArgs a{};
+    a.x = x;
+    a.W_down = W_down;
+    a.W_router = W_router;
+    a.W1 = W1;
+    a.W2 = W2;
+    a.W_up = W_up;
+    a.bias = router_bias;
+    a.out = out;
+    a.T = d.T;
+    a.d = d.d;
+    a.l = d.l;
+    a.N = d.N;
+    a.m = d.m;
+    a.K = K;
+    a.standard = standard ? 1 : 0;
+    a.z_w = ws + p.z;
+    a.z = standard ? x : (const void*)(ws + p.z);
+    a.logits = reinterpret_cast<float*>(ws + p.logits);
+    a.ids = topk_ids ? topk_ids : reinterpret_cast<int32_t*>(ws + p.ids);
+    a.gates = topk_gates ? topk_gates : reinterpret_cast<float*>(ws + p.gates);
+    a.counts = reinterpret_cast<int32_t*>(ws + p.counts);
+    a.offsets = reinterpret_cast<int32_t*>(ws + p.offsets);
+    a.perm = reinterpret_cast<int32_t*>(ws + p.perm);
+    a.slot_of = reinterpret_cast<int32_t*>(ws + p.slot_of);
+    a.blk_counts = reinterpret_cast<int32_t*>(ws + p.blk_counts);
+    a.blk_offsets = reinterpret_cast<int32_t*>(ws + p.blk_offsets);
+    a.tiles = reinterpret_cast<int2*>(ws + p.tiles);
+    a.n_tiles = reinterpret_cast<int32_t*>(ws + p.n_tiles);
+    a.active = reinterpret_cast<int32_t*>(ws + p.active);
+    a.n_active = reinterpret_cast<int32_t*>(ws + p.n_active);
+    a.abuf = ws + p.abuf;
+    a.ybuf = ws + p.ybuf;
+    a.s = ws + p.s;
+    a.tile_rows = p.tile_rows;
+    a.nsplit = p.nsplit;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    if (p.bf16)
+        launch_all<bf16, bf16>(p, a, st, events);
+    else
+        launch_all<float, float>(p, a, st, events);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return fail(LMOE_EHIP, "HIP launch failed: %s", hipGetErrorString(err));
+    return LMOE_OK;
+}
+
+int latentmoe_forward(const void* x, const void* W_down, const void* W_router, const void* W1, const void* W2,
+                      const void* W_up, int32_t K, void* out, const lmoe_dims* dims, const float* router_bias,
+                      int32_t* topk_ids, float* topk_gates, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+    return forward_impl(x, W_down, W_router, W1, W2, W_up, K, out, dims, router_bias, topk_ids, topk_gates,
+                        workspace, workspace_bytes, stream, nullptr);
+}
+
+int latentmoe_forward_timed(const void* x, const void* W_down, const void* W_router, const void* W1,
+                            const void* W2, const void* W_up, int32_t K, void* out, const lmoe_dims* dims,
+                            const float* router_bias, int32_t* topk_ids, float* topk_gates, void* workspace,
+                            size_t workspace_bytes, void* stream, void* const* events) {
+    if (!events) return fail(LMOE_EINVAL, "events is NULL");
+    return forward_impl(x, W_down, W_router, W1, W2, W_up, K, out, dims, router_bias, topk_ids, topk_gates,
+                        workspace, workspace_bytes, stream, events);
+}
+
+const char* latentmoe_status_string(int status) {
+    switch (status) {
+        case LMOE_OK: return "ok";
+        case LMOE_EINVAL: return "invalid argument";
+        case LMOE_EUNSUPPORTED: return "unsupported arguments";
+        case LMOE_EWORKSPACE: return "workspace missing or too small";
+        case LMOE_EHIP: return "HIP launch failure";
+        default: return "unknown status";
+    }
+}
+
+const char* latentmoe_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

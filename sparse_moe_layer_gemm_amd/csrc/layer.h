@@ -1,0 +1,152 @@
+// layer.h -- the arguments every kernel of the layer sees, and the four
+// matrix products of the layer expressed as "problems" that the GEMM kernels
+// (tiled MFMA for bf16, SIMT for float32) instantiate.
+//
+// Every product has the form C[r, c] = epilogue(sum_k A[r, k] * B[c, k]):
+// both operands are read along their contiguous reduction index.
+#pragma once
+
+#include "common.h"
+
+namespace lmoe {
+
+struct LayerArgs {
+    // caller tensors
+    const void* x;         // [T, d]
+    const void* W_down;    // [l, d] or NULL (standard mode)
+    const void* W_router;  // [N, d]
+    const void* W1;        // [N, m, l]
+    const void* W2;        // [N, l, m]
+    const void* W_up;      // [d, l] or NULL (standard mode)
+    const float* bias;     // [N] or NULL
+    void* out;             // [T, d]
+    int T, d, l, N, m, K;
+    int standard;
+    // workspace
+    const void* z;         // [T, l] latent tokens (== x in standard mode)
+    void* z_w;             // writable view of z (latent mode)
+    float* logits;         // [T, N]
+    int32_t* ids;          // [T, K]
+    float* gates;          // [T, K]
+    int32_t* counts;       // [N]
+    int32_t* offsets;      // [N + 1]
+    int32_t* perm;         // [T*K] slot -> t*K + k
+    int32_t* slot_of;      // [T*K] t*K + k -> slot
+    int32_t* blk_counts;   // [nblk, N]
+    int32_t* blk_offsets;  // [nblk, N]
+    int2* tiles;           // grouped-GEMM row tiles: (expert, first slot)
+    int32_t* n_tiles;
+    int32_t* active;       // experts with rows, ascending
+    int32_t* n_active;
+    void* abuf;            // [T*K, m] relu(h)^2
+    void* ybuf;            // expert outputs (layout depends on the path)
+    void* s;               // [T, l] gate-weighted latent sum (latent mode)
+    int tile_rows;         // rows per grouped-GEMM tile
+    int nsplit;            // m-slices of the streaming FFN
+};
+
+// ---------------------------------------------------------------------------
+// z = W_down x and logits = W_router x (+ bias), one product over the
+// concatenated columns [z | logits].
+
+template <class E>
+struct ProjRouter {
+    __device__ static bool tile(const LayerArgs& a, int bx, int bm, int& grp, int& row0, int& row_end) {
+        grp = 0;
+        row0 = bx * bm;
+        row_end = a.T;
+        return row0 < row_end;
+    }
+    __device__ static int ncols(const LayerArgs& a) { return (a.standard ? 0 : a.l) + a.N; }
+    __device__ static int kdim(const LayerArgs& a) { return a.d; }
+    __device__ static const E* a_row(const LayerArgs& a, int, int r) {
+        return static_cast<const E*>(a.x) + (size_t)r * a.d;
+    }
+    __device__ static const E* b_row(const LayerArgs& a, int, int c) {
+        const int lz = a.standard ? 0 : a.l;
+        return c < lz ? static_cast<const E*>(a.W_down) + (size_t)c * a.d
+                      : static_cast<const E*>(a.W_router) + (size_t)(c - lz) * a.d;
+    }
+    __device__ static void store(const LayerArgs& a, int, int r, int c, float v) {
+        const int lz = a.standard ? 0 : a.l;
+        if (c < lz) {
+            static_cast<E*>(a.z_w)[(size_t)r * a.l + c] = from_f32<E>(v);
+        } else {
+            const int e = c - lz;
+            a.logits[(size_t)r * a.N + e] = v + (a.bias ? a.bias[e] : 0.0f);
+        }
+    }
+};
+
+// Expert FFN, first product: h = W1[e] z for the rows routed to e, then
+// relu(h)^2.  Row r of a tile is slot r; its token is perm[r] / K.
+template <class E>
+struct Ffn1 {
+    __device__ static bool tile(const LayerArgs& a, int bx, int, int& grp, int& row0, int& row_end) {
+        if (bx >= *a.n_tiles) return false;
+        const int2 t = a.tiles[bx];
+        grp = t.x;
+        row0 = t.y;
+        row_end = a.offsets[grp + 1];
+        return true;
+    }
+    __device__ static int ncols(const LayerArgs& a) { return a.m; }
+    __device__ static int kdim(const LayerArgs& a) { return a.l; }
+    __device__ static const E* a_row(const LayerArgs& a, int, int slot) {
+        const int t = a.perm[slot] / a.K;
+        return static_cast<const E*>(a.z) + (size_t)t * a.l;
+    }
+    __device__ static const E* b_row(const LayerArgs& a, int e, int c) {
+        return static_cast<const E*>(a.W1) + ((size_t)e * a.m + c) * a.l;
+    }
+    __device__ static void store(const LayerArgs& a, int, int slot, int c, float v) {
+        const float r = v > 0.0f ? v : 0.0f;
+        static_cast<E*>(a.abuf)[(size_t)slot * a.m + c] = from_f32<E>(r * r);
+    }
+};
+
+// Expert FFN, second product: y = W2[e] a, scaled by the slot's gate
+// (so the combine only sums).  YT: storage type of the expert outputs.
+template <class E, class YT>
+struct Ffn2 {
+    __device__ static bool tile(const LayerArgs& a, int bx, int bm, int& grp, int& row0, int& row_end) {
+        return Ffn1<E>::tile(a, bx, bm, grp, row0, row_end);
+    }
+    __device__ static int ncols(const LayerArgs& a) { return a.l; }
+    __device__ static int kdim(const LayerArgs& a) { return a.m; }
+    __device__ static const E* a_row(const LayerArgs& a, int, int slot) {
+        return static_cast<const E*>(a.abuf) + (size_t)slot * a.m;
+    }
+    __device__ static const E* b_row(const LayerArgs& a, int e, int c) {
+        return static_cast<const E*>(a.W2) + ((size_t)e * a.l + c) * a.m;
+    }
+    __device__ static void store(const LayerArgs& a, int, int slot, int c, float v) {
+        const float g = a.gates[a.perm[slot]];
+        static_cast<YT*>(a.ybuf)[(size_t)slot * a.l + c] = from_f32<YT>(g * v);
+    }
+};
+
+// out = x + W_up s.
+template <class E>
+struct Up {
+    __device__ static bool tile(const LayerArgs& a, int bx, int bm, int& grp, int& row0, int& row_end) {
+        grp = 0;
+        row0 = bx * bm;
+        row_end = a.T;
+        return row0 < row_end;
+    }
+    __device__ static int ncols(const LayerArgs& a) { return a.d; }
+    __device__ static int kdim(const LayerArgs& a) { return a.l; }
+    __device__ static const E* a_row(const LayerArgs& a, int, int r) {
+        return static_cast<const E*>(a.s) + (size_t)r * a.l;
+    }
+    __device__ static const E* b_row(const LayerArgs& a, int, int c) {
+        return static_cast<const E*>(a.W_up) + (size_t)c * a.l;
+    }
+    __device__ static void store(const LayerArgs& a, int, int r, int c, float v) {
+        const size_t i = (size_t)r * a.d + c;
+        static_cast<E*>(a.out)[i] = from_f32<E>(to_f32(static_cast<const E*>(a.x)[i]) + v);
+    }
+};
+
+}  // namespace lmoe

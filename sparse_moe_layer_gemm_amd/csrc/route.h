@@ -1,0 +1,281 @@
+// route.h -- top-K gate selection and the token -> expert dispatch.
+//
+// topk_kernel: one wavefront per token, a radix select.  Each logit maps to
+// an order-preserving 32-bit key (NaN ranks as -inf, -0 as +0).  32
+// bisection steps, each counting keys >= a candidate with one ballot per
+// register, find the K-th largest key tau exactly; the selection is every
+// key > tau plus the lowest-index keys == tau, which is exactly the first K
+// in (larger logit, then lower expert index) order.  The K winners are
+// compacted through LDS and each ranks itself against the others.  The gates
+// are the softmax over the K selected logits, which equals the full softmax
+// renormalised over them.
+//
+// Dispatch is a stable counting sort of the T*K (token, rank) pairs by
+// expert, done with per-block bit masks instead of atomics on counters:
+// a block of 256 tokens marks, for every expert, which of its tokens chose
+// that expert (256 bits = 4 words per expert in LDS).  The popcount of the
+// mask is the block's count for the expert; the popcount of the bits below
+// a token is that pair's rank inside the block.  A scan over blocks and
+// experts turns these into slots.  Each token chooses an expert at most once,
+// so the slots of an expert come out ordered by token: the result is
+// deterministic and does not depend on scheduling.
+#pragma once
+
+#include "layer.h"
+
+namespace lmoe {
+
+constexpr int kRouteTok = 256;   // tokens per dispatch block
+constexpr int kMaxExperts = 2048;
+constexpr int kMaxK = 64;
+
+__device__ __forceinline__ uint32_t order_key(float v) {
+    if (v != v) v = -INFINITY;
+    if (v == 0.0f) v = 0.0f;
+    const uint32_t u = __float_as_uint(v);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ int popc64(unsigned long long m) { return __popcll(m); }
+
+template <int NPL>
+__global__ __launch_bounds__(256) void topk_kernel(LayerArgs a) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + wave;
+    __shared__ uint32_t s_key[4][64];
+    __shared__ int s_idx[4][64];
+    __shared__ float s_val[4][64];
+    if (t >= a.T) return;
+    const float* lg = a.logits + (size_t)t * a.N;
+    float v[NPL];
+    uint32_t key[NPL];
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+        const int e = lane + 64 * j;
+        v[j] = e < a.N ? lg[e] : -INFINITY;
+        key[j] = e < a.N ? order_key(v[j]) : 0u;  // padding sorts below every real key
+    }
+    const int K = a.K;
+    // K-th largest key by bisection on its bits
+    uint32_t tau = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = tau | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int j = 0; j < NPL; ++j) cnt += popc64(__ballot(key[j] >= cand));
+        if (cnt >= K) tau = cand;
+    }
+    int gt = 0;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) gt += popc64(__ballot(key[j] > tau));
+    const int need = K - gt;  // keys equal to tau still to take, lowest index first
+    const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int eq_seen = 0, base = 0;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+        const bool eq = key[j] == tau;
+        const unsigned long long me = __ballot(eq);
+        const bool take = key[j] > tau || (eq && eq_seen + popc64(me & below) < need);
+        eq_seen += popc64(me);
+        const unsigned long long mt = __ballot(take);
+        if (take) {
+            const int pos = base + popc64(mt & below);
+            s_key[wave][pos] = key[j];
+            s_idx[wave][pos] = lane + 64 * j;
+            s_val[wave][pos] = v[j];
+        }
+        base += popc64(mt);
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    float my_v = -INFINITY;
+    int my_rank = 0, my_idx = 0;
+    if (lane < K) {
+        const uint32_t mk = s_key[wave][lane];
+        my_idx = s_idx[wave][lane];
+        my_v = s_val[wave][lane];
+        for (int q = 0; q < K; ++q) {
+            const uint32_t qk = s_key[wave][q];
+            my_rank += (qk > mk || (qk == mk && s_idx[wave][q] < my_idx)) ? 1 : 0;
+        }
+    }
+    float mx = my_v;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    const float ex = lane < K ? expf(my_v - mx) : 0.0f;
+    float sum = ex;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+    if (lane < K) {
+        a.ids[(size_t)t * K + my_rank] = my_idx;
+        a.gates[(size_t)t * K + my_rank] = ex / sum;
+    }
+}
+
+// --- dispatch helpers --------------------------------------------------------
+
+// Mark, for every expert, which tokens of block `blk` chose it.
+__device__ inline void build_masks(const LayerArgs& a, int blk, unsigned long long* masks) {
+    for (int i = threadIdx.x; i < a.N * 4; i += blockDim.x) masks[i] = 0ull;
+    __syncthreads();
+    const int t0 = blk * kRouteTok;
+    const int tcount = min(kRouteTok, a.T - t0);
+    const int npairs = tcount * a.K;
+    for (int p = threadIdx.x; p < npairs; p += blockDim.x) {
+        const int u = p / a.K;
+        const int e = a.ids[(size_t)t0 * a.K + p];
+        atomicOr(&masks[e * 4 + (u >> 6)], 1ull << (u & 63));
+    }
+    __syncthreads();
+}
+
+__device__ inline int mask_count(const unsigned long long* m) {
+    return __popcll(m[0]) + __popcll(m[1]) + __popcll(m[2]) + __popcll(m[3]);
+}
+
+__device__ inline int mask_below(const unsigned long long* m, int u) {
+    int c = 0;
+    const int w = u >> 6;
+    for (int i = 0; i < w; ++i) c += __popcll(m[i]);
+    const unsigned long long low = (u & 63) ? ((1ull << (u & 63)) - 1ull) : 0ull;
+    return c + __popcll(m[w] & low);
+}
+
+// Exclusive scan of v[0..n) in LDS, n <= 2 * blockDim.x, blockDim.x == 1024.
+// Returns the total.  wsum: 16 ints of LDS scratch.
+__device__ inline int block_excl_scan(int* v, int n, int* wsum) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int a0 = 2 * tid < n ? v[2 * tid] : 0;
+    const int a1 = 2 * tid + 1 < n ? v[2 * tid + 1] : 0;
+    const int s = a0 + a1;
+    int incl = s;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    if (tid == 0) {
+        int run = 0;
+        for (int w = 0; w < 16; ++w) {
+            const int c = wsum[w];
+            wsum[w] = run;
+            run += c;
+        }
+        wsum[16] = run;
+    }
+    __syncthreads();
+    const int excl = incl - s + wsum[wave];
+    if (2 * tid < n) v[2 * tid] = excl;
+    if (2 * tid + 1 < n) v[2 * tid + 1] = excl + a0;
+    const int total = wsum[16];
+    __syncthreads();
+    return total;
+}
+
+// From per-expert counts in LDS `cnt`: counts, offsets, the active-expert
+// list and the grouped-GEMM tile list in global memory; the exclusive offsets
+// are also left in LDS `off`.  tmp, wsum: LDS scratch.
+__device__ inline void finish_scan(const LayerArgs& a, const int* cnt, int* off, int* tmp, int* wsum) {
+    const int N = a.N;
+    for (int e = threadIdx.x; e < N; e += blockDim.x) {
+        const int c = cnt[e];
+        a.counts[e] = c;
+        off[e] = c;
+        tmp[e] = c > 0 ? 1 : 0;
+    }
+    __syncthreads();
+    const int total = block_excl_scan(off, N, wsum);
+    const int n_act = block_excl_scan(tmp, N, wsum);
+    for (int e = threadIdx.x; e < N; e += blockDim.x) {
+        a.offsets[e] = off[e];
+        if (cnt[e] > 0) a.active[tmp[e]] = e;
+    }
+    if (threadIdx.x == 0) {
+        a.offsets[N] = total;
+        *a.n_active = n_act;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < N; e += blockDim.x) tmp[e] = cdiv(cnt[e], a.tile_rows);
+    __syncthreads();
+    const int ntiles = block_excl_scan(tmp, N, wsum);
+    for (int e = threadIdx.x; e < N; e += blockDim.x) {
+        const int nt = cdiv(cnt[e], a.tile_rows), base = tmp[e], o = off[e];
+        for (int i = 0; i < nt; ++i) a.tiles[base + i] = make_int2(e, o + i * a.tile_rows);
+    }
+    if (threadIdx.x == 0) *a.n_tiles = ntiles;
+    __syncthreads();
+}
+
+__device__ inline void scatter_block(const LayerArgs& a, int blk, const unsigned long long* masks,
+                                     const int* base_of_expert) {
+    const int t0 = blk * kRouteTok;
+    const int tcount = min(kRouteTok, a.T - t0);
+    const int npairs = tcount * a.K;
+    for (int p = threadIdx.x; p < npairs; p += blockDim.x) {
+        const int u = p / a.K;
+        const int flat = t0 * a.K + p;
+        const int e = a.ids[flat];
+        const int slot = base_of_expert[e] + mask_below(masks + e * 4, u);
+        a.perm[slot] = flat;
+        a.slot_of[flat] = slot;
+    }
+}
+
+// Whole dispatch in one workgroup (T <= 256 tokens).
+__global__ __launch_bounds__(1024) void dispatch_one_block_kernel(LayerArgs a) {
+    extern __shared__ unsigned long long smem_u64[];
+    unsigned long long* masks = smem_u64;                      // [N*4]
+    int* cnt = reinterpret_cast<int*>(masks + a.N * 4);         // [N]
+    int* off = cnt + a.N;                                       // [N]
+    int* tmp = off + a.N;                                       // [N]
+    int* wsum = tmp + a.N;                                      // [17]
+    build_masks(a, 0, masks);
+    for (int e = threadIdx.x; e < a.N; e += blockDim.x) cnt[e] = mask_count(masks + e * 4);
+    __syncthreads();
+    finish_scan(a, cnt, off, tmp, wsum);
+    scatter_block(a, 0, masks, off);
+}
+
+// Multi-block dispatch: count -> scan -> scatter.
+__global__ __launch_bounds__(1024) void dispatch_count_kernel(LayerArgs a) {
+    extern __shared__ unsigned long long smem_u64[];
+    unsigned long long* masks = smem_u64;
+    build_masks(a, blockIdx.x, masks);
+    for (int e = threadIdx.x; e < a.N; e += blockDim.x)
+        a.blk_counts[(size_t)blockIdx.x * a.N + e] = mask_count(masks + e * 4);
+}
+
+__global__ __launch_bounds__(1024) void dispatch_scan_kernel(LayerArgs a, int nblk) {
+    extern __shared__ unsigned long long smem_u64[];
+    int* cnt = reinterpret_cast<int*>(smem_u64);
+    int* off = cnt + a.N;
+    int* tmp = off + a.N;
+    int* wsum = tmp + a.N;
+    for (int e = threadIdx.x; e < a.N; e += blockDim.x) {
+        int run = 0;
+        for (int b = 0; b < nblk; ++b) {
+            const int c = a.blk_counts[(size_t)b * a.N + e];
+            a.blk_offsets[(size_t)b * a.N + e] = run;
+            run += c;
+        }
+        cnt[e] = run;
+    }
+    __syncthreads();
+    finish_scan(a, cnt, off, tmp, wsum);
+}
+
+__global__ __launch_bounds__(1024) void dispatch_scatter_kernel(LayerArgs a) {
+    extern __shared__ unsigned long long smem_u64[];
+    unsigned long long* masks = smem_u64;
+    int* base = reinterpret_cast<int*>(masks + a.N * 4);
+    build_masks(a, blockIdx.x, masks);
+    for (int e = threadIdx.x; e < a.N; e += blockDim.x)
+        base[e] = a.offsets[e] + a.blk_offsets[(size_t)blockIdx.x * a.N + e];
+    __syncthreads();
+    scatter_block(a, blockIdx.x, masks, base);
+}
+
+}  // namespace lmoe

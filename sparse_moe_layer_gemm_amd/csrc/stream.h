@@ -1,0 +1,173 @@
+// stream.h -- kernels for few rows per weight matrix (decode shapes).
+//
+// With a handful of tokens per expert the layer is bound by reading weights
+// from HBM once.  These kernels load MFMA operand fragments straight from
+// global memory (both operands are contiguous along the reduction index, so
+// a lane's 8 bf16 of a v_mfma_f32_16x16x32_bf16 operand are one 16-byte
+// load) and keep many such loads in flight per wave.  The 16-row MFMA pads
+// the few real rows; the extra arithmetic is free next to the weight stream.
+//
+//   skinny_kernel<P>: a product with T <= 64 rows.  One workgroup of 16 waves
+//     owns 16 output columns; the waves split the reduction and add their
+//     partial tiles through LDS.
+//   ffn_stream_kernel<MS>: the expert FFN.  Workgroup (a, s) takes active
+//     expert a and the m-slice [s*MS, (s+1)*MS): it computes
+//     relu(W1[e][slice] z)^2 for up to 16 routed rows at a time, keeps it in
+//     LDS, and multiplies it by the matching column slice of W2[e], writing
+//     an fp32 partial expert output per slice.  Every weight byte of an
+//     active expert is read once per 16 rows; no atomics: the combine adds
+//     the slices in a fixed order.
+#pragma once
+
+#include "layer.h"
+
+namespace lmoe {
+
+constexpr int kSkinnyWaves = 16;
+constexpr int kSkinnyMaxRows = 64;
+
+template <class P>
+__global__ __launch_bounds__(1024) void skinny_kernel(LayerArgs a) {
+    const int c0 = blockIdx.x * 16;
+    const int ncols = P::ncols(a), K = P::kdim(a);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int nrb = cdiv(a.T, 16);
+    const int ksteps = K / 32;
+    const int per = cdiv(ksteps, kSkinnyWaves);
+    const int ks0 = wave * per, ks1 = min(ksteps, ks0 + per);
+    const int c = c0 + (lane & 15);
+    const int koff = 8 * (lane >> 4);
+    const bf16* bp = c < ncols ? P::b_row(a, 0, c) + koff : nullptr;
+    const bf16* ap[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+        const int r = rb * 16 + (lane & 15);
+        ap[rb] = (rb < nrb && r < a.T) ? P::a_row(a, 0, r) + koff : nullptr;
+    }
+    f32x4 acc[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int ks = ks0; ks < ks1; ks += 4) {
+        uint4 bv[4], av[4][4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int k0 = (ks + u) * 32;
+            const bool ok = ks + u < ks1;
+            bv[u] = (ok && bp) ? ldg16(bp + k0) : kZero16;
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) av[u][rb] = (ok && ap[rb]) ? ldg16(ap[rb] + k0) : kZero16;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb)
+                if (rb < nrb) acc[rb] = mfma16(as_bf16x8(av[u][rb]), as_bf16x8(bv[u]), acc[rb]);
+    }
+
+    __shared__ f32x4 red[kSkinnyWaves][4][64];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+        if (rb < nrb) red[wave][rb][lane] = acc[rb];
+    __syncthreads();
+    if (threadIdx.x < nrb * 64) {
+        const int rb = threadIdx.x >> 6;
+        f32x4 s = red[0][rb][lane];
+        for (int w = 1; w < kSkinnyWaves; ++w) s += red[w][rb][lane];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = rb * 16 + 4 * (lane >> 4) + r;
+            if (row < a.T && c < ncols) P::store(a, 0, row, c, s[r]);
+        }
+    }
+}
+
+template <int MS>
+__global__ __launch_bounds__(256) void ffn_stream_kernel(LayerArgs a) {
+    const int ai = blockIdx.x;
+    if (ai >= *a.n_active) return;
+    const int e = a.active[ai];
+    const int j0 = blockIdx.y * MS;
+    const int r_begin = a.offsets[e], r_end = a.offsets[e + 1];
+    const int l = a.l, m = a.m;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int lr = lane & 15, koff = 8 * (lane >> 4);
+    const bf16* W1e = static_cast<const bf16*>(a.W1) + (size_t)e * m * l;
+    const bf16* W2e = static_cast<const bf16*>(a.W2) + (size_t)e * l * m;
+    const bf16* Z = static_cast<const bf16*>(a.z);
+    float* Yp = static_cast<float*>(a.ybuf) + (size_t)blockIdx.y * a.T * a.K * l;
+
+    constexpr int NB = MS / 16;        // 16-column blocks of the slice
+    constexpr int NBW = NB / 4;        // per wave
+    constexpr int AST = MS + 8;        // LDS row stride (bf16), padded
+    __shared__ bf16 As[16 * AST];
+
+    for (int rc = r_begin; rc < r_end; rc += 16) {
+        const int nr = min(16, r_end - rc);
+        // ---- phase 1: H[16 x MS] = Z[rows] . W1[e][j0 : j0+MS]^T, reduce over l
+        const int my_slot = rc + min(lr, nr - 1);
+        const bf16* zp = Z + (size_t)(a.perm[my_slot] / a.K) * l + koff;
+        const bf16* bp[NBW];
+#pragma unroll
+        for (int b = 0; b < NBW; ++b) bp[b] = W1e + (size_t)(j0 + (wave + 4 * b) * 16 + lr) * l + koff;
+        f32x4 acc[NBW];
+#pragma unroll
+        for (int b = 0; b < NBW; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int k0 = 0; k0 < l; k0 += 32 * 4) {
+            uint4 zv[4], wv[4][NBW];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const bool ok = k0 + 32 * u < l;
+                zv[u] = ok ? ldg16(zp + k0 + 32 * u) : kZero16;
+#pragma unroll
+                for (int b = 0; b < NBW; ++b) wv[u][b] = ok ? ldg16(bp[b] + k0 + 32 * u) : kZero16;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int b = 0; b < NBW; ++b) acc[b] = mfma16(as_bf16x8(zv[u]), as_bf16x8(wv[u][b]), acc[b]);
+        }
+#pragma unroll
+        for (int b = 0; b < NBW; ++b)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float h = acc[b][r] > 0.0f ? acc[b][r] : 0.0f;
+                As[(4 * (lane >> 4) + r) * AST + (wave + 4 * b) * 16 + lr] = (bf16)(h * h);
+            }
+        __syncthreads();
+        // ---- phase 2: Y[16 x l] = A[16 x MS] . W2[e][:, j0 : j0+MS]^T
+        constexpr int KS = MS / 32;
+        bf16x8 af[KS];
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+            af[kk] = *reinterpret_cast<const bf16x8*>(&As[lr * AST + kk * 32 + koff]);
+        const int nblk = l / 16;
+        for (int ib = wave; ib < nblk; ib += 4 * 4) {
+            uint4 wv[4][KS];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int i0 = (ib + 4 * u) * 16;
+                const bool ok = ib + 4 * u < nblk;
+                const bf16* p = W2e + (size_t)(i0 + lr) * m + j0 + koff;
+#pragma unroll
+                for (int kk = 0; kk < KS; ++kk) wv[u][kk] = ok ? ldg16(p + kk * 32) : kZero16;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int i0 = (ib + 4 * u) * 16;
+                if (ib + 4 * u >= nblk) break;
+                f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < KS; ++kk) y = mfma16(af[kk], as_bf16x8(wv[u][kk]), y);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 4 * (lane >> 4) + r;
+                    if (row < nr) Yp[(size_t)(rc + row) * l + i0 + lr] = y[r];
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
+}  // namespace lmoe

@@ -1,0 +1,126 @@
+"""The C-ABI library on the host: it loads, exports what the header declares,
+sizes its workspace, and rejects bad arguments before touching a GPU.
+
+No test here launches a kernel: every forward call below fails validation,
+which happens before any HIP call.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from sparse_moe_layer_gemm_amd import binding as B
+from sparse_moe_layer_gemm_amd.inputs import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "latentmoe.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        from sparse_moe_layer_gemm_amd import build
+        build.build()
+    return B.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(latentmoe_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_names():
+    assert declared_functions() == sorted(B.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    nm = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (latentmoe_\w+)", nm))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def dims_of(w, path=B.LMOE_PATH_AUTO):
+    return B.make_dims(w.T, w.d, w.l, w.N, w.m, w.dtype, path)
+
+
+@pytest.mark.parametrize("name", sorted(WORKLOADS))
+def test_workspace_sizes(lib, name):
+    w = WORKLOADS[name]
+    n = B.latentmoe_workspace_bytes(dims_of(w), w.K)
+    assert n > 0 and n % 256 == 0
+    lay = B.latentmoe_workspace_layout(dims_of(w), w.K)
+    spans = [(lay.counts, 4 * w.N), (lay.offsets, 4 * (w.N + 1)), (lay.perm, 4 * w.T * w.K),
+             (lay.slot_of, 4 * w.T * w.K), (lay.n_active, 4)]
+    for off, size in spans:
+        assert off % 256 == 0 and off + size <= n
+    spans.sort()
+    for (o1, s1), (o2, _) in zip(spans, spans[1:]):
+        assert o1 + s1 <= o2
+
+
+def test_resolved_paths(lib):
+    S, Tl = B.LMOE_PATH_STREAM, B.LMOE_PATH_TILED
+    assert B.latentmoe_resolved_path(dims_of(WORKLOADS["decode"]), 22) == S
+    assert B.latentmoe_resolved_path(dims_of(WORKLOADS["standard_decode"]), 6) == S
+    assert B.latentmoe_resolved_path(dims_of(WORKLOADS["prefill"]), 22) == Tl
+    assert B.latentmoe_resolved_path(dims_of(WORKLOADS["skewed"]), 16) == Tl
+    assert B.latentmoe_resolved_path(dims_of(WORKLOADS["tiny_f32"]), 4) == Tl
+    assert B.latentmoe_resolved_path(dims_of(WORKLOADS["decode"], Tl), 22) == Tl
+    assert B.latentmoe_resolved_path(dims_of(WORKLOADS["tiny_f32"], S), 4) == B.LMOE_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("field,value,K", [
+    ("T", 0, 4), ("d", 100, 4), ("l", 0, 4), ("m", 65, 4), ("N", 0, 4), ("N", 4096, 4),
+    ("dtype", 7, 4), ("path", 9, 4), (None, None, 0), (None, None, 33), (None, None, 65),
+])
+def test_invalid_dims_rejected(lib, field, value, K):
+    d = dims_of(WORKLOADS["tiny_f32"])
+    if field:
+        setattr(d, field, value)
+    assert B.latentmoe_workspace_bytes(d, K) == 0
+    assert B.latentmoe_resolved_path(d, K) < 0
+    assert B.latentmoe_last_error() != ""
+
+
+FAKE = 1 << 40  # 256-aligned, never dereferenced: every call below fails validation first
+
+
+def call(dims, K, **over):
+    args = dict(x=FAKE, W_down=FAKE + (1 << 30), W_router=FAKE + (2 << 30), W1=FAKE + (3 << 30),
+                W2=FAKE + (4 << 30), W_up=FAKE + (5 << 30), out=FAKE + (6 << 30),
+                workspace=FAKE + (7 << 30), workspace_bytes=B.latentmoe_workspace_bytes(dims, K) if K else 0)
+    args.update(over)
+    return B.latentmoe_forward(args["x"], args["W_down"], args["W_router"], args["W1"], args["W2"],
+                               args["W_up"], K, args["out"], dims, workspace=args["workspace"],
+                               workspace_bytes=args["workspace_bytes"], stream=0, check=False)
+
+
+def test_forward_argument_checks(lib):
+    w = WORKLOADS["decode"]
+    d = dims_of(w)
+    need = B.latentmoe_workspace_bytes(d, w.K)
+    assert call(d, 0) == B.LMOE_EINVAL
+    assert call(d, w.K, x=None) == B.LMOE_EINVAL
+    assert call(d, w.K, W1=None) == B.LMOE_EINVAL
+    assert call(d, w.K, out=None) == B.LMOE_EINVAL
+    assert call(d, w.K, W_down=None) == B.LMOE_EINVAL          # only one projection given
+    assert call(d, w.K, W_down=None, W_up=None) == B.LMOE_EINVAL  # standard mode needs l == d
+    assert call(d, w.K, workspace=None) == B.LMOE_EWORKSPACE
+    assert call(d, w.K, workspace_bytes=need - 1) == B.LMOE_EWORKSPACE
+    assert "needs" in B.latentmoe_last_error()
+    assert call(d, w.K, out=FAKE) == B.LMOE_EINVAL               # out aliases x
+    assert call(d, w.K, out=FAKE + 4096) == B.LMOE_EINVAL        # partial overlap
+    assert call(d, w.K, workspace=FAKE + (7 << 30) + 8) == B.LMOE_EINVAL
+    assert call(d, w.K, W2=FAKE + (4 << 30) + 2) == B.LMOE_EINVAL
+    ws = B.make_dims(w.T, w.d, w.l, w.N, w.m, "f32", B.LMOE_PATH_STREAM)
+    assert call(ws, w.K) == B.LMOE_EUNSUPPORTED
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4, 99):
+        assert isinstance(B.latentmoe_status_string(code), str)
+    assert B.latentmoe_status_string(0) == "ok"

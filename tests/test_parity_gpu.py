@@ -1,0 +1,182 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Full workloads where the oracle finishes in seconds (tiny float32, decode,
+standard-MoE decode); the prefill, standard-MoE prefill and skewed workloads
+run at full size on the GPU in the same launch configuration the benchmark
+times and are compared on sampled tokens (plus the ragged tail).  Smaller
+shapes cover several tiles, ragged tails and the edge cases.
+"""
+import numpy as np
+import pytest
+import torch
+
+from sparse_moe_layer_gemm_amd import binding as B
+from sparse_moe_layer_gemm_amd.inputs import WORKLOADS, Workload, make_inputs
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+S, TL = B.LMOE_PATH_STREAM, B.LMOE_PATH_TILED
+
+
+def sample_tokens(T, n, seed=0):
+    rng = np.random.default_rng(seed)
+    picks = rng.choice(T, size=min(n, T), replace=False)
+    tail = np.arange(max(0, T - 5), T)
+    return np.unique(np.concatenate([picks, tail, [0]])).astype(np.int32)
+
+
+# --- full-size workloads -------------------------------------------------------
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_tiny_f32(seed):
+    w = WORKLOADS["tiny_f32"]
+    P.compare(w, P.gen(w, seed), w.K)
+
+
+@pytest.fixture(scope="module")
+def decode_inputs():
+    w = WORKLOADS["decode"]
+    return w, P.gen(w, 0)
+
+
+@pytest.mark.parametrize("path", [B.LMOE_PATH_AUTO, TL])
+def test_decode(decode_inputs, path):
+    w, inp = decode_inputs
+    P.compare(w, inp, w.K, path=path)
+
+
+def test_decode_seed1():
+    w = WORKLOADS["decode"]
+    P.compare(w, P.gen(w, 1), w.K)
+
+
+@pytest.mark.parametrize("path", [B.LMOE_PATH_AUTO, TL])
+def test_standard_decode(path):
+    w = WORKLOADS["standard_decode"]
+    P.compare(w, P.gen(w, 0), w.K, path=path)
+
+
+def test_prefill_sampled():
+    w = WORKLOADS["prefill"]
+    inp = P.gen(w, 0)
+    P.compare(w, inp, w.K, sample=sample_tokens(w.T, 160))
+
+
+def test_standard_prefill_sampled():
+    w = WORKLOADS["standard_prefill"]
+    inp = P.gen(w, 0)
+    P.compare(w, inp, w.K, sample=sample_tokens(w.T, 160))
+
+
+def test_skewed_sampled():
+    w = WORKLOADS["skewed"]
+    inp = P.gen(w, 0)
+    rep = P.compare(w, inp, w.K, sample=sample_tokens(w.T, 96))
+    counts = np.bincount(rep["ids"].reshape(-1), minlength=w.N)
+    P.log(f"[skew] max rows/expert {counts.max()}, empty experts {(counts == 0).sum()}")
+    assert counts.max() > 10 * w.T * w.K / w.N and (counts == 0).sum() > 0
+
+
+# --- smaller shapes: several tiles, ragged tails, both FFN paths --------------
+
+SMALL_PREFILL = Workload("small_prefill", T=1000, d=512, l=128, N=64, K=6, m=256, dtype="bf16")
+SMALL_DECODE = Workload("small_decode_m192", T=37, d=512, l=256, N=64, K=8, m=192, dtype="bf16")
+
+
+@pytest.mark.parametrize("path", [B.LMOE_PATH_AUTO, S])
+def test_small_prefill(path):
+    P.compare(SMALL_PREFILL, make_inputs(SMALL_PREFILL, 3), SMALL_PREFILL.K, path=path)
+
+
+@pytest.mark.parametrize("path", [B.LMOE_PATH_AUTO, TL])
+def test_small_decode_m192(path):
+    P.compare(SMALL_DECODE, make_inputs(SMALL_DECODE, 4), SMALL_DECODE.K, path=path)
+
+
+@pytest.mark.parametrize("w", [
+    Workload("one_token", T=1, d=256, l=64, N=16, K=3, m=128, dtype="bf16"),
+    Workload("k_is_1", T=50, d=256, l=128, N=16, K=1, m=128, dtype="bf16"),
+    Workload("k_is_n", T=20, d=256, l=64, N=8, K=8, m=64, dtype="bf16"),
+    Workload("n_37", T=70, d=192, l=64, N=37, K=5, m=128, dtype="bf16"),
+    Workload("multi_block_dispatch", T=700, d=256, l=64, N=300, K=7, m=64, dtype="bf16"),
+    Workload("many_experts", T=40, d=256, l=64, N=2048, K=64, m=64, dtype="bf16"),
+    Workload("f32_ragged", T=333, d=192, l=128, N=20, K=3, m=192, dtype="f32"),
+    Workload("f32_one_token", T=1, d=64, l=64, N=4, K=2, m=64, dtype="f32"),
+    Workload("standard_small", T=90, d=256, l=256, N=12, K=2, m=128, dtype="bf16", standard=True),
+    Workload("standard_f32", T=45, d=128, l=128, N=9, K=3, m=64, dtype="f32", standard=True),
+    Workload("biased", T=300, d=256, l=64, N=40, K=4, m=128, dtype="bf16", bias=True),
+], ids=lambda w: w.name)
+@pytest.mark.parametrize("path", [B.LMOE_PATH_AUTO, S, TL])
+def test_edge_shapes(w, path):
+    if w.dtype == "f32" and path == S:
+        pytest.skip("the streaming FFN is bf16 only")
+    P.compare(w, make_inputs(w, 5), w.K, path=path, tag=f"{w.name}/path{path}")
+
+
+def test_all_tokens_on_few_experts():
+    """A huge bias on experts 3 and 7 sends every token there: two experts of
+    T rows each, all others empty (more than 256 rows for one expert)."""
+    w = Workload("concentrated", T=400, d=256, l=128, N=32, K=2, m=128, dtype="bf16", bias=True)
+    inp = make_inputs(w, 6)
+    inp["bias"] = torch.full((w.N,), -50.0)
+    inp["bias"][3] = 50.0
+    inp["bias"][7] = 50.0
+    for path in (S, TL):
+        rep = P.compare(w, inp, w.K, path=path, tag=f"concentrated/path{path}")
+        assert set(np.unique(rep["ids"])) == {3, 7}
+
+
+# --- exact properties ----------------------------------------------------------
+
+@pytest.mark.parametrize("path", [S, TL])
+def test_zero_weights_give_x_exactly(path):
+    w = Workload("zeros", T=77, d=256, l=128, N=16, K=4, m=128, dtype="bf16")
+    inp = make_inputs(w, 7)
+    for key in ("W2", "W_up"):
+        z = dict(inp)
+        z[key] = torch.zeros_like(inp[key])
+        d = P.to_device(z)
+        out = B.forward(d, w.K, path=path)
+        torch.cuda.synchronize()
+        assert torch.equal(out.cpu(), inp["x"]), key
+
+
+def test_identity_projection_matches_standard():
+    """l = d with identity W_down and W_up runs the latent kernels and must
+    agree with the standard MoE: bit-exactly in float32 (every identity
+    product is exact); in bf16 both match the oracle (the latent path rounds
+    s to bf16 once more, so they may differ by an output ulp)."""
+    for dtype, path in (("f32", TL), ("bf16", S), ("bf16", TL)):
+        w = Workload(f"identity_{dtype}", T=64, d=128, l=128, N=8, K=2, m=64, dtype=dtype, standard=True)
+        inp = make_inputs(w, 8)
+        lat = dict(inp)
+        eye = torch.eye(w.d, dtype=w.torch_dtype)
+        lat["W_down"], lat["W_up"] = eye, eye.clone()
+        r_std = P.compare(w, inp, w.K, path=path, tag=f"identity/standard/{dtype}/path{path}")
+        r_lat = P.compare(w.replace(standard=False), lat, w.K, path=path, tag=f"identity/latent/{dtype}/path{path}")
+        assert np.array_equal(r_std["ids"], r_lat["ids"])
+        if dtype == "f32":
+            assert torch.equal(r_std["out"], r_lat["out"])
+
+
+@pytest.mark.parametrize("path", [S, TL])
+def test_deterministic(path):
+    w = Workload("det", T=200, d=512, l=128, N=64, K=6, m=128, dtype="bf16")
+    d = P.to_device(make_inputs(w, 9))
+    a = B.forward(d, w.K, path=path)
+    b = B.forward(d, w.K, path=path)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_routing_buffers_optional_and_stream_argument():
+    w = Workload("opt", T=48, d=256, l=64, N=16, K=3, m=64, dtype="bf16")
+    d = P.to_device(make_inputs(w, 10))
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o1 = B.forward(d, w.K)
+    o2, ids, gates, _ = B.forward(d, w.K, routing=True, stream=s)
+    s.synchronize()
+    assert torch.equal(o1, o2)
+    assert ids.shape == (48, 3) and torch.allclose(gates.sum(1), torch.ones(48, device="cuda"))
