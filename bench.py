@@ -127,7 +127,7 @@ def main():
         step(i)
     # Timed region: the whole forward, with HIP events recorded on the launch
     # stream only around the expert FFN (the dominant kernel).
-    ffn_end = 4 if path == B.LMOE_PATH_STREAM else 5
+    ffn_end = 5  # both FFN kernels: stages 3 and 4
     ev_ffn = None
     if not args.no_events:
         ev_ffn = []

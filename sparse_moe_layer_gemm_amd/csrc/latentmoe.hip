@@ -22,6 +22,7 @@
 #include "combine.h"
 #include "common.h"
 #include "gemm.h"
+#include "gemm2.h"
 #include "layer.h"
 #include "route.h"
 #include "stream.h"
@@ -43,6 +44,9 @@ int fail(int code, const char* fmt, ...) {
 }
 
 constexpr size_t kAlign = 256;
+
+// Tile of the large bf16 GEMM (rows x columns).
+constexpr int kG2M = 128, kG2N = 128;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 // mean rows per expert at or below which the streaming FFN is chosen
@@ -54,9 +58,9 @@ struct Plan {
     int path = LMOE_PATH_TILED;   // resolved: STREAM or TILED
     bool skinny = false;          // projections on the skinny kernel
     int tile_rows = kTileM;
-    int ms = 128;                 // streaming FFN m-slice
-    int nsplit = 1;
     int nblk = 1;                 // dispatch blocks
+    int ms = 128;                 // streaming FFN m-slice
+    int nsplit = 1;               // streaming FFN partial planes
     long long max_tiles = 0;
     size_t es = 2;
     size_t z, logits, ids, gates, counts, offsets, perm, slot_of, blk_counts, blk_offsets, tiles, n_tiles,
@@ -115,10 +119,10 @@ Plan make_plan(const lmoe_dims* dm, int32_t K) {
             p.path = (TK <= (long long)kStreamMaxMeanRows * d.N) ? LMOE_PATH_STREAM : LMOE_PATH_TILED;
         else
             p.path = d.path;
-        p.tile_rows = kTileM;
-        p.skinny = p.path == LMOE_PATH_STREAM && d.T <= kSkinnyMaxRows;
+        p.tile_rows = kG2M;
         p.ms = (d.m % 128 == 0) ? 128 : 64;
         p.nsplit = p.path == LMOE_PATH_STREAM ? d.m / p.ms : 1;
+        p.skinny = p.path == LMOE_PATH_STREAM && d.T <= kSkinnyMaxRows;
     }
     p.nblk = cdiv(d.T, kRouteTok);
     p.max_tiles = TK / p.tile_rows + std::min<long long>(d.N, TK);
@@ -169,6 +173,14 @@ void init_once() {
     });
 }
 
+template <class P>
+void launch_g2(const LayerArgs& a, int nrow_tiles, int ncol_tiles, hipStream_t st) {
+    // a whole number of tiles per XCD, so the remap in the kernel is a bijection
+    const unsigned tiles = (unsigned)nrow_tiles * (unsigned)ncol_tiles;
+    const unsigned g = (tiles + kXcds - 1) / kXcds * kXcds;
+    gemm2_kernel<P, kG2M, kG2N><<<g, dim3(256), 0, st>>>(a, nrow_tiles, ncol_tiles);
+}
+
 template <class E, class YT>
 void launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* events) {
     auto mark = [&](int i) {
@@ -182,7 +194,7 @@ void launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* events
         if (p.skinny) {
             skinny_kernel<ProjRouter<bf16>><<<cdiv(ncols_pr, 16), b1024, 0, st>>>(a);
         } else {
-            gemm_mfma_kernel<ProjRouter<bf16>><<<dim3(cdiv(a.T, kTileM), cdiv(ncols_pr, kTileN)), b256, 0, st>>>(a);
+            launch_g2<ProjRouter<bf16>>(a, cdiv(a.T, kG2M), cdiv(ncols_pr, kG2N), st);
         }
     } else {
         gemm_simt_kernel<ProjRouter<float>><<<dim3(cdiv(a.T, kSimtM), cdiv(ncols_pr, kSimtN)), b256, 0, st>>>(a);
@@ -222,9 +234,9 @@ void launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* events
                 ffn_stream_kernel<64><<<g, b256, 0, st>>>(a);
             mark(4);
         } else {
-            gemm_mfma_kernel<Ffn1<bf16>><<<dim3(mt, cdiv(a.m, kTileN)), b256, 0, st>>>(a);
+            launch_g2<Ffn1<bf16>>(a, (int)mt, cdiv(a.m, kG2N), st);
             mark(4);
-            gemm_mfma_kernel<Ffn2<bf16, YT>><<<dim3(mt, cdiv(a.l, kTileN)), b256, 0, st>>>(a);
+            launch_g2<Ffn2<bf16, YT>>(a, (int)mt, cdiv(a.l, kG2N), st);
         }
     } else {
         gemm_simt_kernel<Ffn1<float>><<<dim3(mt, cdiv(a.m, kSimtN)), b256, 0, st>>>(a);
@@ -245,7 +257,7 @@ void launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* events
             if (p.skinny)
                 skinny_kernel<Up<bf16>><<<cdiv(a.d, 16), b1024, 0, st>>>(a);
             else
-                gemm_mfma_kernel<Up<bf16>><<<dim3(cdiv(a.T, kTileM), cdiv(a.d, kTileN)), b256, 0, st>>>(a);
+                launch_g2<Up<bf16>>(a, cdiv(a.T, kG2M), cdiv(a.d, kG2N), st);
         } else {
             gemm_simt_kernel<Up<float>><<<dim3(cdiv(a.T, kSimtM), cdiv(a.d, kSimtN)), b256, 0, st>>>(a);
         }
@@ -349,7 +361,6 @@ static int forward_impl(const void* x, const void* W_down, const void* W_router,
     a.ybuf = ws + p.ybuf;
     a.s = ws + p.s;
     a.tile_rows = p.tile_rows;
-    a.nsplit = p.nsplit;
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();

@@ -42,7 +42,6 @@ struct LayerArgs {
     void* ybuf;            // expert outputs (layout depends on the path)
     void* s;               // [T, l] gate-weighted latent sum (latent mode)
     int tile_rows;         // rows per grouped-GEMM tile
-    int nsplit;            // m-slices of the streaming FFN
 };
 
 // ---------------------------------------------------------------------------

@@ -38,14 +38,11 @@ __device__ __forceinline__ uint32_t order_key(float v) {
 
 __device__ __forceinline__ int popc64(unsigned long long m) { return __popcll(m); }
 
+// Top-K of token t by one wavefront.  s_key / s_idx / s_val: 64 entries of
+// LDS private to the calling wave.
 template <int NPL>
-__global__ __launch_bounds__(256) void topk_kernel(LayerArgs a) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + wave;
-    __shared__ uint32_t s_key[4][64];
-    __shared__ int s_idx[4][64];
-    __shared__ float s_val[4][64];
-    if (t >= a.T) return;
+__device__ inline void topk_token(const LayerArgs& a, int t, uint32_t* s_key, int* s_idx, float* s_val) {
+    const int lane = threadIdx.x & 63;
     const float* lg = a.logits + (size_t)t * a.N;
     float v[NPL];
     uint32_t key[NPL];
@@ -80,9 +77,9 @@ __global__ __launch_bounds__(256) void topk_kernel(LayerArgs a) {
         const unsigned long long mt = __ballot(take);
         if (take) {
             const int pos = base + popc64(mt & below);
-            s_key[wave][pos] = key[j];
-            s_idx[wave][pos] = lane + 64 * j;
-            s_val[wave][pos] = v[j];
+            s_key[pos] = key[j];
+            s_idx[pos] = lane + 64 * j;
+            s_val[pos] = v[j];
         }
         base += popc64(mt);
     }
@@ -92,12 +89,12 @@ __global__ __launch_bounds__(256) void topk_kernel(LayerArgs a) {
     float my_v = -INFINITY;
     int my_rank = 0, my_idx = 0;
     if (lane < K) {
-        const uint32_t mk = s_key[wave][lane];
-        my_idx = s_idx[wave][lane];
-        my_v = s_val[wave][lane];
+        const uint32_t mk = s_key[lane];
+        my_idx = s_idx[lane];
+        my_v = s_val[lane];
         for (int q = 0; q < K; ++q) {
-            const uint32_t qk = s_key[wave][q];
-            my_rank += (qk > mk || (qk == mk && s_idx[wave][q] < my_idx)) ? 1 : 0;
+            const uint32_t qk = s_key[q];
+            my_rank += (qk > mk || (qk == mk && s_idx[q] < my_idx)) ? 1 : 0;
         }
     }
     float mx = my_v;
@@ -111,6 +108,18 @@ __global__ __launch_bounds__(256) void topk_kernel(LayerArgs a) {
         a.ids[(size_t)t * K + my_rank] = my_idx;
         a.gates[(size_t)t * K + my_rank] = ex / sum;
     }
+    __builtin_amdgcn_wave_barrier();
+}
+
+template <int NPL>
+__global__ __launch_bounds__(256) void topk_kernel(LayerArgs a) {
+    const int wave = threadIdx.x >> 6;
+    const int t = blockIdx.x * 4 + wave;
+    __shared__ uint32_t s_key[4][64];
+    __shared__ int s_idx[4][64];
+    __shared__ float s_val[4][64];
+    if (t >= a.T) return;
+    topk_token<NPL>(a, t, s_key[wave], s_idx[wave], s_val[wave]);
 }
 
 // --- dispatch helpers --------------------------------------------------------
