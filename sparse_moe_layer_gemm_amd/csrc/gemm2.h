@@ -11,8 +11,10 @@
 // per lane and stores 4 columns at a time.
 //
 // Pipeline: global -> registers two k-tiles ahead, registers -> LDS one
-// k-tile ahead (two LDS buffers), the LDS writes of the next k-tile issued
-// between the MFMA groups of the current one.  LDS rows are 64 bf16 = 8
+// k-tile ahead (two LDS buffers).  In MFMA groups 0 and 1 of a k-tile,
+// group g writes parts 2g and 2g+1 of the next k-tile to LDS and then loads
+// the same parts of the k-tile after it into the freed registers, so each
+// load is at least two groups old when the next k-tile starts.  LDS rows are 64 bf16 = 8
 // units of 16 bytes; unit c of row r is stored at c ^ (r & 7), so the
 // 16-byte reads of 8 consecutive rows hit distinct bank groups.
 //
@@ -152,14 +154,16 @@ __global__ __launch_bounds__(256) void gemm2_kernel(LayerArgs a, int nrow_tiles,
     // so that part q of the next k-tile can go to LDS, and part q of the
     // k-tile after it can be loaded, right after MFMA group q.
     auto in_part = [](int i, int n, int q) { return n >= 4 ? (i % 4 == q) : (q == 0); };
-    auto gload_part = [&](int kt, int q) {
+    // the loads of a k-tile are issued during the first two MFMA groups, so
+    // that they are at least two groups old when the next k-tile starts
+    auto gload_group = [&](int kt, int g) {
         const int k0 = kt * kG2K;
 #pragma unroll
         for (int i = 0; i < S::LA; ++i)
-            if (in_part(i, S::LA, q)) ra[i] = ldg16(ap[i] + k0);
+            if (in_part(i, S::LA, 2 * g) || in_part(i, S::LA, 2 * g + 1)) ra[i] = ldg16(ap[i] + k0);
 #pragma unroll
         for (int i = 0; i < S::LB; ++i)
-            if (in_part(i, S::LB, q)) rb[i] = ldg16(bp[i] + k0);
+            if (in_part(i, S::LB, 2 * g) || in_part(i, S::LB, 2 * g + 1)) rb[i] = ldg16(bp[i] + k0);
     };
     auto swrite_part = [&](int st, int q) {
 #pragma unroll
@@ -186,41 +190,57 @@ __global__ __launch_bounds__(256) void gemm2_kernel(LayerArgs a, int nrow_tiles,
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-#pragma unroll
-    for (int q = 0; q < 4; ++q) gload_part(0, q);
+    gload_group(0, 0);
+    gload_group(0, 1);
 #pragma unroll
     for (int q = 0; q < 4; ++q) swrite_part(0, q);
     __syncthreads();
-#pragma unroll
-    for (int q = 0; q < 4; ++q) gload_part(min(1, nk - 1), q);
+    gload_group(min(1, nk - 1), 0);
+    gload_group(min(1, nk - 1), 1);
 
+    // Fragments of MFMA group kk+1 are read from LDS before the MFMAs of
+    // group kk are issued (two register sets), so LDS latency overlaps them.
+    auto read_frags = [&](int st, int kk, bf16x8* af, bf16x8* bfr) {
+        const int chunk = kk * 2 + (lane >> 5);
+#pragma unroll
+        for (int i = 0; i < S::FM; ++i) {
+            const int r = wm * S::WM + i * 32 + (lane & 31);
+            af[i] = as_bf16x8(As[st][r * 8 + (chunk ^ (r & 7))]);
+        }
+#pragma unroll
+        for (int j = 0; j < S::FN; ++j) {
+            const int c = wn * S::WN + j * 32 + (lane & 31);
+            bfr[j] = as_bf16x8(Bs[st][c * 8 + (chunk ^ (c & 7))]);
+        }
+    };
+    auto mfma_group = [&](const bf16x8* af, const bf16x8* bfr) {
+#pragma unroll
+        for (int i = 0; i < S::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < S::FN; ++j) acc[i][j] = mfma32(bfr[j], af[i], acc[i][j]);
+    };
     for (int kt = 0; kt < nk; ++kt) {
         const int st = kt & 1;
         // the loop body is straight-line: the last iterations stage and load
         // a clamped k-tile that is never read
         const int kpre = min(kt + 2, nk - 1);
+        bf16x8 a0[S::FM], b0[S::FN], a1[S::FM], b1[S::FN];
+        read_frags(st, 0, a0, b0);
 #pragma unroll
         for (int kk = 0; kk < kG2K / 16; ++kk) {
-            const int chunk = kk * 2 + (lane >> 5);
-            bf16x8 af[S::FM], bfr[S::FN];
-#pragma unroll
-            for (int i = 0; i < S::FM; ++i) {
-                const int r = wm * S::WM + i * 32 + (lane & 31);
-                af[i] = as_bf16x8(As[st][r * 8 + (chunk ^ (r & 7))]);
+            bf16x8* ac = (kk & 1) ? a1 : a0;
+            bf16x8* bc = (kk & 1) ? b1 : b0;
+            bf16x8* an = (kk & 1) ? a0 : a1;
+            bf16x8* bn = (kk & 1) ? b0 : b1;
+            if (kk + 1 < kG2K / 16) read_frags(st, kk + 1, an, bn);
+            if (kk < 2) {
+                // parts 2kk, 2kk+1 of k-tile kt+1 go to LDS, then the same
+                // registers take parts 2kk, 2kk+1 of k-tile kt+2
+                swrite_part(st ^ 1, 2 * kk);
+                swrite_part(st ^ 1, 2 * kk + 1);
+                gload_group(kpre, kk);
             }
-#pragma unroll
-            for (int j = 0; j < S::FN; ++j) {
-                const int c = wn * S::WN + j * 32 + (lane & 31);
-                bfr[j] = as_bf16x8(Bs[st][c * 8 + (chunk ^ (c & 7))]);
-            }
-#pragma unroll
-            for (int i = 0; i < S::FM; ++i)
-#pragma unroll
-                for (int j = 0; j < S::FN; ++j) acc[i][j] = mfma32(bfr[j], af[i], acc[i][j]);
-            swrite_part(st ^ 1, kk);  // part kk of k-tile kt+1
-            gload_part(kpre, kk);     // part kk of k-tile kt+2
-            // keep each part's loads here: issued one whole k-tile before the
-            // LDS write that needs them
+            mfma_group(ac, bc);
             __builtin_amdgcn_sched_barrier(0);
         }
         __syncthreads();

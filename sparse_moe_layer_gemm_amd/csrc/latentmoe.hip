@@ -57,7 +57,7 @@ struct Plan {
     bool bf16 = false;
     int path = LMOE_PATH_TILED;   // resolved: STREAM or TILED
     bool skinny = false;          // projections on the skinny kernel
-    int tile_rows = kTileM;
+    int tile_rows = kG2M;
     int nblk = 1;                 // dispatch blocks
     int ms = 128;                 // streaming FFN m-slice
     int nsplit = 1;               // streaming FFN partial planes
