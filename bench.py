@@ -169,6 +169,7 @@ def main():
         roof = {"kernel": "gemm_mfma_kernel<Ffn1>+<Ffn2>", "bound": "mfma",
                 "achieved": ffn_flops / (ffn_us * 1e-6) / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "traffic": None}
+    roof["traffic"] = measured_traffic(w, roof["kernel"])
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["kernel_us"] = ffn_us
     roof["copy_GBps_measured"] = copy_gbs
@@ -201,6 +202,23 @@ def main():
                   "roofline_frac": layer_frac, "stage_us": stages},
     }
     print(json.dumps(line), flush=True)
+
+
+def measured_traffic(w, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, each scaled by the same counter on a
+    copy of known size), or None when there is none for this workload or the
+    kernel's sources changed since the counters were taken."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "ffn_stream_decode_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel") != kernel or rec.get("workload") != w.name:
+        return None
+    h = hashlib.sha256(b"".join(open(os.path.join(ROOT, p), "rb").read() for p in rec["sources"])).hexdigest()
+    return rec["traffic_bytes_per_launch"] if h == rec["sources_sha256"] else None
 
 
 def copy_bandwidth(torch, dev, nbytes: int = 1 << 30, reps: int = 10) -> float:
