@@ -45,8 +45,19 @@ int fail(int code, const char* fmt, ...) {
 
 constexpr size_t kAlign = 256;
 
-// Tile of the large bf16 GEMM (rows x columns).
-constexpr int kG2M = 128, kG2N = 128;
+// Tiled bf16 GEMM shapes: rows x columns per workgroup and its wave grid.
+template <int BM_, int BN_, int NWM_, int NWN_>
+struct G2Cfg {
+    static constexpr int BM = BM_, BN = BN_, NWM = NWM_, NWN = NWN_;
+};
+using G2Large = G2Cfg<256, 256, 2, 4>;   // 8 waves, 1 workgroup per CU
+using G2Small = G2Cfg<128, 128, 2, 2>;   // 4 waves, 2 workgroups per CU
+// The expert FFN takes the large tile when experts hold many rows on average
+// (the tile list, shared by both FFN GEMMs, is cut at that height); with few
+// rows per expert the 256-row tile would be mostly padding.
+constexpr int kFfnLargeMinMeanRows = 512;
+using ProjTile = G2Small;
+using UpTile = G2Large;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 // mean rows per expert at or below which the streaming FFN is chosen
@@ -57,7 +68,8 @@ struct Plan {
     bool bf16 = false;
     int path = LMOE_PATH_TILED;   // resolved: STREAM or TILED
     bool skinny = false;          // projections on the skinny kernel
-    int tile_rows = kG2M;
+    int tile_rows = G2Small::BM;
+    bool ffn_large = false;       // tiled FFN on G2Large
     int nblk = 1;                 // dispatch blocks
     int ms = 128;                 // streaming FFN m-slice
     int nsplit = 1;               // streaming FFN partial planes
@@ -119,7 +131,8 @@ Plan make_plan(const lmoe_dims* dm, int32_t K) {
             p.path = (TK <= (long long)kStreamMaxMeanRows * d.N) ? LMOE_PATH_STREAM : LMOE_PATH_TILED;
         else
             p.path = d.path;
-        p.tile_rows = kG2M;
+        p.ffn_large = TK >= (long long)kFfnLargeMinMeanRows * d.N;
+        p.tile_rows = p.ffn_large ? G2Large::BM : G2Small::BM;
         p.ms = (d.m % 128 == 0) ? 128 : 64;
         p.nsplit = p.path == LMOE_PATH_STREAM ? d.m / p.ms : 1;
         p.skinny = p.path == LMOE_PATH_STREAM && d.T <= kSkinnyMaxRows;
@@ -173,12 +186,13 @@ void init_once() {
     });
 }
 
-template <class P>
+template <class P, class C>
 void launch_g2(const LayerArgs& a, int nrow_tiles, int ncol_tiles, hipStream_t st) {
     // a whole number of tiles per XCD, so the remap in the kernel is a bijection
     const unsigned tiles = (unsigned)nrow_tiles * (unsigned)ncol_tiles;
     const unsigned g = (tiles + kXcds - 1) / kXcds * kXcds;
-    gemm2_kernel<P, kG2M, kG2N><<<g, dim3(256), 0, st>>>(a, nrow_tiles, ncol_tiles);
+    gemm2_kernel<P, C::BM, C::BN, C::NWM, C::NWN><<<g, dim3(64 * C::NWM * C::NWN), 0, st>>>(a, nrow_tiles,
+                                                                                          ncol_tiles);
 }
 
 template <class E, class YT>
@@ -194,7 +208,7 @@ void launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* events
         if (p.skinny) {
             skinny_kernel<ProjRouter<bf16>><<<cdiv(ncols_pr, 16), b1024, 0, st>>>(a);
         } else {
-            launch_g2<ProjRouter<bf16>>(a, cdiv(a.T, kG2M), cdiv(ncols_pr, kG2N), st);
+            launch_g2<ProjRouter<bf16>, ProjTile>(a, cdiv(a.T, ProjTile::BM), cdiv(ncols_pr, ProjTile::BN), st);
         }
     } else {
         gemm_simt_kernel<ProjRouter<float>><<<dim3(cdiv(a.T, kSimtM), cdiv(ncols_pr, kSimtN)), b256, 0, st>>>(a);
@@ -234,9 +248,15 @@ void launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* events
                 ffn_stream_kernel<64><<<g, b256, 0, st>>>(a);
             mark(4);
         } else {
-            launch_g2<Ffn1<bf16>>(a, (int)mt, cdiv(a.m, kG2N), st);
-            mark(4);
-            launch_g2<Ffn2<bf16, YT>>(a, (int)mt, cdiv(a.l, kG2N), st);
+            if (p.ffn_large) {
+                launch_g2<Ffn1<bf16>, G2Large>(a, (int)mt, cdiv(a.m, G2Large::BN), st);
+                mark(4);
+                launch_g2<Ffn2<bf16, YT>, G2Large>(a, (int)mt, cdiv(a.l, G2Large::BN), st);
+            } else {
+                launch_g2<Ffn1<bf16>, G2Small>(a, (int)mt, cdiv(a.m, G2Small::BN), st);
+                mark(4);
+                launch_g2<Ffn2<bf16, YT>, G2Small>(a, (int)mt, cdiv(a.l, G2Small::BN), st);
+            }
         }
     } else {
         gemm_simt_kernel<Ffn1<float>><<<dim3(mt, cdiv(a.m, kSimtN)), b256, 0, st>>>(a);
@@ -257,7 +277,7 @@ void launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* events
             if (p.skinny)
                 skinny_kernel<Up<bf16>><<<cdiv(a.d, 16), b1024, 0, st>>>(a);
             else
-                launch_g2<Up<bf16>>(a, cdiv(a.T, kG2M), cdiv(a.d, kG2N), st);
+                launch_g2<Up<bf16>, UpTile>(a, cdiv(a.T, UpTile::BM), cdiv(a.d, UpTile::BN), st);
         } else {
             gemm_simt_kernel<Up<float>><<<dim3(cdiv(a.T, kSimtM), cdiv(a.d, kSimtN)), b256, 0, st>>>(a);
         }

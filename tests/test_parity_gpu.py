@@ -106,6 +106,10 @@ def test_small_decode_m192(path):
     Workload("standard_small", T=90, d=256, l=256, N=12, K=2, m=128, dtype="bf16", standard=True),
     Workload("standard_f32", T=45, d=128, l=128, N=9, K=3, m=64, dtype="f32", standard=True),
     Workload("biased", T=300, d=256, l=64, N=40, K=4, m=128, dtype="bf16", bias=True),
+    # >= 512 rows per expert on average: the FFN runs on 256 x 256 tiles, here
+    # with ragged rows (~750 per expert), ragged FFN columns (m = 320, l = 192)
+    # and a ragged up-projection (T = 1500, d = 320)
+    Workload("large_tile_ragged", T=1500, d=320, l=192, N=4, K=2, m=320, dtype="bf16"),
 ], ids=lambda w: w.name)
 @pytest.mark.parametrize("path", [B.LMOE_PATH_AUTO, S, TL])
 def test_edge_shapes(w, path):
