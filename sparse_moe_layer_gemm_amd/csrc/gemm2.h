@@ -141,11 +141,16 @@ struct RowCtx<Up<bf16>> {
 template <class P, int BM, int BN, int NWM, int NWN>
 __global__ __launch_bounds__(64 * NWM * NWN) void gemm2_kernel(LayerArgs a, int nrow_tiles, int ncol_tiles) {
     using S = G2Shape<BM, BN, NWM, NWN>;
-    // XCD-aware remap of the workgroup id to a logical tile; the grid is
-    // kXcds * per_xcd workgroups, so every logical tile gets exactly one.
-    const int G = nrow_tiles * ncol_tiles;
+    // XCD-aware remap of the workgroup id to a logical tile.  The grid holds
+    // kXcds * ceil(bound / kXcds) workgroups for the host's bound on the tile
+    // count; the remap spreads the actual count (the tile list's length for
+    // the FFN) over the 8 XCDs, so no XCD is left with only empty tiles, and
+    // every logical tile still gets exactly one workgroup.
+    const int G = P::row_tiles(a, nrow_tiles) * ncol_tiles;
     const int per_xcd = (G + kXcds - 1) / kXcds;
-    const int logical = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+    const int slot = blockIdx.x / kXcds;
+    if (slot >= per_xcd) return;
+    const int logical = (blockIdx.x % kXcds) * per_xcd + slot;
     if (logical >= G) return;
     const int rt = logical / ncol_tiles, ct = logical % ncol_tiles;
     int grp, row0, row_end;

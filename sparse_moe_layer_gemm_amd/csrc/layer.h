@@ -56,6 +56,8 @@ struct ProjRouter {
         row_end = a.T;
         return row0 < row_end;
     }
+    // row tiles of this launch: the host's count
+    __device__ static int row_tiles(const LayerArgs&, int host_count) { return host_count; }
     __device__ static int ncols(const LayerArgs& a) { return (a.standard ? 0 : a.l) + a.N; }
     __device__ static int kdim(const LayerArgs& a) { return a.d; }
     __device__ static const E* a_row(const LayerArgs& a, int, int r) {
@@ -89,6 +91,8 @@ struct Ffn1 {
         row_end = a.offsets[grp + 1];
         return true;
     }
+    // the tile list's length, known only on the device (the host passes a bound)
+    __device__ static int row_tiles(const LayerArgs& a, int) { return *a.n_tiles; }
     __device__ static int ncols(const LayerArgs& a) { return a.m; }
     __device__ static int kdim(const LayerArgs& a) { return a.l; }
     __device__ static const E* a_row(const LayerArgs& a, int, int slot) {
@@ -111,6 +115,7 @@ struct Ffn2 {
     __device__ static bool tile(const LayerArgs& a, int bx, int bm, int& grp, int& row0, int& row_end) {
         return Ffn1<E>::tile(a, bx, bm, grp, row0, row_end);
     }
+    __device__ static int row_tiles(const LayerArgs& a, int b) { return Ffn1<E>::row_tiles(a, b); }
     __device__ static int ncols(const LayerArgs& a) { return a.l; }
     __device__ static int kdim(const LayerArgs& a) { return a.m; }
     __device__ static const E* a_row(const LayerArgs& a, int, int slot) {
@@ -134,6 +139,7 @@ struct Up {
         row_end = a.T;
         return row0 < row_end;
     }
+    __device__ static int row_tiles(const LayerArgs&, int host_count) { return host_count; }
     __device__ static int ncols(const LayerArgs& a) { return a.d; }
     __device__ static int kdim(const LayerArgs& a) { return a.l; }
     __device__ static const E* a_row(const LayerArgs& a, int, int r) {
