@@ -65,17 +65,27 @@ __device__ __forceinline__ void store_cols(E* dst, int c0, int ncols, const f32x
     }
 }
 
-// Per-problem epilogue of 4 consecutive columns c0 .. c0+3 of one row:
-// load() fetches what the row contributes (bias, gate, residual) and store()
-// applies it and writes.  All load()s of a thread are issued before its
-// first store(), so they overlap instead of each waiting behind the stores
-// that the compiler cannot prove disjoint from them.
+// Per-problem epilogue of 4 consecutive columns c0 .. c0+3 of one row.
+// Loads in the epilogue sit behind the tile's stores in the one vector
+// memory counter, so a load issued after a store waits for that store to
+// complete.  The operands are therefore loaded early:
+//   row_value(): one float per row (the gate), loaded by one thread per row
+//     when the tile starts and passed through LDS (kRowVal);
+//   col_load():  per-column data of the thread's 4 columns (the router
+//     bias), loaded when the tile starts;
+//   load():      per-element data (the residual), loaded for all passes of
+//     an epilogue round before the round's first store.
+struct NoPre {};
+
 template <class P>
 struct RowCtx;
 
 template <>
 struct RowCtx<ProjRouter<bf16>> {
-    __device__ static f32x4 load(const LayerArgs& a, int, int, int c0) {
+    static constexpr bool kRowVal = false;
+    __device__ static float row_value(const LayerArgs&, int, int) { return 0.0f; }
+    using ColPre = f32x4;
+    __device__ static f32x4 col_load(const LayerArgs& a, int c0) {
         f32x4 b = {0.0f, 0.0f, 0.0f, 0.0f};
         const int e0 = c0 - (a.standard ? 0 : a.l);
         if (a.bias && e0 >= 0)
@@ -83,7 +93,10 @@ struct RowCtx<ProjRouter<bf16>> {
                 if (e0 + i < a.N) b[i] = a.bias[e0 + i];
         return b;
     }
-    __device__ static void store(const LayerArgs& a, int, int r, int c0, f32x4 v, const f32x4& b) {
+    using Pre = NoPre;
+    __device__ static NoPre load(const LayerArgs&, int, int, int) { return NoPre{}; }
+    __device__ static void store(const LayerArgs& a, int, int r, int c0, f32x4 v, const NoPre&, const f32x4& b,
+                                 float) {
         const int lz = a.standard ? 0 : a.l;
         if (c0 < lz) {
             store_cols(static_cast<bf16*>(a.z_w) + (size_t)r * a.l + c0, c0, lz, v);
@@ -96,8 +109,14 @@ struct RowCtx<ProjRouter<bf16>> {
 
 template <>
 struct RowCtx<Ffn1<bf16>> {
-    __device__ static f32x4 load(const LayerArgs&, int, int, int) { return f32x4{}; }
-    __device__ static void store(const LayerArgs& a, int, int slot, int c0, f32x4 v, const f32x4&) {
+    static constexpr bool kRowVal = false;
+    __device__ static float row_value(const LayerArgs&, int, int) { return 0.0f; }
+    using ColPre = NoPre;
+    __device__ static NoPre col_load(const LayerArgs&, int) { return NoPre{}; }
+    using Pre = NoPre;
+    __device__ static NoPre load(const LayerArgs&, int, int, int) { return NoPre{}; }
+    __device__ static void store(const LayerArgs& a, int, int slot, int c0, f32x4 v, const NoPre&, const NoPre&,
+                                 float) {
         for (int i = 0; i < 4; ++i) {
             const float t = v[i] > 0.0f ? v[i] : 0.0f;
             v[i] = t * t;
@@ -108,94 +127,123 @@ struct RowCtx<Ffn1<bf16>> {
 
 template <>
 struct RowCtx<Ffn2<bf16, bf16>> {
-    __device__ static f32x4 load(const LayerArgs& a, int, int slot, int) {
-        const float g = a.gates[a.perm[slot]];
-        return f32x4{g, g, g, g};
-    }
-    __device__ static void store(const LayerArgs& a, int, int slot, int c0, f32x4 v, const f32x4& g) {
+    static constexpr bool kRowVal = true;   // the slot's gate
+    __device__ static float row_value(const LayerArgs& a, int, int slot) { return a.gates[a.perm[slot]]; }
+    using ColPre = NoPre;
+    __device__ static NoPre col_load(const LayerArgs&, int) { return NoPre{}; }
+    using Pre = NoPre;
+    __device__ static NoPre load(const LayerArgs&, int, int, int) { return NoPre{}; }
+    __device__ static void store(const LayerArgs& a, int, int slot, int c0, f32x4 v, const NoPre&, const NoPre&,
+                                 float g) {
         store_cols(static_cast<bf16*>(a.ybuf) + (size_t)slot * a.l + c0, c0, a.l, v * g);
     }
 };
 
 template <>
 struct RowCtx<Up<bf16>> {
-    __device__ static f32x4 load(const LayerArgs& a, int, int r, int c0) {
-        const bf16* xr = static_cast<const bf16*>(a.x) + (size_t)r * a.d + c0;
-        f32x4 x;
-        if (c0 + 3 < a.d) {
-            const uint2 u = *reinterpret_cast<const uint2*>(xr);
-            x[0] = __uint_as_float(u.x << 16);
-            x[1] = __uint_as_float(u.x & 0xffff0000u);
-            x[2] = __uint_as_float(u.y << 16);
-            x[3] = __uint_as_float(u.y & 0xffff0000u);
-        } else {
-            for (int i = 0; i < 4; ++i) x[i] = c0 + i < a.d ? (float)xr[i] : 0.0f;
-        }
-        return x;
+    static constexpr bool kRowVal = false;
+    __device__ static float row_value(const LayerArgs&, int, int) { return 0.0f; }
+    using ColPre = NoPre;
+    __device__ static NoPre col_load(const LayerArgs&, int) { return NoPre{}; }
+    using Pre = uint2;   // 4 bf16 of the residual row (d is a multiple of 64, so never ragged)
+    __device__ static uint2 load(const LayerArgs& a, int, int r, int c0) {
+        return *reinterpret_cast<const uint2*>(static_cast<const bf16*>(a.x) + (size_t)r * a.d + c0);
     }
-    __device__ static void store(const LayerArgs& a, int, int r, int c0, f32x4 v, const f32x4& x) {
-        store_cols(static_cast<bf16*>(a.out) + (size_t)r * a.d + c0, c0, a.d, v + x);
+    __device__ static void store(const LayerArgs& a, int, int r, int c0, f32x4 v, const uint2& u, const NoPre&,
+                                 float) {
+        v[0] += __uint_as_float(u.x << 16);
+        v[1] += __uint_as_float(u.x & 0xffff0000u);
+        v[2] += __uint_as_float(u.y << 16);
+        v[3] += __uint_as_float(u.y & 0xffff0000u);
+        store_cols(static_cast<bf16*>(a.out) + (size_t)r * a.d + c0, c0, a.d, v);
     }
 };
 
 template <class P, int BM, int BN, int NWM, int NWN>
 __global__ __launch_bounds__(64 * NWM * NWN) void gemm2_kernel(LayerArgs a, int nrow_tiles, int ncol_tiles) {
     using S = G2Shape<BM, BN, NWM, NWN>;
-    // XCD-aware remap of the workgroup id to a logical tile.  The grid holds
-    // kXcds * ceil(bound / kXcds) workgroups for the host's bound on the tile
-    // count; the remap spreads the actual count (the tile list's length for
-    // the FFN) over the 8 XCDs, so no XCD is left with only empty tiles, and
-    // every logical tile still gets exactly one workgroup.
+    // Persistent workgroups.  Logical tiles (row-tile-major) are split into
+    // 8 contiguous ranges, one per XCD (workgroup b runs on XCD b % 8); the
+    // gridDim / 8 workgroups of an XCD take its range's tiles round robin,
+    // so the tiles in flight on an XCD at any time are neighbours (the rows
+    // of one expert against all its weight columns) and share that XCD's
+    // L2.  The actual tile count is read on the device for the FFN (the
+    // host only knows a bound).
     const int G = P::row_tiles(a, nrow_tiles) * ncol_tiles;
     const int per_xcd = (G + kXcds - 1) / kXcds;
-    const int slot = blockIdx.x / kXcds;
-    if (slot >= per_xcd) return;
-    const int logical = (blockIdx.x % kXcds) * per_xcd + slot;
-    if (logical >= G) return;
-    const int rt = logical / ncol_tiles, ct = logical % ncol_tiles;
-    int grp, row0, row_end;
-    if (!P::tile(a, rt, BM, grp, row0, row_end)) return;
-    const int col0 = ct * BN;
+    const int xcd = blockIdx.x % kXcds, nslot = gridDim.x / kXcds;
     const int ncols = P::ncols(a);
-    if (col0 >= ncols) return;
-    const int K = P::kdim(a);
-    const int nk = K / kG2K;
+    const int nk = P::kdim(a) / kG2K;
+    struct Tile {
+        int grp, row0, row_end, col0;
+    };
+    auto tile_at = [&](int slot, Tile& t) -> bool {
+        if (slot >= per_xcd) return false;
+        const int logical = xcd * per_xcd + slot;
+        if (logical >= G) return false;
+        if (!P::tile(a, logical / ncol_tiles, BM, t.grp, t.row0, t.row_end)) return false;
+        t.col0 = (logical % ncol_tiles) * BN;
+        return t.col0 < ncols;
+    };
 
-    // two LDS stages of both operands; after the k-loop the same memory
-    // stages the output tile
-    constexpr int kStageU4 = 2 * (BM + BN) * 8;
-    __shared__ uint4 smem[kStageU4];
-    uint4(*As)[BM * 8] = reinterpret_cast<uint4(*)[BM * 8]>(smem);
-    uint4(*Bs)[BN * 8] = reinterpret_cast<uint4(*)[BN * 8]>(smem + 2 * BM * 8);
+    // Two LDS stages, each [A rows | B rows] contiguous; after a tile's last
+    // k-step its stage also stages the output tile.
+    constexpr int kStageU4 = (BM + BN) * 8;
+    __shared__ uint4 smem[2 * kStageU4];
+    __shared__ float rowval[RowCtx<P>::kRowVal ? BM : 1];
+    auto As = [&](int st) { return smem + st * kStageU4; };
+    auto Bs = [&](int st) { return smem + st * kStageU4 + BM * 8; };
 
     const int tid = threadIdx.x;
     const int ch = tid & 7;   // 16-byte unit within a row's k-slice
     const int lrow = tid >> 3;
-    // Rows past the tile's end (and columns past ncols) read a valid row
+
+    // The load cursor runs two k-steps ahead of the MFMAs, across tile
+    // boundaries: (lslot, lkt) is the next k-step to load, ap/bp its rows.
+    // Rows past a tile's end (and columns past ncols) read a valid row
     // instead: each output element depends only on its own row and column,
     // and those outputs are never stored.  No load is conditional, so the
     // compiler can count the loads in flight exactly.
+    int lslot = blockIdx.x / kXcds, lkt = 0;
+    Tile ct;  // the tile the MFMAs work on
+    if (!tile_at(lslot, ct)) return;
+    int cslot = lslot;
     const bf16* ap[S::LA];
     const bf16* bp[S::LB];
+    auto set_rows = [&](const Tile& t) {
 #pragma unroll
-    for (int i = 0; i < S::LA; ++i) {
-        const int r = row0 + lrow + S::RSTEP * i;
-        ap[i] = P::a_row(a, grp, r < row_end ? r : row0) + ch * 8;
-    }
+        for (int i = 0; i < S::LA; ++i) {
+            const int r = t.row0 + lrow + S::RSTEP * i;
+            ap[i] = P::a_row(a, t.grp, r < t.row_end ? r : t.row0) + ch * 8;
+        }
 #pragma unroll
-    for (int i = 0; i < S::LB; ++i) {
-        const int c = col0 + lrow + S::RSTEP * i;
-        bp[i] = P::b_row(a, grp, c < ncols ? c : col0) + ch * 8;
-    }
+        for (int i = 0; i < S::LB; ++i) {
+            const int c = t.col0 + lrow + S::RSTEP * i;
+            bp[i] = P::b_row(a, t.grp, c < ncols ? c : t.col0) + ch * 8;
+        }
+    };
+    set_rows(ct);
+    // past the last tile the cursor stays on a valid k-step that is loaded
+    // again and never used
+    auto advance_load = [&]() {
+        if (++lkt < nk) return;
+        Tile nt;
+        if (tile_at(lslot + nslot, nt)) {
+            lslot += nslot;
+            lkt = 0;
+            set_rows(nt);
+        } else {
+            lkt = nk - 1;
+        }
+    };
+
     uint4 ra[S::LA], rb[S::LB];
     // Staged loads are split in 4 parts (load index i belongs to part i % 4),
-    // so that part q of the next k-tile can go to LDS, and part q of the
-    // k-tile after it can be loaded, right after MFMA group q.
+    // so that part q of the next k-step can go to LDS, and part q of the
+    // k-step after it can be loaded, right after MFMA group q.
     auto in_part = [](int i, int n, int q) { return n >= 4 ? (i % 4 == q) : (q == 0); };
-    // the loads of a k-tile are issued during the first two MFMA groups, so
-    // that they are at least two groups old when the next k-tile starts
-    auto gload_group = [&](int kt, int g) {
-        const int k0 = kt * kG2K;
+    auto gload_group = [&](int g) {
+        const int k0 = lkt * kG2K;
 #pragma unroll
         for (int i = 0; i < S::LA; ++i)
             if (in_part(i, S::LA, 2 * g) || in_part(i, S::LA, 2 * g + 1)) ra[i] = ldg16(ap[i] + k0);
@@ -204,51 +252,61 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm2_kernel(LayerArgs a, int 
             if (in_part(i, S::LB, 2 * g) || in_part(i, S::LB, 2 * g + 1)) rb[i] = ldg16(bp[i] + k0);
     };
     auto swrite_part = [&](int st, int q) {
+        uint4* as = As(st);
+        uint4* bs = Bs(st);
 #pragma unroll
         for (int i = 0; i < S::LA; ++i)
             if (in_part(i, S::LA, q)) {
                 const int r = lrow + S::RSTEP * i;
-                As[st][r * 8 + (ch ^ g2_swz(r))] = ra[i];
+                as[r * 8 + (ch ^ g2_swz(r))] = ra[i];
             }
 #pragma unroll
         for (int i = 0; i < S::LB; ++i)
             if (in_part(i, S::LB, q)) {
                 const int r = lrow + S::RSTEP * i;
-                Bs[st][r * 8 + (ch ^ g2_swz(r))] = rb[i];
+                bs[r * 8 + (ch ^ g2_swz(r))] = rb[i];
             }
     };
 
     const int wave = tid >> 6, lane = tid & 63;
     const int wm = wave / NWN, wn = wave % NWN;
     f32x16 acc[S::FM][S::FN];
+    auto zero_acc = [&]() {
 #pragma unroll
-    for (int i = 0; i < S::FM; ++i)
+        for (int i = 0; i < S::FM; ++i)
 #pragma unroll
-        for (int j = 0; j < S::FN; ++j)
+            for (int j = 0; j < S::FN; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    };
+    zero_acc();
 
-    gload_group(0, 0);
-    gload_group(0, 1);
+    // prologue: k-step 0 into stage 0, k-step 1 into the registers
+    gload_group(0);
+    gload_group(1);
+    advance_load();
 #pragma unroll
     for (int q = 0; q < 4; ++q) swrite_part(0, q);
     __syncthreads();
-    gload_group(min(1, nk - 1), 0);
-    gload_group(min(1, nk - 1), 1);
+    gload_group(0);
+    gload_group(1);
+    advance_load();
 
     // Fragments of MFMA group kk+1 are read from LDS before the MFMAs of
     // group kk are issued (two register sets), so LDS latency overlaps them.
     auto read_frags = [&](int st, int kk, bf16x8* af, bf16x8* bfr) {
         const int chunk = kk * 2 + (lane >> 5);
+        const uint4* as = As(st);
+        const uint4* bs = Bs(st);
 #pragma unroll
         for (int i = 0; i < S::FM; ++i) {
             const int r = wm * S::WM + i * 32 + (lane & 31);
-            af[i] = as_bf16x8(As[st][r * 8 + (chunk ^ g2_swz(r))]);
+            af[i] = as_bf16x8(as[r * 8 + (chunk ^ g2_swz(r))]);
         }
 #pragma unroll
         for (int j = 0; j < S::FN; ++j) {
             const int c = wn * S::WN + j * 32 + (lane & 31);
-            bfr[j] = as_bf16x8(Bs[st][c * 8 + (chunk ^ g2_swz(c))]);
+            bfr[j] = as_bf16x8(bs[c * 8 + (chunk ^ g2_swz(c))]);
         }
     };
     auto mfma_group = [&](const bf16x8* af, const bf16x8* bfr) {
@@ -257,11 +315,86 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm2_kernel(LayerArgs a, int 
 #pragma unroll
             for (int j = 0; j < S::FN; ++j) acc[i][j] = mfma32(bfr[j], af[i], acc[i][j]);
     };
-    for (int kt = 0; kt < nk; ++kt) {
-        const int st = kt & 1;
-        // the loop body is straight-line: the last iterations stage and load
-        // a clamped k-tile that is never read
-        const int kpre = min(kt + 2, nk - 1);
+
+    // Epilogue of tile ct from stage st (free once its last k-step is done;
+    // the other stage already holds the next tile's first k-step).  The
+    // fp32 tile goes through LDS row-major, in rounds of kEpiRows rows
+    // (16-byte unit u of local row r at u ^ (r & 15), so 16 lanes on 16 rows
+    // of one unit and 16 lanes on 16 units of one row both hit distinct bank
+    // slots), and is read back 4 columns per lane with consecutive lanes on
+    // consecutive columns: each store instruction covers whole rows instead
+    // of 16 bytes of 32 rows.  Each round is written by the waves that own
+    // its rows.
+    constexpr int kEpiRows = (kStageU4 * 16 / (BN * 4)) < BM ? (kStageU4 * 16 / (BN * 4)) : BM;
+    constexpr int kUpr = BN / 4, kPasses = kEpiRows * kUpr / S::NT;
+    static_assert(!RowCtx<P>::kRowVal || BM <= S::NT, "one thread per row for the row values");
+    // per-tile operands, loaded when the compute cursor enters a tile
+    float rv = 0.0f;
+    typename RowCtx<P>::ColPre colpre;
+    auto tile_loads = [&]() {
+        if constexpr (RowCtx<P>::kRowVal) {
+            if (tid < BM && ct.row0 + tid < ct.row_end) rv = RowCtx<P>::row_value(a, ct.grp, ct.row0 + tid);
+        }
+        const int c = ct.col0 + 4 * (tid % kUpr);
+        if (c < ncols) colpre = RowCtx<P>::col_load(a, c);
+    };
+    tile_loads();
+    static_assert(kEpiRows % 32 == 0 && BM % kEpiRows == 0 && kUpr >= 16, "epilogue tiling");
+    static_assert(kEpiRows * kUpr % S::NT == 0 && S::NT % kUpr == 0, "epilogue passes");
+    auto epilogue = [&](int st) {
+        // the epilogue's lane-dependent offsets are recomputed from an opaque
+        // copy of the thread id, so they are not hoisted out of the tile loop
+        // and kept live (in registers) across the k-steps
+        int etid = tid;
+        asm volatile("" : "+v"(etid));
+        const int lane = etid & 63;
+        float* tile = reinterpret_cast<float*>(As(st));
+        const int u = etid % kUpr, c = ct.col0 + 4 * u;
+        if constexpr (RowCtx<P>::kRowVal) {
+            if (etid < BM) rowval[etid] = rv;   // read after the round's barrier
+        }
+#pragma unroll
+        for (int h = 0; h < BM / kEpiRows; ++h) {
+            if (h > 0) __syncthreads();  // the previous round's reads are done
+#pragma unroll
+            for (int i = 0; i < S::FM; ++i) {
+                if ((wm * S::WM + i * 32) / kEpiRows != h) continue;
+                const int rl = wm * S::WM + i * 32 + (lane & 31) - h * kEpiRows;
+#pragma unroll
+                for (int j = 0; j < S::FN; ++j)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int uu = (wn * S::WN + j * 32 + 8 * g + 4 * (lane >> 5)) >> 2;
+                        const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                                         acc[i][j][4 * g + 3]};
+                        *reinterpret_cast<f32x4*>(tile + rl * BN + ((uu ^ (rl & 15)) << 2)) = v;
+                    }
+            }
+            // row of this thread's unit in pass it: it * (NT / kUpr) + tid / kUpr;
+            // the per-element operands of all passes are loaded before the stores
+            typename RowCtx<P>::Pre pre[kPasses];
+#pragma unroll
+            for (int it = 0; it < kPasses; ++it) {
+                const int row = ct.row0 + h * kEpiRows + it * (S::NT / kUpr) + etid / kUpr;
+                if (row < ct.row_end && c < ncols) pre[it] = RowCtx<P>::load(a, ct.grp, row, c);
+            }
+            __syncthreads();
+#pragma unroll
+            for (int it = 0; it < kPasses; ++it) {
+                const int rl = it * (S::NT / kUpr) + etid / kUpr;
+                const int row = ct.row0 + h * kEpiRows + rl;
+                if (row < ct.row_end && c < ncols) {
+                    const f32x4 v = *reinterpret_cast<const f32x4*>(tile + rl * BN + ((u ^ (rl & 15)) << 2));
+                    RowCtx<P>::store(a, ct.grp, row, c, v, pre[it], colpre,
+                                     RowCtx<P>::kRowVal ? rowval[h * kEpiRows + rl] : 0.0f);
+                }
+            }
+        }
+        __syncthreads();  // the stage is free for the k-step after next
+    };
+
+    for (int step = 0, ckt = 0;; ++step) {
+        const int st = step & 1;
         bf16x8 a0[S::FM], b0[S::FN], a1[S::FM], b1[S::FN];
         read_frags(st, 0, a0, b0);
 #pragma unroll
@@ -272,65 +405,24 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm2_kernel(LayerArgs a, int 
             bf16x8* bn = (kk & 1) ? b0 : b1;
             if (kk + 1 < kG2K / 16) read_frags(st, kk + 1, an, bn);
             if (kk < 2) {
-                // parts 2kk, 2kk+1 of k-tile kt+1 go to LDS, then the same
-                // registers take parts 2kk, 2kk+1 of k-tile kt+2
+                // parts 2kk, 2kk+1 of the next k-step go to LDS, then the
+                // same registers take parts 2kk, 2kk+1 of the k-step after
                 swrite_part(st ^ 1, 2 * kk);
                 swrite_part(st ^ 1, 2 * kk + 1);
-                gload_group(kpre, kk);
+                gload_group(kk);
             }
             mfma_group(ac, bc);
             __builtin_amdgcn_sched_barrier(0);
         }
+        advance_load();
         __syncthreads();
-    }
-
-    // Epilogue through LDS: the fp32 tile is written row-major (16-byte unit
-    // u of local row r at u ^ (r & 15), so 16 lanes on 16 rows of one unit
-    // and 16 lanes on 16 units of one row both hit distinct bank slots),
-    // then read back 4 columns per lane with consecutive lanes on
-    // consecutive columns: each store instruction covers whole rows instead
-    // of 16 bytes of 32 rows.  A tile larger than the LDS goes in rounds of
-    // kEpiRows rows, each round written by the waves that own those rows.
-    constexpr int kEpiRows = (kStageU4 * 16 / (BN * 4)) < BM ? (kStageU4 * 16 / (BN * 4)) : BM;
-    static_assert(kEpiRows % S::WM == 0 && BM % kEpiRows == 0 && BN / 4 >= 16, "epilogue tiling");
-    float* tile = reinterpret_cast<float*>(smem);
-#pragma unroll
-    for (int h = 0; h < BM / kEpiRows; ++h) {
-        __syncthreads();  // the k-loop (or the previous round) is done with the LDS
-        if (wm * S::WM / kEpiRows == h) {
-#pragma unroll
-            for (int i = 0; i < S::FM; ++i) {
-                const int rl = wm * S::WM + i * 32 + (lane & 31) - h * kEpiRows;
-#pragma unroll
-                for (int j = 0; j < S::FN; ++j)
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const int u = (wn * S::WN + j * 32 + 8 * g + 4 * (lane >> 5)) >> 2;
-                        const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                                         acc[i][j][4 * g + 3]};
-                        *reinterpret_cast<f32x4*>(tile + rl * BN + ((u ^ (rl & 15)) << 2)) = v;
-                    }
-            }
-        }
-        // row/column of this thread's unit in pass it: rl = it * (NT / (BN/4)) + tid / (BN/4)
-        constexpr int kUpr = BN / 4, kPasses = kEpiRows * kUpr / S::NT;
-        static_assert(kEpiRows * kUpr % S::NT == 0 && S::NT % kUpr == 0, "epilogue passes");
-        const int u = tid % kUpr, c = col0 + 4 * u;
-        f32x4 pre[kPasses];
-#pragma unroll
-        for (int it = 0; it < kPasses; ++it) {
-            const int row = row0 + h * kEpiRows + it * (S::NT / kUpr) + tid / kUpr;
-            if (row < row_end && c < ncols) pre[it] = RowCtx<P>::load(a, grp, row, c);
-        }
-        __syncthreads();
-#pragma unroll
-        for (int it = 0; it < kPasses; ++it) {
-            const int rl = it * (S::NT / kUpr) + tid / kUpr;
-            const int row = row0 + h * kEpiRows + rl;
-            if (row < row_end && c < ncols) {
-                const f32x4 v = *reinterpret_cast<const f32x4*>(tile + rl * BN + ((u ^ (rl & 15)) << 2));
-                RowCtx<P>::store(a, grp, row, c, v, pre[it]);
-            }
+        if (++ckt == nk) {
+            epilogue(st);
+            cslot += nslot;
+            if (!tile_at(cslot, ct)) break;
+            ckt = 0;
+            zero_acc();
+            tile_loads();
         }
     }
 }

@@ -13,6 +13,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <mutex>
@@ -46,12 +47,13 @@ int fail(int code, const char* fmt, ...) {
 constexpr size_t kAlign = 256;
 
 // Tiled bf16 GEMM shapes: rows x columns per workgroup and its wave grid.
-template <int BM_, int BN_, int NWM_, int NWN_>
+// PER_CU: workgroups resident per CU (the LDS stages bound it).
+template <int BM_, int BN_, int NWM_, int NWN_, int PER_CU_>
 struct G2Cfg {
-    static constexpr int BM = BM_, BN = BN_, NWM = NWM_, NWN = NWN_;
+    static constexpr int BM = BM_, BN = BN_, NWM = NWM_, NWN = NWN_, PER_CU = PER_CU_;
 };
-using G2Large = G2Cfg<256, 256, 2, 4>;   // 8 waves, 1 workgroup per CU
-using G2Small = G2Cfg<128, 128, 2, 2>;   // 4 waves, 2 workgroups per CU
+using G2Large = G2Cfg<256, 256, 2, 4, 1>;   // 8 waves, 128 KB LDS
+using G2Small = G2Cfg<128, 128, 2, 2, 2>;   // 4 waves, 64 KB LDS
 // The expert FFN takes the large tile when experts hold many rows on average
 // (the tile list, shared by both FFN GEMMs, is cut at that height); with few
 // rows per expert the 256-row tile would be mostly padding.
@@ -186,13 +188,28 @@ void init_once() {
     });
 }
 
+// Compute units of the current device (cached per device ordinal).
+int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+// Persistent launch: one wave of resident workgroups (a multiple of 8, one
+// range of tiles per XCD), or fewer when there are fewer tiles.
 template <class P, class C>
 void launch_g2(const LayerArgs& a, int nrow_tiles, int ncol_tiles, hipStream_t st) {
-    // a whole number of tiles per XCD, so the remap in the kernel is a bijection
-    const unsigned tiles = (unsigned)nrow_tiles * (unsigned)ncol_tiles;
-    const unsigned g = (tiles + kXcds - 1) / kXcds * kXcds;
-    gemm2_kernel<P, C::BM, C::BN, C::NWM, C::NWN><<<g, dim3(64 * C::NWM * C::NWN), 0, st>>>(a, nrow_tiles,
-                                                                                          ncol_tiles);
+    const long long tiles = (long long)nrow_tiles * ncol_tiles;
+    const long long resident = (long long)device_cus() * C::PER_CU / kXcds * kXcds;
+    const long long g = std::max<long long>(kXcds, std::min<long long>((tiles + kXcds - 1) / kXcds * kXcds, resident));
+    gemm2_kernel<P, C::BM, C::BN, C::NWM, C::NWN>
+        <<<(unsigned)g, dim3(64 * C::NWM * C::NWN), 0, st>>>(a, nrow_tiles, ncol_tiles);
 }
 
 template <class E, class YT>
