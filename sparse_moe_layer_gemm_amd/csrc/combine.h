@@ -12,73 +12,95 @@
 
 namespace lmoe {
 
-__device__ __forceinline__ float4 load4(const float* p) { return *reinterpret_cast<const float4*>(p); }
-__device__ __forceinline__ float4 load4(const bf16* p) {
-    const uint2 u = *reinterpret_cast<const uint2*>(p);
-    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
-                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
-}
-__device__ __forceinline__ void store4(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
-__device__ __forceinline__ void store4(bf16* p, float4 v) {
-    p[0] = (bf16)v.x;
-    p[1] = (bf16)v.y;
-    p[2] = (bf16)v.z;
-    p[3] = (bf16)v.w;
-}
-
-// One workgroup per (token, 256-column chunk): its 4 waves take the ranks
-// k = w, w+4, ... and their partial sums are added in wave order through LDS,
-// so the result does not depend on scheduling.
-template <class E, class YT>
+// Work item = (token t, 16-byte column chunk q of its l values): VPC = 8
+// values for bf16 expert outputs, 4 for fp32.  A workgroup of 256 threads
+// holds 256 / RS items, and RS rank groups per item: group g sums the ranks
+// k = g, g + RS, ... in increasing order; the groups' sums are then added in
+// group order through LDS, so the result does not depend on scheduling.
+// RS = 1 (one thread per item) when there are enough tokens to fill the GPU,
+// 4 or 16 for decode-sized batches.  The rank loop is unrolled so the loads
+// of several ranks (and partial planes) are in flight together; no store
+// happens before the last load.
+template <class E, class YT, int RS>
 __global__ __launch_bounds__(256) void combine_kernel(LayerArgs a, int nsplit, int gated) {
-    const int l = a.l;
-    const int chunks = l / 256 + (l % 256 ? 1 : 0);
-    const int t = blockIdx.x / chunks;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int i0 = (blockIdx.x % chunks) * 256 + lane * 4;
-    const bool live = i0 < l;
-    const size_t plane = (size_t)a.T * a.K * l;
-    const YT* Y = static_cast<const YT*>(a.ybuf);
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    constexpr int VPC = 16 / (int)sizeof(YT);
+    constexpr int IPB = 256 / RS;
+    const int cpt = a.l / VPC;
+    const int item = blockIdx.x * IPB + (int)threadIdx.x % IPB;
+    const int g = (int)threadIdx.x / IPB;
+    const bool live = item < a.T * cpt;
+    const int t = live ? item / cpt : 0, c0 = (live ? item % cpt : 0) * VPC;
+    const size_t plane = (size_t)a.T * a.K * a.l;
+    const YT* Y = static_cast<const YT*>(a.ybuf) + c0;
+    float acc[VPC];
+#pragma unroll
+    for (int i = 0; i < VPC; ++i) acc[i] = 0.0f;
     if (live) {
-        for (int k = wave; k < a.K; k += 4) {
-            const size_t flat = (size_t)t * a.K + k;
-            const YT* yp = Y + (size_t)a.slot_of[flat] * l + i0;
-            float4 part = load4(yp);
-            for (int sp = 1; sp < nsplit; ++sp) {
-                const float4 q = load4(yp + sp * plane);
-                part.x += q.x;
-                part.y += q.y;
-                part.z += q.z;
-                part.w += q.w;
+        const int* so = a.slot_of + (size_t)t * a.K;
+        const float* gt = a.gates + (size_t)t * a.K;
+#pragma unroll 4
+        for (int k = g; k < a.K; k += RS) {
+            const YT* yp = Y + (size_t)so[k] * a.l;
+            uint4 raw = ldg16(yp);
+            float part[VPC];
+            if constexpr (VPC == 8) {
+                const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    part[2 * i] = __uint_as_float(w[i] << 16);
+                    part[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+                }
+            } else {
+                part[0] = __uint_as_float(raw.x);
+                part[1] = __uint_as_float(raw.y);
+                part[2] = __uint_as_float(raw.z);
+                part[3] = __uint_as_float(raw.w);
+                for (int sp = 1; sp < nsplit; ++sp) {
+                    const uint4 q = ldg16(yp + sp * plane);
+                    part[0] += __uint_as_float(q.x);
+                    part[1] += __uint_as_float(q.y);
+                    part[2] += __uint_as_float(q.z);
+                    part[3] += __uint_as_float(q.w);
+                }
             }
-            const float g = gated ? a.gates[flat] : 1.0f;
-            acc.x = fmaf(g, part.x, acc.x);
-            acc.y = fmaf(g, part.y, acc.y);
-            acc.z = fmaf(g, part.z, acc.z);
-            acc.w = fmaf(g, part.w, acc.w);
+            const float gk = gated ? gt[k] : 1.0f;
+#pragma unroll
+            for (int i = 0; i < VPC; ++i) acc[i] = fmaf(gk, part[i], acc[i]);
         }
     }
-    __shared__ float4 red[4][64];
-    red[wave][lane] = acc;
-    __syncthreads();
-    if (wave != 0 || !live) return;
-    float4 s = red[0][lane];
+    if constexpr (RS > 1) {
+        __shared__ float red[RS][VPC][IPB];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) {
-        const float4 q = red[w][lane];
-        s.x += q.x;
-        s.y += q.y;
-        s.z += q.z;
-        s.w += q.w;
+        for (int i = 0; i < VPC; ++i) red[g][i][threadIdx.x % IPB] = acc[i];
+        __syncthreads();
+        if (g != 0) return;
+#pragma unroll
+        for (int i = 0; i < VPC; ++i) {
+            float v = red[0][i][threadIdx.x];
+            for (int r = 1; r < RS; ++r) v += red[r][i][threadIdx.x];
+            acc[i] = v;
+        }
     }
+    if (!live) return;
+    E* dst;
     if (a.standard) {
-        const size_t o = (size_t)t * a.d + i0;
-        const float4 xv = load4(static_cast<const E*>(a.x) + o);
-        store4(static_cast<E*>(a.out) + o, make_float4(xv.x + s.x, xv.y + s.y, xv.z + s.z, xv.w + s.w));
+        const size_t o = (size_t)t * a.d + c0;
+        const E* xp = static_cast<const E*>(a.x) + o;
+#pragma unroll
+        for (int i = 0; i < VPC; ++i) acc[i] += to_f32(xp[i]);
+        dst = static_cast<E*>(a.out) + o;
     } else {
-        store4(static_cast<E*>(a.s) + (size_t)t * l + i0, s);
+        dst = static_cast<E*>(a.s) + (size_t)t * a.l + c0;
     }
+    // one vector store of the VPC values (rows are 16-byte aligned: l and d
+    // are multiples of 64)
+    E v[VPC];
+#pragma unroll
+    for (int i = 0; i < VPC; ++i) v[i] = from_f32<E>(acc[i]);
+    if constexpr (sizeof(E) * VPC == 16)
+        *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(v);
+    else
+        *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(v);
 }
 
 }  // namespace lmoe

@@ -212,6 +212,19 @@ void launch_g2(const LayerArgs& a, int nrow_tiles, int ncol_tiles, hipStream_t s
         <<<(unsigned)g, dim3(64 * C::NWM * C::NWN), 0, st>>>(a, nrow_tiles, ncol_tiles);
 }
 
+// Rank groups per combine item: enough threads to fill the GPU.
+template <class E, class YT>
+void launch_combine(const LayerArgs& a, int nsplit, int gated, hipStream_t st) {
+    const long long items = (long long)a.T * (a.l / (16 / (int)sizeof(YT)));
+    if (items >= 131072) {
+        combine_kernel<E, YT, 1><<<(unsigned)((items + 255) / 256), dim3(256), 0, st>>>(a, nsplit, gated);
+    } else if (items >= 16384) {
+        combine_kernel<E, YT, 4><<<(unsigned)((items + 63) / 64), dim3(256), 0, st>>>(a, nsplit, gated);
+    } else {
+        combine_kernel<E, YT, 16><<<(unsigned)((items + 15) / 16), dim3(256), 0, st>>>(a, nsplit, gated);
+    }
+}
+
 template <class E, class YT>
 void launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* events) {
     auto mark = [&](int i) {
@@ -282,11 +295,10 @@ void launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* events
     }
     // 5. combine
     mark(5);
-    const dim3 gc((unsigned)a.T * cdiv(a.l, 256));
     if (p.path == LMOE_PATH_STREAM)
-        combine_kernel<E, float><<<gc, b256, 0, st>>>(a, p.nsplit, 1);
+        launch_combine<E, float>(a, p.nsplit, 1, st);
     else
-        combine_kernel<E, YT><<<gc, b256, 0, st>>>(a, 1, 0);
+        launch_combine<E, YT>(a, 1, 0, st);
     // 6. back to d with the residual
     mark(6);
     if (!a.standard) {
