@@ -271,7 +271,7 @@ void launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* events
     const unsigned mt = (unsigned)p.max_tiles;
     if constexpr (sizeof(E) == 2) {
         if (p.path == LMOE_PATH_STREAM) {
-            const dim3 g(a.N, p.nsplit);
+            const dim3 g(p.nsplit, a.N);
             if (p.ms == 128)
                 ffn_stream_kernel<128><<<g, b256, 0, st>>>(a);
             else

@@ -10,7 +10,7 @@
 //   skinny_kernel<P>: a product with T <= 64 rows.  One workgroup of 16 waves
 //     owns 16 output columns; the waves split the reduction and add their
 //     partial tiles through LDS.
-//   ffn_stream_kernel<MS>: the expert FFN.  Workgroup (a, s) takes active
+//   ffn_stream_kernel<MS>: the expert FFN.  Workgroup (s, a) takes active
 //     expert a and the m-slice [s*MS, (s+1)*MS): it computes
 //     relu(W1[e][slice] z)^2 for up to 16 routed rows at a time, keeps it in
 //     LDS, and multiplies it by the matching column slice of W2[e], writing
@@ -84,10 +84,10 @@ __global__ __launch_bounds__(1024) void skinny_kernel(LayerArgs a) {
 
 template <int MS>
 __global__ __launch_bounds__(256) void ffn_stream_kernel(LayerArgs a) {
-    const int ai = blockIdx.x;
+    const int ai = blockIdx.y;
     if (ai >= *a.n_active) return;
     const int e = a.active[ai];
-    const int j0 = blockIdx.y * MS;
+    const int j0 = blockIdx.x * MS;
     const int r_begin = a.offsets[e], r_end = a.offsets[e + 1];
     const int l = a.l, m = a.m;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -95,7 +95,7 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(LayerArgs a) {
     const bf16* W1e = static_cast<const bf16*>(a.W1) + (size_t)e * m * l;
     const bf16* W2e = static_cast<const bf16*>(a.W2) + (size_t)e * l * m;
     const bf16* Z = static_cast<const bf16*>(a.z);
-    float* Yp = static_cast<float*>(a.ybuf) + (size_t)blockIdx.y * a.T * a.K * l;
+    float* Yp = static_cast<float*>(a.ybuf) + (size_t)blockIdx.x * a.T * a.K * l;
 
     constexpr int NB = MS / 16;        // 16-column blocks of the slice
     constexpr int NBW = NB / 4;        // per wave
@@ -135,35 +135,50 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(LayerArgs a) {
                 As[(4 * (lane >> 4) + r) * AST + (wave + 4 * b) * 16 + lr] = (bf16)(h * h);
             }
         __syncthreads();
-        // ---- phase 2: Y[16 x l] = A[16 x MS] . W2[e][:, j0 : j0+MS]^T
+        // ---- phase 2: Y[16 x l] = A[16 x MS] . W2[e][:, j0 : j0+MS]^T.  The
+        // weight fragment is the MFMA's first operand, so lane l holds output
+        // columns i0 + 4 (l / 16) .. +3 of row l % 16: one 16-byte store.
+        // Results are kept for kPass passes of 4 blocks and stored together,
+        // since a load issued behind pending stores waits for them to complete.
         constexpr int KS = MS / 32;
+        constexpr int kPass = 4;   // block passes per batch of stores
         bf16x8 af[KS];
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk)
             af[kk] = *reinterpret_cast<const bf16x8*>(&As[lr * AST + kk * 32 + koff]);
         const int nblk = l / 16;
-        for (int ib = wave; ib < nblk; ib += 4 * 4) {
-            uint4 wv[4][KS];
+        // a wave takes blocks wave + 4 (4 it + u), kPass passes it per batch
+        for (int ib0 = wave; ib0 < nblk; ib0 += 16 * kPass) {
+            f32x4 yb[kPass][4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int i0 = (ib + 4 * u) * 16;
-                const bool ok = ib + 4 * u < nblk;
-                const bf16* p = W2e + (size_t)(i0 + lr) * m + j0 + koff;
+            for (int it = 0; it < kPass; ++it) {
+                uint4 wv[4][KS];
 #pragma unroll
-                for (int kk = 0; kk < KS; ++kk) wv[u][kk] = ok ? ldg16(p + kk * 32) : kZero16;
-            }
+                for (int u = 0; u < 4; ++u) {
+                    const int ib = ib0 + 16 * it + 4 * u;
+                    const bool ok = ib < nblk;
+                    const bf16* p = W2e + (size_t)(ib * 16 + lr) * m + j0 + koff;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int i0 = (ib + 4 * u) * 16;
-                if (ib + 4 * u >= nblk) break;
-                f32x4 y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kk = 0; kk < KS; ++kk) y = mfma16(af[kk], as_bf16x8(wv[u][kk]), y);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = 4 * (lane >> 4) + r;
-                    if (row < nr) Yp[(size_t)(rc + row) * l + i0 + lr] = y[r];
+                    for (int kk = 0; kk < KS; ++kk) wv[u][kk] = ok ? ldg16(p + kk * 32) : kZero16;
                 }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kk = 0; kk < KS; ++kk) y = mfma16(as_bf16x8(wv[u][kk]), af[kk], y);
+                    yb[it][u] = y;
+                }
+            }
+            if (lr < nr) {
+#pragma unroll
+                for (int it = 0; it < kPass; ++it)
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int ib = ib0 + 16 * it + 4 * u;
+                        if (ib < nblk)
+                            *reinterpret_cast<f32x4*>(&Yp[(size_t)(rc + lr) * l + ib * 16 + 4 * (lane >> 4)]) =
+                                yb[it][u];
+                    }
             }
         }
         __syncthreads();
