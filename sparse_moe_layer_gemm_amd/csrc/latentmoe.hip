@@ -18,6 +18,7 @@
 #include <cstdio>
 #include <mutex>
 #include <string>
+#include <type_traits>
 
 #include "../../include/latentmoe.h"
 #include "combine.h"
@@ -62,6 +63,14 @@ using ProjTile = G2Small;
 using UpTile = G2Large;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
+// The skinny projection's reduction is split into enough k-ranges that the
+// (16-column group, k-range) workgroups cover the CUs; its partial tiles
+// are part[split][T][stride], stride = columns rounded up to 4 floats.
+constexpr int kMaxProjSplit = 16;
+int proj_split(int ncols) { return std::max(1, std::min(kMaxProjSplit, 512 / cdiv(ncols, 16))); }
+int proj_stride(int ncols) { return (ncols + 3) / 4 * 4; }
+size_t proj_part_floats(int ncols) { return (size_t)proj_split(ncols) * proj_stride(ncols); }  // per token row
+
 // mean rows per expert at or below which the streaming FFN is chosen
 constexpr int kStreamMaxMeanRows = 16;
 
@@ -78,7 +87,7 @@ struct Plan {
     long long max_tiles = 0;
     size_t es = 2;
     size_t z, logits, ids, gates, counts, offsets, perm, slot_of, blk_counts, blk_offsets, tiles, n_tiles,
-        active, n_active, abuf, ybuf, s, total;
+        active, n_active, abuf, ybuf, s, part, total;
 };
 
 bool mult64(int v) { return v > 0 && v % 64 == 0; }
@@ -170,6 +179,12 @@ Plan make_plan(const lmoe_dims* dm, int32_t K) {
         p.ybuf = take((size_t)TK * d.l * p.es);
     }
     p.s = take((size_t)d.T * d.l * p.es);
+    // partial tiles of the split projection, for either mode (standard mode,
+    // W_down == NULL, is only known at the call: N instead of l + N columns)
+    size_t part_bytes = 0;
+    if (p.skinny)
+        part_bytes = std::max(proj_part_floats(d.l + d.N), proj_part_floats(d.N)) * d.T * 4;
+    p.part = take(part_bytes);
     p.total = o;
     return p;
 }
@@ -232,11 +247,16 @@ void launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* events
     };
     const dim3 b256(256), b1024(1024);
     const int ncols_pr = (a.standard ? 0 : a.l) + a.N;
+    PartIn pin{nullptr, 0, 0, 0};
+    float* part = reinterpret_cast<float*>(a.part);
     // 1. projection + router logits
     mark(0);
     if constexpr (sizeof(E) == 2) {
         if (p.skinny) {
-            skinny_kernel<ProjRouter<bf16>><<<cdiv(ncols_pr, 16), b1024, 0, st>>>(a);
+            const int split = proj_split(ncols_pr), stride = proj_stride(ncols_pr);
+            skinny_part_kernel<ProjRouter<bf16>>
+                <<<dim3(cdiv(ncols_pr, 16), split), b256, 0, st>>>(a, part, split, stride);
+            pin = PartIn{part, split, stride, a.standard ? 0 : a.l};
         } else {
             launch_g2<ProjRouter<bf16>, ProjTile>(a, cdiv(a.T, ProjTile::BM), cdiv(ncols_pr, ProjTile::BN), st);
         }
@@ -246,15 +266,21 @@ void launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* events
     // 2. top-K gates
     mark(1);
     {
-        const dim3 g(cdiv(a.T, 4));
+        auto launch_topk = [&](auto npl) {
+            constexpr int NPL = decltype(npl)::value;
+            if (pin.nsplit > 0)
+                topk_part_kernel<NPL><<<dim3(a.T), b256, 0, st>>>(a, pin);
+            else
+                topk_kernel<NPL><<<dim3(cdiv(a.T, 4)), b256, 0, st>>>(a);
+        };
         if (a.N <= 256)
-            topk_kernel<4><<<g, b256, 0, st>>>(a);
+            launch_topk(std::integral_constant<int, 4>{});
         else if (a.N <= 512)
-            topk_kernel<8><<<g, b256, 0, st>>>(a);
+            launch_topk(std::integral_constant<int, 8>{});
         else if (a.N <= 1024)
-            topk_kernel<16><<<g, b256, 0, st>>>(a);
+            launch_topk(std::integral_constant<int, 16>{});
         else
-            topk_kernel<32><<<g, b256, 0, st>>>(a);
+            launch_topk(std::integral_constant<int, 32>{});
     }
     // 3. dispatch
     mark(2);
@@ -409,6 +435,7 @@ static int forward_impl(const void* x, const void* W_down, const void* W_router,
     a.abuf = ws + p.abuf;
     a.ybuf = ws + p.ybuf;
     a.s = ws + p.s;
+    a.part = ws + p.part;
     a.tile_rows = p.tile_rows;
 
     hipStream_t st = static_cast<hipStream_t>(stream);

@@ -41,6 +41,7 @@ struct LayerArgs {
     void* abuf;            // [T*K, m] relu(h)^2
     void* ybuf;            // expert outputs (layout depends on the path)
     void* s;               // [T, l] gate-weighted latent sum (latent mode)
+    void* part;            // split-reduction partial tiles of the skinny projection
     int tile_rows;         // rows per grouped-GEMM tile
 };
 

@@ -38,12 +38,22 @@ __device__ __forceinline__ uint32_t order_key(float v) {
 
 __device__ __forceinline__ int popc64(unsigned long long m) { return __popcll(m); }
 
-// Top-K of token t by one wavefront.  s_key / s_idx / s_val: 64 entries of
-// LDS private to the calling wave.
+// Split-reduction input of the top-K kernel: nsplit fp32 partial tiles
+// part[s][T][stride] of [z | logits] (lz + N columns, rows padded to a
+// multiple of 4 floats).  nsplit = 0: the logits are already in
+// LayerArgs::logits (bias included) and z is written.
+struct PartIn {
+    const float* part;
+    int nsplit, stride, lz;
+};
+
+// Top-K of token t by one wavefront, from its N logits at lg (global
+// memory or LDS).  s_key / s_idx / s_val: 64 entries of LDS private to the
+// calling wave.
 template <int NPL>
-__device__ inline void topk_token(const LayerArgs& a, int t, uint32_t* s_key, int* s_idx, float* s_val) {
+__device__ inline void topk_token(const LayerArgs& a, int t, const float* lg, uint32_t* s_key, int* s_idx,
+                                  float* s_val) {
     const int lane = threadIdx.x & 63;
-    const float* lg = a.logits + (size_t)t * a.N;
     float v[NPL];
     uint32_t key[NPL];
 #pragma unroll
@@ -119,7 +129,35 @@ __global__ __launch_bounds__(256) void topk_kernel(LayerArgs a) {
     __shared__ int s_idx[4][64];
     __shared__ float s_val[4][64];
     if (t >= a.T) return;
-    topk_token<NPL>(a, t, s_key[wave], s_idx[wave], s_val[wave]);
+    topk_token<NPL>(a, t, a.logits + (size_t)t * a.N, s_key[wave], s_idx[wave], s_val[wave]);
+}
+
+// One workgroup per token, after the split projection: its 256 threads add
+// the partial tiles in split order (logits: then the bias, into LDS; z:
+// rounded once to bf16, to global memory), then wave 0 selects the top K.
+template <int NPL>
+__global__ __launch_bounds__(256) void topk_part_kernel(LayerArgs a, PartIn pin) {
+    const int t = blockIdx.x;
+    __shared__ float lg[64 * NPL];
+    __shared__ uint32_t s_key[64];
+    __shared__ int s_idx[64];
+    __shared__ float s_val[64];
+    const size_t ps = (size_t)a.T * pin.stride;
+    const float* pt = pin.part + (size_t)t * pin.stride;
+    for (int e = threadIdx.x; e < a.N; e += 256) {
+        float acc = 0.0f;
+        for (int s = 0; s < pin.nsplit; ++s) acc += pt[s * ps + pin.lz + e];
+        lg[e] = a.bias ? acc + a.bias[e] : acc;
+    }
+    bf16* zo = static_cast<bf16*>(a.z_w) + (size_t)t * a.l;
+    for (int c = 4 * threadIdx.x; c < pin.lz; c += 1024) {
+        f32x4 zs = *reinterpret_cast<const f32x4*>(pt + c);
+        for (int s = 1; s < pin.nsplit; ++s) zs += *reinterpret_cast<const f32x4*>(pt + s * ps + c);
+        const bf16 b[4] = {(bf16)zs[0], (bf16)zs[1], (bf16)zs[2], (bf16)zs[3]};
+        *reinterpret_cast<uint2*>(zo + c) = *reinterpret_cast<const uint2*>(b);
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) topk_token<NPL>(a, t, lg, s_key, s_idx, s_val);
 }
 
 // --- dispatch helpers --------------------------------------------------------

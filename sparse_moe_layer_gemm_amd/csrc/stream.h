@@ -10,6 +10,8 @@
 //   skinny_kernel<P>: a product with T <= 64 rows.  One workgroup of 16 waves
 //     owns 16 output columns; the waves split the reduction and add their
 //     partial tiles through LDS.
+//   skinny_part_kernel<P>: the same, with the reduction also split over
+//     workgroups (fp32 partial tiles added by the consumer).
 //   ffn_stream_kernel<MS>: the expert FFN.  Workgroup (s, a) takes active
 //     expert a and the m-slice [s*MS, (s+1)*MS): it computes
 //     relu(W1[e][slice] z)^2 for up to 16 routed rows at a time, keeps it in
@@ -78,6 +80,69 @@ __global__ __launch_bounds__(1024) void skinny_kernel(LayerArgs a) {
         for (int r = 0; r < 4; ++r) {
             const int row = rb * 16 + 4 * (lane >> 4) + r;
             if (row < a.T && c < ncols) P::store(a, 0, row, c, s[r]);
+        }
+    }
+}
+
+// z and the router logits for T <= 64 rows, split over the reduction so
+// that enough workgroups stream the weights: workgroup (g, s) takes the 16
+// columns of group g and k-range s of `nsplit`, its 4 waves split that
+// range further and add their partial tiles through LDS, and the fp32
+// partial tile goes to part[s][T][stride].  The top-K kernel adds the
+// partials in split order (then the bias) and writes z.
+template <class P>
+__global__ __launch_bounds__(256) void skinny_part_kernel(LayerArgs a, float* part, int nsplit, int stride) {
+    const int c0 = blockIdx.x * 16, s = blockIdx.y;
+    const int ncols = P::ncols(a), K = P::kdim(a);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int nrb = cdiv(a.T, 16);
+    const int ksteps = K / 32;
+    const int kc = cdiv(ksteps, nsplit);
+    const int kb = s * kc, ke = min(ksteps, kb + kc);
+    const int per = cdiv(kc, 4);
+    const int ks0 = kb + wave * per, ks1 = min(ke, ks0 + per);
+    const int c = c0 + (lane & 15);
+    const int koff = 8 * (lane >> 4);
+    const bf16* bp = c < ncols ? P::b_row(a, 0, c) + koff : nullptr;
+    const bf16* ap[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+        const int r = rb * 16 + (lane & 15);
+        ap[rb] = (rb < nrb && r < a.T) ? P::a_row(a, 0, r) + koff : nullptr;
+    }
+    f32x4 acc[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ks = ks0; ks < ks1; ks += 4) {
+        uint4 bv[4], av[4][4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int k0 = (ks + u) * 32;
+            const bool ok = ks + u < ks1;
+            bv[u] = (ok && bp) ? ldg16(bp + k0) : kZero16;
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) av[u][rb] = (ok && ap[rb]) ? ldg16(ap[rb] + k0) : kZero16;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb)
+                if (rb < nrb) acc[rb] = mfma16(as_bf16x8(av[u][rb]), as_bf16x8(bv[u]), acc[rb]);
+    }
+    __shared__ f32x4 red[4][4][64];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+        if (rb < nrb) red[wave][rb][lane] = acc[rb];
+    __syncthreads();
+    const int rb = threadIdx.x >> 6;
+    if (rb < nrb) {
+        f32x4 v = red[0][rb][lane];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) v += red[w][rb][lane];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = rb * 16 + 4 * (lane >> 4) + r;
+            if (row < a.T && c < ncols) part[((size_t)s * a.T + row) * stride + c] = v[r];
         }
     }
 }
