@@ -30,6 +30,7 @@ if ROOT not in sys.path:
 METRIC = "LatentMoE fwd tokens/s (d4096 ℓ1024 E512 top22); % of HBM/MFMA roofline"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+FP32_VECTOR_PEAK_TFLOPS = 157.3   # the float32 path runs on the vector ALUs
 
 
 def parse():
@@ -164,16 +165,22 @@ def main():
         ffn_bytes = A * 2 * w.l * w.m * w.elem_bytes
         roof = {"kernel": "ffn_stream_kernel", "bound": "hbm", "achieved": ffn_bytes / (ffn_us * 1e-6) / 1e9,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": None}
+    elif w.dtype == "f32":
+        ffn_flops = 4.0 * w.T * w.K * w.l * w.m
+        roof = {"kernel": "gemm_simt_kernel<Ffn1>+<Ffn2>", "bound": "alu",
+                "achieved": ffn_flops / (ffn_us * 1e-6) / 1e12, "peak": FP32_VECTOR_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "traffic": None}
     else:
         ffn_flops = 4.0 * w.T * w.K * w.l * w.m
-        roof = {"kernel": "gemm_mfma_kernel<Ffn1>+<Ffn2>", "bound": "mfma",
+        roof = {"kernel": "gemm2_kernel<Ffn1>+<Ffn2>", "bound": "mfma",
                 "achieved": ffn_flops / (ffn_us * 1e-6) / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "traffic": None}
     roof["traffic"] = measured_traffic(w, roof["kernel"])
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["kernel_us"] = ffn_us
     roof["copy_GBps_measured"] = copy_gbs
-    layer_frac = max(lay_bytes / (HBM_PEAK_GBS * 1e9), lay_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)) / (ms * 1e-3)
+    flop_peak = FP32_VECTOR_PEAK_TFLOPS if w.dtype == "f32" else MFMA_BF16_PEAK_TFLOPS
+    layer_frac = max(lay_bytes / (HBM_PEAK_GBS * 1e9), lay_flops / (flop_peak * 1e12)) / (ms * 1e-3)
 
     cpu = None
     if args.cpu_seconds > 0:
