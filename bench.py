@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--weight-sets", type=int, default=2)
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget; 0 skips it")
     ap.add_argument("--no-events", action="store_true", help="time without stage events")
+    ap.add_argument("--sweep", default="",
+                    help="comma-separated token counts: one JSON line per count, the workload's shape with "
+                         "T tokens (x = the first T rows of one draw), no CPU baseline")
     return ap.parse_args()
 
 
@@ -79,8 +82,12 @@ def algorithmic(w, A: float):
     return nbytes, flops
 
 
+ARGS = None
+
+
 def main():
-    args = parse()
+    global ARGS
+    args = ARGS = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; the layer is not sharded "
@@ -98,10 +105,35 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     B.lib()
-    sets = []
-    for s in range(max(1, args.weight_sets)):
-        inp = make_inputs(w, seed=s)
-        sets.append((inp, {k: (None if v is None else v.to(dev)) for k, v in inp.items()}))
+
+    def draw_sets(wk):
+        sets = []
+        for s in range(max(1, args.weight_sets)):
+            inp = make_inputs(wk, seed=s)
+            sets.append((inp, {k: (None if v is None else v.to(dev)) for k, v in inp.items()}))
+        return sets
+
+    if args.sweep:
+        counts = [int(t) for t in args.sweep.split(",") if t.strip()]
+        base = draw_sets(w.replace(T=max(counts)))
+        for T in counts:
+            wt = w.replace(name=f"{w.name}_T{T}", T=T)
+            sets = [({**c, "x": c["x"][:T]}, {**g, "x": g["x"][:T].contiguous()}) for c, g in base]
+            print(json.dumps(measure(wt, sets, 0.0)), flush=True)
+        return
+    print(json.dumps(measure(w, draw_sets(w), args.cpu_seconds)), flush=True)
+
+
+def measure(w, sets, cpu_seconds: float) -> dict:
+    """One JSON record: w's forward timed over `sets` (CPU and device copies
+    of the inputs, alternating between steps)."""
+    import numpy as np
+    import torch
+
+    from sparse_moe_layer_gemm_amd import binding as B
+
+    args = ARGS
+    dev = torch.device("cuda:0")
     dims = B.dims_for(sets[0][1], w.K, args.path)
     path = B.latentmoe_resolved_path(dims, w.K)
     ws = B.alloc_workspace(dims, w.K, dev)
@@ -183,8 +215,8 @@ def main():
     layer_frac = max(lay_bytes / (HBM_PEAK_GBS * 1e9), lay_flops / (flop_peak * 1e12)) / (ms * 1e-3)
 
     cpu = None
-    if args.cpu_seconds > 0:
-        cpu = cpu_baseline(w, sets[0][0], args.cpu_seconds)
+    if cpu_seconds > 0:
+        cpu = cpu_baseline(w, sets[0][0], cpu_seconds)
 
     line = {
         "metric": METRIC,
@@ -208,7 +240,7 @@ def main():
         "layer": {"algorithmic_bytes": lay_bytes, "algorithmic_flops": lay_flops, "active_experts": A,
                   "roofline_frac": layer_frac, "stage_us": stages},
     }
-    print(json.dumps(line), flush=True)
+    return line
 
 
 def measured_traffic(w, kernel: str):

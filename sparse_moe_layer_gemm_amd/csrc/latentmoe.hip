@@ -67,9 +67,13 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 // (16-column group, k-range) workgroups cover the CUs; its partial tiles
 // are part[split][T][stride], stride = columns rounded up to 4 floats.
 constexpr int kMaxProjSplit = 16;
-int proj_split(int ncols) { return std::max(1, std::min(kMaxProjSplit, 512 / cdiv(ncols, 16))); }
+int proj_split(int ncols, int T) {
+    return std::max(1, std::min(kMaxProjSplit, 512 / (cdiv(ncols, 16) * cdiv(T, 64))));
+}
 int proj_stride(int ncols) { return (ncols + 3) / 4 * 4; }
-size_t proj_part_floats(int ncols) { return (size_t)proj_split(ncols) * proj_stride(ncols); }  // per token row
+size_t proj_part_floats(int ncols, int T) {  // per token row
+    return (size_t)proj_split(ncols, T) * proj_stride(ncols);
+}
 
 // mean rows per expert at or below which the streaming FFN is chosen
 constexpr int kStreamMaxMeanRows = 16;
@@ -183,7 +187,7 @@ Plan make_plan(const lmoe_dims* dm, int32_t K) {
     // W_down == NULL, is only known at the call: N instead of l + N columns)
     size_t part_bytes = 0;
     if (p.skinny)
-        part_bytes = std::max(proj_part_floats(d.l + d.N), proj_part_floats(d.N)) * d.T * 4;
+        part_bytes = std::max(proj_part_floats(d.l + d.N, d.T), proj_part_floats(d.N, d.T)) * d.T * 4;
     p.part = take(part_bytes);
     p.total = o;
     return p;
@@ -253,9 +257,9 @@ void launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* events
     mark(0);
     if constexpr (sizeof(E) == 2) {
         if (p.skinny) {
-            const int split = proj_split(ncols_pr), stride = proj_stride(ncols_pr);
+            const int split = proj_split(ncols_pr, a.T), stride = proj_stride(ncols_pr);
             skinny_part_kernel<ProjRouter<bf16>>
-                <<<dim3(cdiv(ncols_pr, 16), split), b256, 0, st>>>(a, part, split, stride);
+                <<<dim3(cdiv(ncols_pr, 16), split, cdiv(a.T, 64)), b256, 0, st>>>(a, part, split, stride);
             pin = PartIn{part, split, stride, a.standard ? 0 : a.l};
         } else {
             launch_g2<ProjRouter<bf16>, ProjTile>(a, cdiv(a.T, ProjTile::BM), cdiv(ncols_pr, ProjTile::BN), st);
@@ -330,7 +334,7 @@ void launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* events
     if (!a.standard) {
         if constexpr (sizeof(E) == 2) {
             if (p.skinny)
-                skinny_kernel<Up<bf16>><<<cdiv(a.d, 16), b1024, 0, st>>>(a);
+                skinny_kernel<Up<bf16>><<<dim3(cdiv(a.d, 16), cdiv(a.T, 64)), b1024, 0, st>>>(a);
             else
                 launch_g2<Up<bf16>, UpTile>(a, cdiv(a.T, UpTile::BM), cdiv(a.d, UpTile::BN), st);
         } else {

@@ -7,9 +7,9 @@
 // load) and keep many such loads in flight per wave.  The 16-row MFMA pads
 // the few real rows; the extra arithmetic is free next to the weight stream.
 //
-//   skinny_kernel<P>: a product with T <= 64 rows.  One workgroup of 16 waves
-//     owns 16 output columns; the waves split the reduction and add their
-//     partial tiles through LDS.
+//   skinny_kernel<P>: a product with T <= 256 rows.  One workgroup of 16
+//     waves owns 16 output columns of a group of 64 rows; the waves split the
+//     reduction and add their partial tiles through LDS.
 //   skinny_part_kernel<P>: the same, with the reduction also split over
 //     workgroups (fp32 partial tiles added by the consumer).
 //   ffn_stream_kernel<MS>: the expert FFN.  Workgroup (s, a) takes active
@@ -26,14 +26,14 @@
 namespace lmoe {
 
 constexpr int kSkinnyWaves = 16;
-constexpr int kSkinnyMaxRows = 64;
+constexpr int kSkinnyMaxRows = 256;   // rows of a skinny product (in groups of 64)
 
 template <class P>
 __global__ __launch_bounds__(1024) void skinny_kernel(LayerArgs a) {
-    const int c0 = blockIdx.x * 16;
+    const int c0 = blockIdx.x * 16, r0 = blockIdx.y * 64;   // 16 columns x a group of 64 rows
     const int ncols = P::ncols(a), K = P::kdim(a);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int nrb = cdiv(a.T, 16);
+    const int nrb = min(4, cdiv(a.T - r0, 16));
     const int ksteps = K / 32;
     const int per = cdiv(ksteps, kSkinnyWaves);
     const int ks0 = wave * per, ks1 = min(ksteps, ks0 + per);
@@ -43,7 +43,7 @@ __global__ __launch_bounds__(1024) void skinny_kernel(LayerArgs a) {
     const bf16* ap[4];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
-        const int r = rb * 16 + (lane & 15);
+        const int r = r0 + rb * 16 + (lane & 15);
         ap[rb] = (rb < nrb && r < a.T) ? P::a_row(a, 0, r) + koff : nullptr;
     }
     f32x4 acc[4];
@@ -78,24 +78,24 @@ __global__ __launch_bounds__(1024) void skinny_kernel(LayerArgs a) {
         for (int w = 1; w < kSkinnyWaves; ++w) s += red[w][rb][lane];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int row = rb * 16 + 4 * (lane >> 4) + r;
+            const int row = r0 + rb * 16 + 4 * (lane >> 4) + r;
             if (row < a.T && c < ncols) P::store(a, 0, row, c, s[r]);
         }
     }
 }
 
-// z and the router logits for T <= 64 rows, split over the reduction so
-// that enough workgroups stream the weights: workgroup (g, s) takes the 16
-// columns of group g and k-range s of `nsplit`, its 4 waves split that
+// z and the router logits for T <= 256 rows, split over the reduction so
+// that enough workgroups stream the weights: workgroup (g, s, q) takes the
+// 16 columns of group g, k-range s of `nsplit` and rows 64q .. 64q+63; its 4 waves split that
 // range further and add their partial tiles through LDS, and the fp32
 // partial tile goes to part[s][T][stride].  The top-K kernel adds the
 // partials in split order (then the bias) and writes z.
 template <class P>
 __global__ __launch_bounds__(256) void skinny_part_kernel(LayerArgs a, float* part, int nsplit, int stride) {
-    const int c0 = blockIdx.x * 16, s = blockIdx.y;
+    const int c0 = blockIdx.x * 16, s = blockIdx.y, r0 = blockIdx.z * 64;
     const int ncols = P::ncols(a), K = P::kdim(a);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int nrb = cdiv(a.T, 16);
+    const int nrb = min(4, cdiv(a.T - r0, 16));
     const int ksteps = K / 32;
     const int kc = cdiv(ksteps, nsplit);
     const int kb = s * kc, ke = min(ksteps, kb + kc);
@@ -107,7 +107,7 @@ __global__ __launch_bounds__(256) void skinny_part_kernel(LayerArgs a, float* pa
     const bf16* ap[4];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
-        const int r = rb * 16 + (lane & 15);
+        const int r = r0 + rb * 16 + (lane & 15);
         ap[rb] = (rb < nrb && r < a.T) ? P::a_row(a, 0, r) + koff : nullptr;
     }
     f32x4 acc[4];
@@ -141,7 +141,7 @@ __global__ __launch_bounds__(256) void skinny_part_kernel(LayerArgs a, float* pa
         for (int w = 1; w < 4; ++w) v += red[w][rb][lane];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int row = rb * 16 + 4 * (lane >> 4) + r;
+            const int row = r0 + rb * 16 + 4 * (lane >> 4) + r;
             if (row < a.T && c < ncols) part[((size_t)s * a.T + row) * stride + c] = v[r];
         }
     }

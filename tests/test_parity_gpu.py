@@ -78,6 +78,32 @@ def test_skewed_sampled():
     assert counts.max() > 10 * w.T * w.K / w.N and (counts == 0).sum() > 0
 
 
+# --- batch sweep: the decode-shaped layers at T = 1 ... 256 tokens ------------
+# (x = the first T rows of one draw; the path and kernels change with T: the
+# split skinny projection up to 64 tokens, the tiled projection above)
+
+SWEEP_T = [1, 2, 4, 8, 16, 64, 128, 256]
+
+
+@pytest.fixture(scope="module")
+def sweep_decode():
+    w = WORKLOADS["decode"].replace(T=max(SWEEP_T))
+    return w, make_inputs(w, 7)
+
+
+@pytest.mark.parametrize("T", SWEEP_T)
+def test_decode_batch_sweep(sweep_decode, T):
+    w0, inp = sweep_decode
+    w = w0.replace(name=f"decode_T{T}", T=T)
+    P.compare(w, {**inp, "x": inp["x"][:T]}, w.K, tag=f"decode_T{T}")
+
+
+@pytest.mark.parametrize("T", [1, 8, 64, 256])
+def test_standard_decode_batch_sweep(T):
+    w = WORKLOADS["standard_decode"].replace(name=f"standard_decode_T{T}", T=T)
+    P.compare(w, make_inputs(w, 8), w.K, tag=f"standard_decode_T{T}")
+
+
 # --- smaller shapes: several tiles, ragged tails, both FFN paths --------------
 
 SMALL_PREFILL = Workload("small_prefill", T=1000, d=512, l=128, N=64, K=6, m=256, dtype="bf16")
