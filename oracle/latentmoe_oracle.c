@@ -29,12 +29,20 @@
  *      (10100.com article section 2.2: aggregate, then up-project).
  *   6. out = x + W_up s (third bullet of the same qingkeai.online section).
  *      The residual add is a reading: the pages do not state one.
+ *   7. Optional shared expert at the full width d (m_shared > 0): a dense
+ *      FFN on x beside the routed path, its output added to the layer's:
+ *      out += Ws2 max(Ws1 x, 0)^2.  The shared expert stays at d
+ *      (qingkeai.online article, closing paragraph of "LatentMoE 具体怎么做";
+ *      zhichai.net section 2, last paragraph) and its output is summed with
+ *      the routed one (10100.com article section 3.3, the shared-expert
+ *      stream).  Its width m_shared and its activation (the routed experts'
+ *      squared ReLU) are readings: the pages give neither.
  * Standard mode (no projections, l == d): z = x and out = x + s, the plain
- * MoE of 10100.com Figure 3a.
+ * MoE of 10100.com Figure 3a (plus the shared expert when present).
  *
  * Storage (row-major; the reduction index is the fastest one):
  *   x [T,d]  W_down [l,d]  W_router [N,d]  W1 [N,m,l]  W2 [N,l,m]  W_up [d,l]
- *   bias [N] float32 or NULL.
+ *   Ws1 [m_shared,d]  Ws2 [d,m_shared]  bias [N] float32 or NULL.
  * Element type of x and the weights: float32 (dtype 0) or bfloat16 bit
  * patterns (dtype 1).  Each element is widened to double at use; every sum is
  * accumulated in double in index order.
@@ -53,6 +61,7 @@ typedef struct {
     int32_t T, d, l, N, K, m;
     int32_t dtype;    /* 0: float32 arrays, 1: bfloat16 bit patterns */
     int32_t standard; /* 1: no projections (requires l == d) */
+    int32_t m_shared; /* width of the shared expert, 0: none */
 } oracle_dims;
 
 static double widen(const void* base, int dtype, size_t i) {
@@ -75,6 +84,7 @@ static int outranks(const double* logit, int a, int b) {
  */
 static void one_token(const oracle_dims* D, int t, const void* x, const void* Wd,
                       const void* Wr, const void* W1, const void* W2, const void* Wu,
+                      const void* Ws1, const void* Ws2,
                       const float* bias, const int32_t* forced, double* out_t,
                       int32_t* ids_t, double* gates_t, double* logits_t, double* gap_t,
                       double* work) {
@@ -84,7 +94,8 @@ static void one_token(const oracle_dims* D, int t, const void* x, const void* Wd
     double* p = z + l;            /* [N] */
     double* h = p + N;            /* [m] */
     double* s = h + m;            /* [l] */
-    char* chosen = (char*)(s + l);/* [N] */
+    double* hs = s + l;           /* [m_shared] */
+    char* chosen = (char*)(hs + D->m_shared); /* [N] */
 
     for (int i = 0; i < d; ++i) xt[i] = widen(x, dt, (size_t)t * d + i);
 
@@ -166,6 +177,22 @@ static void one_token(const oracle_dims* D, int t, const void* x, const void* Wd
         }
         out_t[n] = xt[n] + acc;
     }
+
+    /* step 7: the shared expert at full d, added to the output */
+    const int ms = D->m_shared;
+    if (ms > 0) {
+        for (int j = 0; j < ms; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < d; ++i) acc += widen(Ws1, dt, (size_t)j * d + i) * xt[i];
+            const double r = acc < 0.0 ? 0.0 : acc;
+            hs[j] = r * r;
+        }
+        for (int n = 0; n < d; ++n) {
+            double acc = 0.0;
+            for (int j = 0; j < ms; ++j) acc += widen(Ws2, dt, (size_t)n * ms + j) * hs[j];
+            out_t[n] += acc;
+        }
+    }
 }
 
 /*
@@ -173,20 +200,24 @@ static void one_token(const oracle_dims* D, int t, const void* x, const void* Wd
  * first n_sel tokens when sel is NULL).  Outputs are indexed by position in
  * the selection:  out [n_sel,d]  ids [n_sel,K]  gates [n_sel,K]
  * logits [n_sel,N]  gap [n_sel]  (gap = K-th minus (K+1)-th largest logit).
- * forced_ids [n_sel,K] or NULL.  Returns 0, or -1 on bad arguments.
+ * forced_ids [n_sel,K] or NULL.  Ws1 / Ws2: the shared expert, used only
+ * when D->m_shared > 0.  Returns 0, or -1 on bad arguments.
  */
 int oracle_forward(const oracle_dims* D, const void* x, const void* Wd, const void* Wr,
-                   const void* W1, const void* W2, const void* Wu, const float* bias,
+                   const void* W1, const void* W2, const void* Wu, const void* Ws1,
+                   const void* Ws2, const float* bias,
                    const int32_t* sel, int32_t n_sel, const int32_t* forced_ids,
                    double* out, int32_t* ids, double* gates, double* logits, double* gap) {
     if (!D || !x || !Wr || !W1 || !W2 || !out || !ids || !gates || !logits || !gap) return -1;
-    if (D->K < 1 || D->K > D->N || D->T < 0 || n_sel < 0) return -1;
+    if (D->K < 1 || D->K > D->N || D->T < 0 || n_sel < 0 || D->m_shared < 0) return -1;
     if (D->standard ? (D->l != D->d) : (!Wd || !Wu)) return -1;
+    if (D->m_shared > 0 && (!Ws1 || !Ws2)) return -1;
     for (int q = 0; q < n_sel; ++q) {
         int t = sel ? sel[q] : q;
         if (t < 0 || t >= D->T) return -1;
     }
-    const size_t work_doubles = (size_t)D->d + 2 * (size_t)D->l + D->N + D->m + (D->N + 7) / 8 + 1;
+    const size_t work_doubles =
+        (size_t)D->d + 2 * (size_t)D->l + D->N + D->m + D->m_shared + (D->N + 7) / 8 + 1;
     int bad = 0;
 #pragma omp parallel
     {
@@ -198,7 +229,7 @@ int oracle_forward(const oracle_dims* D, const void* x, const void* Wd, const vo
 #pragma omp for schedule(dynamic, 1)
             for (int q = 0; q < n_sel; ++q) {
                 int t = sel ? sel[q] : q;
-                one_token(D, t, x, Wd, Wr, W1, W2, Wu, bias,
+                one_token(D, t, x, Wd, Wr, W1, W2, Wu, Ws1, Ws2, bias,
                           forced_ids ? forced_ids + (size_t)q * D->K : NULL,
                           out + (size_t)q * D->d, ids + (size_t)q * D->K,
                           gates + (size_t)q * D->K, logits + (size_t)q * D->N, gap + q, work);

@@ -26,7 +26,7 @@ CFLAGS = ["-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-fPIC", "-s
 
 
 class _Dims(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_int32) for n in ("T", "d", "l", "N", "K", "m", "dtype", "standard")]
+    _fields_ = [(n, ctypes.c_int32) for n in ("T", "d", "l", "N", "K", "m", "dtype", "standard", "m_shared")]
 
 
 def build(src: str = SRC, out: str = LIB, extra: Sequence[str] = ()) -> str:
@@ -47,7 +47,7 @@ class Oracle:
         f = self.lib.oracle_forward
         f.restype = ctypes.c_int
         P = ctypes.c_void_p
-        f.argtypes = [ctypes.POINTER(_Dims), P, P, P, P, P, P, P, P, ctypes.c_int32, P, P, P, P, P, P]
+        f.argtypes = [ctypes.POINTER(_Dims), P, P, P, P, P, P, P, P, P, P, ctypes.c_int32, P, P, P, P, P, P]
         self.lib.oracle_threads.restype = ctypes.c_int
         self.lib.oracle_set_threads.argtypes = [ctypes.c_int]
 
@@ -59,12 +59,13 @@ class Oracle:
 
     def forward(self, x, W_down, W_router, W1, W2, W_up, K: int, *, bias=None,
                 standard: bool = False, sel: Optional[Sequence[int]] = None,
-                forced_ids=None):
+                forced_ids=None, W_s1=None, W_s2=None):
         """Evaluate the layer for the tokens in `sel` (all tokens if None).
 
         Arrays: numpy float32, or uint16 holding bfloat16 bits, in the
         storage layout x [T,d], W_down [l,d], W_router [N,d], W1 [N,m,l],
-        W2 [N,l,m], W_up [d,l]; bias float32 [N] or None.
+        W2 [N,l,m], W_up [d,l]; bias float32 [N] or None; the shared expert
+        W_s1 [m_s,d] and W_s2 [d,m_s], or None for none.
         Returns dict(out [n,d] f64, ids [n,K] i32, gates [n,K] f64,
         logits [n,N] f64, gap [n] f64).
         """
@@ -76,12 +77,15 @@ class Oracle:
         N = W_router.shape[0]
         m = W1.shape[1]
         l = W1.shape[2]
-        arrs = [x, W_down, W_router, W1, W2, W_up]
+        if (W_s1 is None) != (W_s2 is None):
+            raise ValueError("W_s1 and W_s2 come together")
+        ms = 0 if W_s1 is None else int(W_s1.shape[0])
+        arrs = [x, W_down, W_router, W1, W2, W_up, W_s1, W_s2]
         for a in arrs:
             if a is not None and a.dtype != x.dtype:
                 raise TypeError("all of x and the weights must share one dtype")
         arrs = [None if a is None else np.ascontiguousarray(a) for a in arrs]
-        x, W_down, W_router, W1, W2, W_up = arrs
+        x, W_down, W_router, W1, W2, W_up, W_s1, W_s2 = arrs
         if bias is not None:
             bias = np.ascontiguousarray(bias, dtype=np.float32)
         if sel is None:
@@ -93,7 +97,7 @@ class Oracle:
         if forced_ids is not None:
             forced_ids = np.ascontiguousarray(np.asarray(forced_ids, dtype=np.int32))
             assert forced_ids.shape == (n, K)
-        D = _Dims(T, d, l, N, K, m, dtype, 1 if standard else 0)
+        D = _Dims(T, d, l, N, K, m, dtype, 1 if standard else 0, ms)
         out = np.empty((n, d), np.float64)
         ids = np.empty((n, K), np.int32)
         gates = np.empty((n, K), np.float64)
@@ -104,7 +108,7 @@ class Oracle:
             return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
         rc = self.lib.oracle_forward(ctypes.byref(D), p(x), p(W_down), p(W_router), p(W1), p(W2),
-                                     p(W_up), p(bias), p(sel_arr), n, p(forced_ids),
+                                     p(W_up), p(W_s1), p(W_s2), p(bias), p(sel_arr), n, p(forced_ids),
                                      p(out), p(ids), p(gates), p(logits), p(gap))
         if rc != 0:
             raise ValueError("oracle_forward rejected its arguments")

@@ -21,6 +21,10 @@ What pins what:
   homogeneity  2 W2 -> 2x, 2 W1 -> 4x (ReLU^2 is degree 2), 2 W_up -> 2x
   symmetry     token permutation permutes outputs; relabelling experts keeps
                outputs
+  shared       with the routed experts silenced (W2 = 0) the layer is x plus
+  expert       a dense FFN on x evaluated with numpy float64 matmuls; with
+               them on, adding the shared expert adds exactly that FFN;
+               W_s2 = 0 gives the layer without it bit-exactly
 """
 from __future__ import annotations
 
@@ -71,7 +75,24 @@ def f64(a):
 
 def run(o, L, K, **kw):
     return o.forward(L["x"], L["W_down"], L["W_router"], L["W1"], L["W2"], L["W_up"], K,
-                     bias=L.get("bias"), standard=L["W_down"] is None, **kw)
+                     bias=L.get("bias"), standard=L["W_down"] is None,
+                     W_s1=L.get("W_s1"), W_s2=L.get("W_s2"), **kw)
+
+
+def add_shared(L, seed, ms):
+    """A shared expert of width ms on the layer L (float32 values)."""
+    r = _rng(seed)
+    T, d = L["x"].shape
+    L = dict(L)
+    L["W_s1"] = (r.standard_normal((ms, d)) / np.sqrt(d)).astype(np.float32)
+    L["W_s2"] = (r.standard_normal((d, ms)) / np.sqrt(ms)).astype(np.float32)
+    return L
+
+
+def np_shared(L):
+    """x -> W_s2 relu(W_s1 x)^2 with numpy float64 matmuls."""
+    h = f64(L["x"]) @ f64(L["W_s1"]).T
+    return (np.maximum(h, 0.0) ** 2) @ f64(L["W_s2"]).T
 
 
 def np_logits(L):
@@ -330,6 +351,32 @@ def pin_selection_and_forced_ids(o):
     assert np.array_equal(rf["out"], r["out"][sel])
 
 
+def pin_shared_expert(o):
+    """The shared expert at full d: a dense FFN on x added to the layer."""
+    for standard in (False, True):
+        d = 24
+        l = d if standard else 8
+        L = add_shared(rand_layer(31, T=7, d=d, l=l, N=6, m=10, standard=standard), 32, ms=12)
+        K = 3
+        # routed experts silenced: out = x + shared(x), nothing else
+        L0 = dict(L)
+        L0["W2"] = np.zeros_like(L["W2"])
+        r0 = run(o, L0, K)
+        assert np.allclose(r0["out"], f64(L["x"]) + np_shared(L), rtol=1e-12, atol=1e-12), \
+            "layer with silenced experts != x + W_s2 relu(W_s1 x)^2"
+        # routed experts on: the shared expert adds exactly its FFN
+        with_s = run(o, L, K)["out"]
+        Ln = dict(L)
+        Ln["W_s1"] = Ln["W_s2"] = None
+        without = run(o, Ln, K)["out"]
+        assert np.allclose(with_s - without, np_shared(L), rtol=1e-10, atol=1e-12), \
+            "the shared expert does not add its own FFN output"
+        # W_s2 = 0: the layer without a shared expert, bit-exactly
+        Lz = dict(L)
+        Lz["W_s2"] = np.zeros_like(L["W_s2"])
+        assert np.array_equal(run(o, Lz, K)["out"], without), "W_s2 = 0 changed the output"
+
+
 ALL_PINS = [
     pin_routing_bruteforce,
     pin_tie_break,
@@ -342,4 +389,5 @@ ALL_PINS = [
     pin_homogeneity,
     pin_symmetries,
     pin_selection_and_forced_ids,
+    pin_shared_expert,
 ]

@@ -54,6 +54,12 @@ MUTANTS = {
     "gap_from_top": ("*gap_t = logits_t[ids_t[K - 1]] - logits_t[next];",
                      "*gap_t = logits_t[ids_t[0]] - logits_t[next];"),
     "standard_mode_projects": ("            acc = s[n];\n", "            acc = 0.5 * s[n];\n"),
+    "shared_dropped": ("out_t[n] += acc;", "(void)acc;"),
+    "shared_relu_not_squared": ("hs[j] = r * r;", "hs[j] = r;"),
+    "shared_on_latent": ("acc += widen(Ws1, dt, (size_t)j * d + i) * xt[i];",
+                         "acc += widen(Ws1, dt, (size_t)j * d + i) * (i < l ? z[i] : 0.0);"),
+    "shared_transposed_Ws1": ("widen(Ws1, dt, (size_t)j * d + i)", "widen(Ws1, dt, (size_t)i * ms + j)"),
+    "shared_transposed_Ws2": ("widen(Ws2, dt, (size_t)n * ms + j)", "widen(Ws2, dt, (size_t)j * d + n)"),
 }
 
 
