@@ -77,8 +77,9 @@ def algorithmic(w, A: float):
     """Whole-layer algorithmic bytes and flops (A = experts that got rows)."""
     B = w.elem_bytes
     lat = 0 if w.standard else 1
-    nbytes = B * (2 * w.T * w.d + lat * 2 * w.d * w.l + w.d * w.N + A * 2 * w.l * w.m) + (4 * w.N if w.bias else 0)
-    flops = lat * 4 * w.T * w.d * w.l + 2 * w.T * w.d * w.N + 4 * w.T * w.K * w.l * w.m
+    nbytes = B * (2 * w.T * w.d + lat * 2 * w.d * w.l + w.d * w.N + A * 2 * w.l * w.m + 2 * w.d * w.m_shared) \
+        + (4 * w.N if w.bias else 0)
+    flops = lat * 4 * w.T * w.d * w.l + 2 * w.T * w.d * w.N + 4 * w.T * w.K * w.l * w.m + 4 * w.T * w.d * w.m_shared
     return nbytes, flops
 
 
@@ -145,7 +146,8 @@ def measure(w, sets, cpu_seconds: float) -> dict:
     def step(i, events=None):
         d = sets[i % len(sets)][1]
         B.latentmoe_forward(d["x"], d["W_down"], d["W_router"], d["W1"], d["W2"], d["W_up"], w.K, out, dims,
-                            router_bias=d["bias"], workspace=ws, stream=stream, events=events)
+                            router_bias=d["bias"], workspace=ws, stream=stream, events=events,
+                            W_shared1=d.get("W_s1"), W_shared2=d.get("W_s2"))
 
     # active experts per weight set (for the algorithmic byte count)
     lay = B.latentmoe_workspace_layout(dims, w.K)
@@ -232,7 +234,7 @@ def measure(w, sets, cpu_seconds: float) -> dict:
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "d": w.d, "l": w.l, "N": w.N, "K": w.K, "m": w.m,
-                   "standard": w.standard, "bias": w.bias, "weight_sets": len(sets),
+                   "m_shared": w.m_shared, "standard": w.standard, "bias": w.bias, "weight_sets": len(sets),
                    "ffn_path": "stream" if path == B.LMOE_PATH_STREAM else "tiled",
                    "parallelism": "single GPU"},
         "roofline": roof,
@@ -292,7 +294,7 @@ def cpu_baseline(w, inp, budget_s: float):
     while True:
         sel = np.arange(n % w.T, n % w.T + chunk, dtype=np.int32) % w.T
         orc.forward(arr["x"], arr["W_down"], arr["W_router"], arr["W1"], arr["W2"], arr["W_up"], w.K,
-                    bias=arr["bias"], standard=w.standard, sel=sel)
+                    bias=arr["bias"], standard=w.standard, sel=sel, W_s1=arr.get("W_s1"), W_s2=arr.get("W_s2"))
         n += chunk
         passes += 1
         el = time.perf_counter() - t0

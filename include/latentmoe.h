@@ -20,6 +20,12 @@
  *            plus the residual (a reading)
  * Standard mode (W_down == W_up == NULL, l == d): z = x and out = x + s, the
  * plain MoE of 10100.com Figure 3a, run through the same kernels.
+ * Optional shared expert (latentmoe_forward_shared, dims.m_shared > 0): a
+ * dense FFN at the full width d beside the routed experts, its output added:
+ *   out   += W_shared2 relu(W_shared1 x)^2
+ * (the shared expert stays at d: qingkeai.online article, same section, last
+ * paragraph; its output is summed with the routed one: 10100.com article,
+ * section 3.3).  Its width and activation are readings.
  *
  * Layout: every array is dense and row-major, with the reduction index
  * fastest (the PyTorch nn.Linear [out, in] convention), so both operands of
@@ -29,6 +35,7 @@
  *   W1       [N, m, l]  (expert e at W1 + e*m*l)
  *   W2       [N, l, m]  (expert e at W2 + e*l*m)
  *   W_up     [d, l]
+ *   W_shared1 [m_shared, d]    W_shared2 [d, m_shared]
  *   router_bias [N] float32, topk_ids [T, K] int32, topk_gates [T, K] float32
  * One element type covers x, the weights and out: float32 or bfloat16.
  * Accumulation is float32; router logits and gates are float32 throughout.
@@ -81,6 +88,7 @@ typedef struct {
     int32_t m;      /* expert hidden width, multiple of 64 */
     int32_t dtype;  /* lmoe_dtype */
     int32_t path;   /* lmoe_path */
+    int32_t m_shared; /* shared expert width: 0 (none) or a multiple of 64 */
 } lmoe_dims;
 
 /* Bytes of device workspace latentmoe_forward needs for these dims and K
@@ -93,7 +101,8 @@ size_t latentmoe_workspace_bytes(const lmoe_dims* dims, int32_t K);
  * (it changes both the selection and the gates).
  * topk_ids / topk_gates: NULL, or caller buffers that receive the selected
  * experts in rank order (largest logit first) and their gates.
- * out must not alias x or any weight.
+ * out must not alias x or any weight.  dims->m_shared must be 0 (the shared
+ * expert goes through latentmoe_forward_shared).
  */
 int latentmoe_forward(const void* x, const void* W_down, const void* W_router,
                       const void* W1, const void* W2, const void* W_up, int32_t K,
@@ -102,18 +111,35 @@ int latentmoe_forward(const void* x, const void* W_down, const void* W_router,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * latentmoe_forward with stage timing, for benchmarks and profilers.
+ * The layer forward with a shared expert: latentmoe_forward plus
+ * out += W_shared2 relu(W_shared1 x)^2, W_shared1 [m_shared, d] and
+ * W_shared2 [d, m_shared] in the element type of x, dims->m_shared > 0 (a
+ * multiple of 64).  The shared expert's output is added to the layer's before
+ * the single rounding of out.  Same memory, stream and error rules.
+ */
+int latentmoe_forward_shared(const void* x, const void* W_down, const void* W_router,
+                             const void* W1, const void* W2, const void* W_up,
+                             const void* W_shared1, const void* W_shared2, int32_t K,
+                             void* out, const lmoe_dims* dims, const float* router_bias,
+                             int32_t* topk_ids, float* topk_gates,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * latentmoe_forward_shared with stage timing, for benchmarks and profilers
+ * (W_shared1 = W_shared2 = NULL and dims->m_shared = 0: latentmoe_forward).
  * events: an array of LMOE_N_STAGE_EVENTS hipEvent_t handles created by
  * the caller; NULL entries are skipped.  Event i is recorded on `stream` at
- * the start of stage i, the last one after the final stage.  Stages: 0 projection + router logits, 1 top-K gates,
- * 2 dispatch, 3 expert FFN first kernel (the whole FFN on the streaming path),
- * 4 expert FFN second kernel (empty on the streaming path), 5 combine,
- * 6 projection back to d (empty in standard mode).  The computation is the
- * same as latentmoe_forward's.
+ * the start of stage i, the last one after the final stage.  Stages:
+ * 0 projection + router logits (and the shared expert's two products),
+ * 1 top-K gates, 2 dispatch, 3 expert FFN first kernel (the whole FFN on the
+ * streaming path), 4 expert FFN second kernel (empty on the streaming path),
+ * 5 combine, 6 projection back to d (empty in standard mode).  The
+ * computation is the same as the untimed call's.
  */
 #define LMOE_N_STAGE_EVENTS 8
 int latentmoe_forward_timed(const void* x, const void* W_down, const void* W_router,
-                            const void* W1, const void* W2, const void* W_up, int32_t K,
+                            const void* W1, const void* W2, const void* W_up,
+                            const void* W_shared1, const void* W_shared2, int32_t K,
                             void* out, const lmoe_dims* dims, const float* router_bias,
                             int32_t* topk_ids, float* topk_gates,
                             void* workspace, size_t workspace_bytes, void* stream,

@@ -25,6 +25,7 @@ STAGES = ("proj_router", "topk", "dispatch", "ffn1", "ffn2", "combine", "up")
 EXPORTED = (
     "latentmoe_workspace_bytes",
     "latentmoe_forward",
+    "latentmoe_forward_shared",
     "latentmoe_forward_timed",
     "latentmoe_status_string",
     "latentmoe_last_error",
@@ -34,7 +35,7 @@ EXPORTED = (
 
 
 class lmoe_dims(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_int32) for n in ("T", "d", "l", "N", "m", "dtype", "path")]
+    _fields_ = [(n, ctypes.c_int32) for n in ("T", "d", "l", "N", "m", "dtype", "path", "m_shared")]
 
 
 class lmoe_ws_layout(ctypes.Structure):
@@ -63,9 +64,12 @@ def lib():
         L.latentmoe_forward.restype = ctypes.c_int
         L.latentmoe_forward.argtypes = [P, P, P, P, P, P, ctypes.c_int32, P, ctypes.POINTER(lmoe_dims),
                                         P, P, P, P, ctypes.c_size_t, P]
+        L.latentmoe_forward_shared.restype = ctypes.c_int
+        L.latentmoe_forward_shared.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_int32, P,
+                                               ctypes.POINTER(lmoe_dims), P, P, P, P, ctypes.c_size_t, P]
         L.latentmoe_forward_timed.restype = ctypes.c_int
-        L.latentmoe_forward_timed.argtypes = [P, P, P, P, P, P, ctypes.c_int32, P, ctypes.POINTER(lmoe_dims),
-                                              P, P, P, P, ctypes.c_size_t, P, P]
+        L.latentmoe_forward_timed.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_int32, P,
+                                              ctypes.POINTER(lmoe_dims), P, P, P, P, ctypes.c_size_t, P, P]
         L.latentmoe_status_string.restype = ctypes.c_char_p
         L.latentmoe_status_string.argtypes = [ctypes.c_int]
         L.latentmoe_last_error.restype = ctypes.c_char_p
@@ -79,12 +83,12 @@ def lib():
     return _lib
 
 
-def make_dims(T, d, l, N, m, dtype, path=LMOE_PATH_AUTO) -> lmoe_dims:
+def make_dims(T, d, l, N, m, dtype, path=LMOE_PATH_AUTO, m_shared=0) -> lmoe_dims:
     if isinstance(dtype, torch.dtype):
         dtype = LMOE_F32 if dtype == torch.float32 else LMOE_BF16
     elif isinstance(dtype, str):
         dtype = LMOE_F32 if dtype == "f32" else LMOE_BF16
-    return lmoe_dims(T, d, l, N, m, dtype, path)
+    return lmoe_dims(T, d, l, N, m, dtype, path, m_shared)
 
 
 def latentmoe_workspace_bytes(dims: lmoe_dims, K: int) -> int:
@@ -126,13 +130,15 @@ def _check(rc: int) -> None:
 def latentmoe_forward(x, W_down, W_router, W1, W2, W_up, K: int, out, dims: lmoe_dims,
                       router_bias=None, topk_ids=None, topk_gates=None, workspace=None,
                       workspace_bytes: Optional[int] = None, stream=None, check: bool = True,
-                      events=None) -> int:
+                      events=None, W_shared1=None, W_shared2=None) -> int:
     """Call the C entry point with raw device pointers taken from tensors.
 
     `stream`: a torch.cuda.Stream, a raw hipStream_t int, or None for torch's
     current stream.  `events`: None, or a ctypes array of
     LMOE_N_STAGE_EVENTS hipEvent_t handles (calls latentmoe_forward_timed).
-    Returns the status (raises on failure when check=True).
+    W_shared1 / W_shared2 (with dims.m_shared > 0): calls
+    latentmoe_forward_shared.  Returns the status (raises on failure when
+    check=True).
     """
     if stream is None:
         stream_ptr = torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
@@ -142,13 +148,16 @@ def latentmoe_forward(x, W_down, W_router, W1, W2, W_up, K: int, out, dims: lmoe
         stream_ptr = stream.cuda_stream
     if workspace_bytes is None:
         workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    args = (_ptr(x), _ptr(W_down), _ptr(W_router), _ptr(W1), _ptr(W2), _ptr(W_up), int(K), _ptr(out),
-            ctypes.byref(dims), _ptr(router_bias), _ptr(topk_ids), _ptr(topk_gates), _ptr(workspace),
-            ctypes.c_size_t(workspace_bytes), stream_ptr)
-    if events is None:
-        rc = lib().latentmoe_forward(*args)
+    head = (_ptr(x), _ptr(W_down), _ptr(W_router), _ptr(W1), _ptr(W2), _ptr(W_up))
+    shared = (_ptr(W_shared1), _ptr(W_shared2))
+    tail = (int(K), _ptr(out), ctypes.byref(dims), _ptr(router_bias), _ptr(topk_ids), _ptr(topk_gates),
+            _ptr(workspace), ctypes.c_size_t(workspace_bytes), stream_ptr)
+    if events is not None:
+        rc = lib().latentmoe_forward_timed(*head, *shared, *tail, ctypes.cast(events, ctypes.c_void_p))
+    elif W_shared1 is not None or W_shared2 is not None:
+        rc = lib().latentmoe_forward_shared(*head, *shared, *tail)
     else:
-        rc = lib().latentmoe_forward_timed(*args, ctypes.cast(events, ctypes.c_void_p))
+        rc = lib().latentmoe_forward(*head, *tail)
     if check:
         _check(rc)
     return rc
@@ -158,7 +167,8 @@ def dims_for(inputs: dict, K: int, path: int = LMOE_PATH_AUTO) -> lmoe_dims:
     x, W1 = inputs["x"], inputs["W1"]
     T, d = x.shape
     N, m, l = W1.shape
-    return make_dims(T, d, l, N, m, x.dtype, path)
+    ws1 = inputs.get("W_s1")
+    return make_dims(T, d, l, N, m, x.dtype, path, 0 if ws1 is None else ws1.shape[0])
 
 
 def alloc_workspace(dims: lmoe_dims, K: int, device) -> torch.Tensor:
@@ -187,7 +197,8 @@ def forward(inputs: dict, K: int, *, path: int = LMOE_PATH_AUTO, workspace: Opti
         gates = torch.empty((x.shape[0], K), dtype=torch.float32, device=x.device)
     latentmoe_forward(x, inputs.get("W_down"), inputs["W_router"], inputs["W1"], inputs["W2"],
                       inputs.get("W_up"), K, out, dims, router_bias=inputs.get("bias"),
-                      topk_ids=ids, topk_gates=gates, workspace=workspace, stream=stream)
+                      topk_ids=ids, topk_gates=gates, workspace=workspace, stream=stream,
+                      W_shared1=inputs.get("W_s1"), W_shared2=inputs.get("W_s2"))
     if routing:
         return out, ids, gates, workspace
     return out

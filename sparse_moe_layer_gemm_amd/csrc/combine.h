@@ -84,10 +84,15 @@ __global__ __launch_bounds__(256) void combine_kernel(LayerArgs a, int nsplit, i
     if (!live) return;
     E* dst;
     if (a.standard) {
+        // out = x + s (+ the shared expert's float32 output), rounded once
         const size_t o = (size_t)t * a.d + c0;
         const E* xp = static_cast<const E*>(a.x) + o;
 #pragma unroll
         for (int i = 0; i < VPC; ++i) acc[i] += to_f32(xp[i]);
+        if (a.y_s) {
+#pragma unroll
+            for (int i = 0; i < VPC; ++i) acc[i] += a.y_s[o + i];
+        }
         dst = static_cast<E*>(a.out) + o;
     } else {
         dst = static_cast<E*>(a.s) + (size_t)t * a.l + c0;

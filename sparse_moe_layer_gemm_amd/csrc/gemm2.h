@@ -159,6 +159,67 @@ struct RowCtx<Up<bf16>> {
     }
 };
 
+template <>
+struct RowCtx<Shared1<bf16>> {
+    static constexpr bool kRowVal = false;
+    __device__ static float row_value(const LayerArgs&, int, int) { return 0.0f; }
+    using ColPre = NoPre;
+    __device__ static NoPre col_load(const LayerArgs&, int) { return NoPre{}; }
+    using Pre = NoPre;
+    __device__ static NoPre load(const LayerArgs&, int, int, int) { return NoPre{}; }
+    __device__ static void store(const LayerArgs& a, int, int r, int c0, f32x4 v, const NoPre&, const NoPre&,
+                                 float) {
+        for (int i = 0; i < 4; ++i) {
+            const float t = v[i] > 0.0f ? v[i] : 0.0f;
+            v[i] = t * t;
+        }
+        store_cols(static_cast<bf16*>(a.a_s) + (size_t)r * a.m_s + c0, c0, a.m_s, v);
+    }
+};
+
+template <>
+struct RowCtx<Shared2<bf16>> {
+    static constexpr bool kRowVal = false;
+    __device__ static float row_value(const LayerArgs&, int, int) { return 0.0f; }
+    using ColPre = NoPre;
+    __device__ static NoPre col_load(const LayerArgs&, int) { return NoPre{}; }
+    using Pre = NoPre;
+    __device__ static NoPre load(const LayerArgs&, int, int, int) { return NoPre{}; }
+    __device__ static void store(const LayerArgs& a, int, int r, int c0, f32x4 v, const NoPre&, const NoPre&,
+                                 float) {
+        store_cols(a.y_s + (size_t)r * a.d + c0, c0, a.d, v);
+    }
+};
+
+// out = x + W_up s + y_s: the residual row and the shared expert's float32
+// output are loaded together before the stores.
+struct UpSharedPre {
+    uint2 x;
+    f32x4 ys;
+};
+
+template <>
+struct RowCtx<UpShared<bf16>> {
+    static constexpr bool kRowVal = false;
+    __device__ static float row_value(const LayerArgs&, int, int) { return 0.0f; }
+    using ColPre = NoPre;
+    __device__ static NoPre col_load(const LayerArgs&, int) { return NoPre{}; }
+    using Pre = UpSharedPre;
+    __device__ static UpSharedPre load(const LayerArgs& a, int, int r, int c0) {
+        const size_t i = (size_t)r * a.d + c0;
+        return UpSharedPre{*reinterpret_cast<const uint2*>(static_cast<const bf16*>(a.x) + i),
+                           *reinterpret_cast<const f32x4*>(a.y_s + i)};
+    }
+    __device__ static void store(const LayerArgs& a, int, int r, int c0, f32x4 v, const UpSharedPre& p,
+                                 const NoPre&, float) {
+        v[0] += __uint_as_float(p.x.x << 16) + p.ys[0];
+        v[1] += __uint_as_float(p.x.x & 0xffff0000u) + p.ys[1];
+        v[2] += __uint_as_float(p.x.y << 16) + p.ys[2];
+        v[3] += __uint_as_float(p.x.y & 0xffff0000u) + p.ys[3];
+        store_cols(static_cast<bf16*>(a.out) + (size_t)r * a.d + c0, c0, a.d, v);
+    }
+};
+
 template <class P, int BM, int BN, int NWM, int NWN>
 __global__ __launch_bounds__(64 * NWM * NWN) void gemm2_kernel(LayerArgs a, int nrow_tiles, int ncol_tiles) {
     using S = G2Shape<BM, BN, NWM, NWN>;

@@ -91,7 +91,7 @@ struct Plan {
     long long max_tiles = 0;
     size_t es = 2;
     size_t z, logits, ids, gates, counts, offsets, perm, slot_of, blk_counts, blk_offsets, tiles, n_tiles,
-        active, n_active, abuf, ybuf, s, part, total;
+        active, n_active, abuf, ybuf, s, part, a_s, y_s, total;
 };
 
 bool mult64(int v) { return v > 0 && v % 64 == 0; }
@@ -125,6 +125,10 @@ Plan make_plan(const lmoe_dims* dm, int32_t K) {
     }
     if (d.dtype != LMOE_F32 && d.dtype != LMOE_BF16) {
         p.status = fail(LMOE_EINVAL, "dtype=%d is not LMOE_F32 or LMOE_BF16", d.dtype);
+        return p;
+    }
+    if (d.m_shared < 0 || d.m_shared % 64 != 0) {
+        p.status = fail(LMOE_EINVAL, "m_shared=%d must be 0 or a positive multiple of 64", d.m_shared);
         return p;
     }
     if (d.path != LMOE_PATH_AUTO && d.path != LMOE_PATH_STREAM && d.path != LMOE_PATH_TILED) {
@@ -189,6 +193,8 @@ Plan make_plan(const lmoe_dims* dm, int32_t K) {
     if (p.skinny)
         part_bytes = std::max(proj_part_floats(d.l + d.N, d.T), proj_part_floats(d.N, d.T)) * d.T * 4;
     p.part = take(part_bytes);
+    p.a_s = take((size_t)d.T * d.m_shared * p.es);
+    p.y_s = take(d.m_shared > 0 ? (size_t)d.T * d.d * 4 : 0);
     p.total = o;
     return p;
 }
@@ -267,6 +273,22 @@ void launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* events
     } else {
         gemm_simt_kernel<ProjRouter<float>><<<dim3(cdiv(a.T, kSimtM), cdiv(ncols_pr, kSimtN)), b256, 0, st>>>(a);
     }
+    // the shared expert: a_s = relu(W_s1 x)^2, y_s = W_s2 a_s (float32),
+    // added to the output by the up-projection (latent) or the combine
+    if (a.m_s > 0) {
+        if constexpr (sizeof(E) == 2) {
+            if (p.skinny) {
+                skinny_kernel<Shared1<bf16>><<<dim3(cdiv(a.m_s, 16), cdiv(a.T, 64)), b1024, 0, st>>>(a);
+                skinny_kernel<Shared2<bf16>><<<dim3(cdiv(a.d, 16), cdiv(a.T, 64)), b1024, 0, st>>>(a);
+            } else {
+                launch_g2<Shared1<bf16>, G2Small>(a, cdiv(a.T, G2Small::BM), cdiv(a.m_s, G2Small::BN), st);
+                launch_g2<Shared2<bf16>, G2Small>(a, cdiv(a.T, G2Small::BM), cdiv(a.d, G2Small::BN), st);
+            }
+        } else {
+            gemm_simt_kernel<Shared1<float>><<<dim3(cdiv(a.T, kSimtM), cdiv(a.m_s, kSimtN)), b256, 0, st>>>(a);
+            gemm_simt_kernel<Shared2<float>><<<dim3(cdiv(a.T, kSimtM), cdiv(a.d, kSimtN)), b256, 0, st>>>(a);
+        }
+    }
     // 2. top-K gates
     mark(1);
     {
@@ -331,7 +353,7 @@ void launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* events
         launch_combine<E, YT>(a, 1, 0, st);
     // 6. back to d with the residual
     mark(6);
-    if (!a.standard) {
+    if (!a.standard && a.m_s == 0) {
         if constexpr (sizeof(E) == 2) {
             if (p.skinny)
                 skinny_kernel<Up<bf16>><<<dim3(cdiv(a.d, 16), cdiv(a.T, 64)), b1024, 0, st>>>(a);
@@ -339,6 +361,17 @@ void launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* events
                 launch_g2<Up<bf16>, UpTile>(a, cdiv(a.T, UpTile::BM), cdiv(a.d, UpTile::BN), st);
         } else {
             gemm_simt_kernel<Up<float>><<<dim3(cdiv(a.T, kSimtM), cdiv(a.d, kSimtN)), b256, 0, st>>>(a);
+        }
+    } else if (!a.standard) {
+        // with the shared expert's output added in the same epilogue (its
+        // wider per-row operands fit the 128 x 128 tile's registers)
+        if constexpr (sizeof(E) == 2) {
+            if (p.skinny)
+                skinny_kernel<UpShared<bf16>><<<dim3(cdiv(a.d, 16), cdiv(a.T, 64)), b1024, 0, st>>>(a);
+            else
+                launch_g2<UpShared<bf16>, G2Small>(a, cdiv(a.T, G2Small::BM), cdiv(a.d, G2Small::BN), st);
+        } else {
+            gemm_simt_kernel<UpShared<float>><<<dim3(cdiv(a.T, kSimtM), cdiv(a.d, kSimtN)), b256, 0, st>>>(a);
         }
     }
     mark(7);
@@ -377,9 +410,9 @@ int latentmoe_workspace_layout(const lmoe_dims* dims, int32_t K, lmoe_ws_layout*
 }
 
 static int forward_impl(const void* x, const void* W_down, const void* W_router, const void* W1, const void* W2,
-                        const void* W_up, int32_t K, void* out, const lmoe_dims* dims, const float* router_bias,
-                        int32_t* topk_ids, float* topk_gates, void* workspace, size_t workspace_bytes,
-                        void* stream, void* const* events) {
+                        const void* W_up, const void* W_s1, const void* W_s2, int32_t K, void* out,
+                        const lmoe_dims* dims, const float* router_bias, int32_t* topk_ids, float* topk_gates,
+                        void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
     g_last_error.clear();
     const Plan p = make_plan(dims, K);
     if (p.status != LMOE_OK) return p.status;
@@ -389,6 +422,9 @@ static int forward_impl(const void* x, const void* W_down, const void* W_router,
     if ((W_down == nullptr) != (W_up == nullptr))
         return fail(LMOE_EINVAL, "W_down and W_up must be both NULL (standard MoE) or both set");
     const bool standard = W_down == nullptr;
+    if ((d.m_shared > 0) != (W_s1 != nullptr) || (W_s1 == nullptr) != (W_s2 == nullptr))
+        return fail(LMOE_EINVAL, "W_shared1 and W_shared2 must be both set when m_shared > 0 and both NULL when "
+                                 "m_shared == 0 (m_shared=%d)", d.m_shared);
     if (standard && d.l != d.d) return fail(LMOE_EINVAL, "standard mode (no projections) needs l == d");
     if (!workspace) return fail(LMOE_EWORKSPACE, "workspace is NULL");
     if (workspace_bytes < p.total)
@@ -398,7 +434,7 @@ static int forward_impl(const void* x, const void* W_down, const void* W_router,
     if (overlaps(out, xbytes, workspace, p.total)) return fail(LMOE_EINVAL, "out must not alias the workspace");
     if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
         return fail(LMOE_EINVAL, "workspace must be 256-byte aligned");
-    const void* ptrs[] = {x, W_down, W_router, W1, W2, W_up, out};
+    const void* ptrs[] = {x, W_down, W_router, W1, W2, W_up, W_s1, W_s2, out};
     for (const void* q : ptrs)
         if (q && (reinterpret_cast<uintptr_t>(q) & 15) != 0)
             return fail(LMOE_EINVAL, "tensor pointers must be 16-byte aligned");
@@ -412,6 +448,9 @@ static int forward_impl(const void* x, const void* W_down, const void* W_router,
     a.W1 = W1;
     a.W2 = W2;
     a.W_up = W_up;
+    a.W_s1 = W_s1;
+    a.W_s2 = W_s2;
+    a.m_s = d.m_shared;
     a.bias = router_bias;
     a.out = out;
     a.T = d.T;
@@ -440,6 +479,8 @@ static int forward_impl(const void* x, const void* W_down, const void* W_router,
     a.ybuf = ws + p.ybuf;
     a.s = ws + p.s;
     a.part = ws + p.part;
+    a.a_s = d.m_shared > 0 ? ws + p.a_s : nullptr;
+    a.y_s = d.m_shared > 0 ? reinterpret_cast<float*>(ws + p.y_s) : nullptr;
     a.tile_rows = p.tile_rows;
 
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -457,17 +498,32 @@ int latentmoe_forward(const void* x, const void* W_down, const void* W_router, c
                       const void* W_up, int32_t K, void* out, const lmoe_dims* dims, const float* router_bias,
                       int32_t* topk_ids, float* topk_gates, void* workspace, size_t workspace_bytes,
                       void* stream) {
-    return forward_impl(x, W_down, W_router, W1, W2, W_up, K, out, dims, router_bias, topk_ids, topk_gates,
-                        workspace, workspace_bytes, stream, nullptr);
+    if (dims && dims->m_shared != 0)
+        return fail(LMOE_EINVAL, "m_shared=%d: a shared expert goes through latentmoe_forward_shared",
+                    dims->m_shared);
+    return forward_impl(x, W_down, W_router, W1, W2, W_up, nullptr, nullptr, K, out, dims, router_bias, topk_ids,
+                        topk_gates, workspace, workspace_bytes, stream, nullptr);
+}
+
+int latentmoe_forward_shared(const void* x, const void* W_down, const void* W_router, const void* W1,
+                             const void* W2, const void* W_up, const void* W_shared1, const void* W_shared2,
+                             int32_t K, void* out, const lmoe_dims* dims, const float* router_bias,
+                             int32_t* topk_ids, float* topk_gates, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+    if (dims && dims->m_shared <= 0)
+        return fail(LMOE_EINVAL, "latentmoe_forward_shared needs m_shared > 0 (got %d)", dims->m_shared);
+    return forward_impl(x, W_down, W_router, W1, W2, W_up, W_shared1, W_shared2, K, out, dims, router_bias,
+                        topk_ids, topk_gates, workspace, workspace_bytes, stream, nullptr);
 }
 
 int latentmoe_forward_timed(const void* x, const void* W_down, const void* W_router, const void* W1,
-                            const void* W2, const void* W_up, int32_t K, void* out, const lmoe_dims* dims,
-                            const float* router_bias, int32_t* topk_ids, float* topk_gates, void* workspace,
-                            size_t workspace_bytes, void* stream, void* const* events) {
+                            const void* W2, const void* W_up, const void* W_shared1, const void* W_shared2,
+                            int32_t K, void* out, const lmoe_dims* dims, const float* router_bias,
+                            int32_t* topk_ids, float* topk_gates, void* workspace, size_t workspace_bytes,
+                            void* stream, void* const* events) {
     if (!events) return fail(LMOE_EINVAL, "events is NULL");
-    return forward_impl(x, W_down, W_router, W1, W2, W_up, K, out, dims, router_bias, topk_ids, topk_gates,
-                        workspace, workspace_bytes, stream, events);
+    return forward_impl(x, W_down, W_router, W1, W2, W_up, W_shared1, W_shared2, K, out, dims, router_bias,
+                        topk_ids, topk_gates, workspace, workspace_bytes, stream, events);
 }
 
 const char* latentmoe_status_string(int status) {

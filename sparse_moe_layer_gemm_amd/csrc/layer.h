@@ -18,10 +18,13 @@ struct LayerArgs {
     const void* W1;        // [N, m, l]
     const void* W2;        // [N, l, m]
     const void* W_up;      // [d, l] or NULL (standard mode)
+    const void* W_s1;      // [m_s, d] shared expert, or NULL
+    const void* W_s2;      // [d, m_s]
     const float* bias;     // [N] or NULL
     void* out;             // [T, d]
     int T, d, l, N, m, K;
     int standard;
+    int m_s;               // shared expert width (0: none)
     // workspace
     const void* z;         // [T, l] latent tokens (== x in standard mode)
     void* z_w;             // writable view of z (latent mode)
@@ -42,6 +45,8 @@ struct LayerArgs {
     void* ybuf;            // expert outputs (layout depends on the path)
     void* s;               // [T, l] gate-weighted latent sum (latent mode)
     void* part;            // split-reduction partial tiles of the skinny projection
+    void* a_s;             // [T, m_s] relu(W_s1 x)^2 (shared expert)
+    float* y_s;            // [T, d] W_s2 a_s, float32 (shared expert)
     int tile_rows;         // rows per grouped-GEMM tile
 };
 
@@ -152,6 +157,55 @@ struct Up {
     __device__ static void store(const LayerArgs& a, int, int r, int c, float v) {
         const size_t i = (size_t)r * a.d + c;
         static_cast<E*>(a.out)[i] = from_f32<E>(to_f32(static_cast<const E*>(a.x)[i]) + v);
+    }
+};
+
+// Shared expert, first product: a_s = relu(W_s1 x)^2 over all tokens.
+template <class E>
+struct Shared1 {
+    __device__ static bool tile(const LayerArgs& a, int bx, int bm, int& grp, int& row0, int& row_end) {
+        return Up<E>::tile(a, bx, bm, grp, row0, row_end);
+    }
+    __device__ static int row_tiles(const LayerArgs&, int host_count) { return host_count; }
+    __device__ static int ncols(const LayerArgs& a) { return a.m_s; }
+    __device__ static int kdim(const LayerArgs& a) { return a.d; }
+    __device__ static const E* a_row(const LayerArgs& a, int, int r) {
+        return static_cast<const E*>(a.x) + (size_t)r * a.d;
+    }
+    __device__ static const E* b_row(const LayerArgs& a, int, int c) {
+        return static_cast<const E*>(a.W_s1) + (size_t)c * a.d;
+    }
+    __device__ static void store(const LayerArgs& a, int, int r, int c, float v) {
+        const float t = v > 0.0f ? v : 0.0f;
+        static_cast<E*>(a.a_s)[(size_t)r * a.m_s + c] = from_f32<E>(t * t);
+    }
+};
+
+// Shared expert, second product: y_s = W_s2 a_s, kept in float32 so that the
+// layer's output is still rounded once (in the up-projection or combine).
+template <class E>
+struct Shared2 {
+    __device__ static bool tile(const LayerArgs& a, int bx, int bm, int& grp, int& row0, int& row_end) {
+        return Up<E>::tile(a, bx, bm, grp, row0, row_end);
+    }
+    __device__ static int row_tiles(const LayerArgs&, int host_count) { return host_count; }
+    __device__ static int ncols(const LayerArgs& a) { return a.d; }
+    __device__ static int kdim(const LayerArgs& a) { return a.m_s; }
+    __device__ static const E* a_row(const LayerArgs& a, int, int r) {
+        return static_cast<const E*>(a.a_s) + (size_t)r * a.m_s;
+    }
+    __device__ static const E* b_row(const LayerArgs& a, int, int c) {
+        return static_cast<const E*>(a.W_s2) + (size_t)c * a.m_s;
+    }
+    __device__ static void store(const LayerArgs& a, int, int r, int c, float v) { a.y_s[(size_t)r * a.d + c] = v; }
+};
+
+// out = x + W_up s + y_s (latent mode with a shared expert), one rounding.
+template <class E>
+struct UpShared : Up<E> {
+    __device__ static void store(const LayerArgs& a, int, int r, int c, float v) {
+        const size_t i = (size_t)r * a.d + c;
+        static_cast<E*>(a.out)[i] = from_f32<E>(to_f32(static_cast<const E*>(a.x)[i]) + a.y_s[i] + v);
     }
 };
 

@@ -24,10 +24,13 @@ operands of every product):
   W2       [N, l, m]     y_i   = sum_j W2[e, i, j] a_j
   W_up     [d, l]        out_n = x_n + sum_i W_up[n, i] s_i
   bias     [N] float32 (skewed workload only)
+  W_s1     [m_s, d], W_s2 [d, m_s]   shared expert (the *_shared workloads)
 
 Recipe: one CPU torch.Generator seeded with `seed`; draws in the order x,
 W_down, W_router, W1 (one draw of [m, l] per expert, expert 0 first), W2 (one
-[l, m] draw per expert), W_up, bias.  Every draw is float32 N(0, 1); weights
+[l, m] draw per expert), W_up, bias, W_s1, W_s2 (the last two only for a
+shared expert, so the other arrays are the same with or without one).
+Every draw is float32 N(0, 1); weights
 are multiplied by 1/sqrt(fan_in) in float32; for bf16 workloads every array
 except the bias is then rounded to bfloat16 (round-to-nearest-even).
 x ~ N(0, 1) throughout, so routing is near uniform except where the fixed
@@ -54,6 +57,7 @@ class Workload:
     dtype: str            # "f32" or "bf16"
     standard: bool = False  # no projections: l == d, z = x, out = x + s
     bias: bool = False      # fixed per-expert logit bias ~ N(0, 1)
+    m_shared: int = 0       # shared expert width (0: none)
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -67,7 +71,8 @@ class Workload:
         return 4 if self.dtype == "f32" else 2
 
 
-# The five workloads (the standard-MoE one at two token counts).
+# The five workloads (the standard-MoE one at two token counts), and the
+# decode / prefill layers with a shared expert.
 WORKLOADS: Dict[str, Workload] = {
     "tiny_f32": Workload("tiny_f32", T=64, d=256, l=64, N=32, K=4, m=128, dtype="f32"),
     "decode": Workload("decode", T=32, d=4096, l=1024, N=512, K=22, m=768, dtype="bf16"),
@@ -78,6 +83,12 @@ WORKLOADS: Dict[str, Workload] = {
                                  dtype="bf16", standard=True),
     "skewed": Workload("skewed", T=8192, d=7168, l=1792, N=896, K=16, m=512, dtype="bf16",
                        bias=True),
+    # The decode and prefill layers with a shared expert at the full width d
+    # (the pages keep it at d but give no width: m_shared = m is a choice).
+    "decode_shared": Workload("decode_shared", T=32, d=4096, l=1024, N=512, K=22, m=768, dtype="bf16",
+                              m_shared=768),
+    "prefill_shared": Workload("prefill_shared", T=16384, d=4096, l=1024, N=512, K=22, m=768, dtype="bf16",
+                               m_shared=768),
 }
 
 
@@ -92,7 +103,7 @@ def make_inputs(w: Workload, seed: int = 0, *, x_only_seed: Optional[int] = None
     """Draw the inputs of workload `w` on the CPU.
 
     Returns a dict with keys x, W_down, W_router, W1, W2, W_up, bias (None
-    where the workload has no such array).  Arrays are contiguous CPU tensors
+    where the workload has no such array), and W_s1, W_s2 for a shared expert.  Arrays are contiguous CPU tensors
     in the workload's storage dtype; bias stays float32.
     """
     gen = torch.Generator(device="cpu")
@@ -118,6 +129,9 @@ def make_inputs(w: Workload, seed: int = 0, *, x_only_seed: Optional[int] = None
     else:
         out["W_up"] = _draw(gen, (w.d, w.l), 1.0 / math.sqrt(w.l)).to(dt)
     out["bias"] = _draw(gen, (w.N,), None) if w.bias else None
+    if w.m_shared > 0:
+        out["W_s1"] = _draw(gen, (w.m_shared, w.d), 1.0 / math.sqrt(w.d)).to(dt)
+        out["W_s2"] = _draw(gen, (w.d, w.m_shared), 1.0 / math.sqrt(w.m_shared)).to(dt)
     if x_only_seed is not None:
         g2 = torch.Generator(device="cpu")
         g2.manual_seed(x_only_seed)

@@ -16,7 +16,7 @@ Comparison rules:
     number of intermediate bf16 roundings on the path taken, each of relative
     size 2^-9 at up to ~5 RMS per element: 3 on the streaming path (z,
     relu(h)^2, s) and 4 on the tiled path, which also stores the gate-scaled
-    expert outputs in bf16.  (A numpy emulation of these rounding points
+    expert outputs in bf16; one more with a shared expert (its relu(h)^2).  (A numpy emulation of these rounding points
     reproduces the GPU's worst elements exactly.);
   * dispatch arrays: bit-exact against a stable counting sort of the GPU's
     own ids (computed here with numpy).
@@ -53,7 +53,8 @@ def oracle_arrays(inp):
 
 def run_oracle(arr, K, sel=None, forced=None):
     return O.forward(arr["x"], arr["W_down"], arr["W_router"], arr["W1"], arr["W2"], arr["W_up"], K,
-                     bias=arr["bias"], standard=arr["W_down"] is None, sel=sel, forced_ids=forced)
+                     bias=arr["bias"], standard=arr["W_down"] is None, sel=sel, forced_ids=forced,
+                     W_s1=arr.get("W_s1"), W_s2=arr.get("W_s2"))
 
 
 def expected_dispatch(ids: np.ndarray, N: int):
@@ -134,6 +135,7 @@ def compare(w: Workload, inp, K: int, path: int = B.LMOE_PATH_AUTO, sample: Opti
         moe = ref_out - x64(inp["x"])[sel]
         moe_rms = float(np.sqrt(np.mean(moe ** 2)))
         n_round = 3 if B.latentmoe_resolved_path(dims, K) == B.LMOE_PATH_STREAM else 4
+        n_round += 1 if inp.get("W_s1") is not None else 0   # the shared expert's relu(h)^2
         tol = half_ulp_bf16(np.maximum(np.abs(ref_out), np.abs(out_g[sel]))) + n_round * 1e-2 * moe_rms
         rule = f"ulp/2 + {n_round}e-2*rms(moe)"
     frac = float((err / tol).max())

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def dims_of(w, path=B.LMOE_PATH_AUTO):
-    return B.make_dims(w.T, w.d, w.l, w.N, w.m, w.dtype, path)
+    return B.make_dims(w.T, w.d, w.l, w.N, w.m, w.dtype, path, w.m_shared)
 
 
 @pytest.mark.parametrize("name", sorted(WORKLOADS))
@@ -75,7 +75,8 @@ def test_resolved_paths(lib):
 
 @pytest.mark.parametrize("field,value,K", [
     ("T", 0, 4), ("d", 100, 4), ("l", 0, 4), ("m", 65, 4), ("N", 0, 4), ("N", 4096, 4),
-    ("dtype", 7, 4), ("path", 9, 4), (None, None, 0), (None, None, 33), (None, None, 65),
+    ("dtype", 7, 4), ("path", 9, 4), ("m_shared", 96, 4), ("m_shared", -64, 4),
+    (None, None, 0), (None, None, 33), (None, None, 65),
 ])
 def test_invalid_dims_rejected(lib, field, value, K):
     d = dims_of(WORKLOADS["tiny_f32"])
@@ -118,6 +119,34 @@ def test_forward_argument_checks(lib):
     assert call(d, w.K, W2=FAKE + (4 << 30) + 2) == B.LMOE_EINVAL
     ws = B.make_dims(w.T, w.d, w.l, w.N, w.m, "f32", B.LMOE_PATH_STREAM)
     assert call(ws, w.K) == B.LMOE_EUNSUPPORTED
+
+
+def call_shared(dims, K, **over):
+    args = dict(x=FAKE, W_down=FAKE + (1 << 30), W_router=FAKE + (2 << 30), W1=FAKE + (3 << 30),
+                W2=FAKE + (4 << 30), W_up=FAKE + (5 << 30), out=FAKE + (6 << 30),
+                workspace=FAKE + (7 << 30), workspace_bytes=B.latentmoe_workspace_bytes(dims, K),
+                W_shared1=FAKE + (8 << 30), W_shared2=FAKE + (9 << 30))
+    args.update(over)
+    P = ctypes.c_void_p
+    return B.lib().latentmoe_forward_shared(
+        P(args["x"]), P(args["W_down"]), P(args["W_router"]), P(args["W1"]), P(args["W2"]), P(args["W_up"]),
+        None if args["W_shared1"] is None else P(args["W_shared1"]),
+        None if args["W_shared2"] is None else P(args["W_shared2"]), K, P(args["out"]), ctypes.byref(dims),
+        None, None, None, P(args["workspace"]), ctypes.c_size_t(args["workspace_bytes"]), None)
+
+
+def test_shared_expert_argument_checks(lib):
+    w = WORKLOADS["decode_shared"]
+    d = dims_of(w)
+    plain = dims_of(WORKLOADS["decode"])
+    assert B.latentmoe_workspace_bytes(d, w.K) > B.latentmoe_workspace_bytes(plain, w.K)
+    assert call(d, w.K) == B.LMOE_EINVAL                                  # m_shared > 0 needs the _shared call
+    assert "latentmoe_forward_shared" in B.latentmoe_last_error()
+    assert call_shared(plain, w.K) == B.LMOE_EINVAL                       # the _shared call needs m_shared > 0
+    assert call_shared(d, w.K, W_shared2=None) == B.LMOE_EINVAL           # both shared weights or none
+    assert call_shared(d, w.K, W_shared1=None, W_shared2=None) == B.LMOE_EINVAL
+    assert call_shared(d, w.K, W_shared2=FAKE + (9 << 30) + 2) == B.LMOE_EINVAL   # misaligned
+    assert call_shared(d, w.K, workspace_bytes=B.latentmoe_workspace_bytes(plain, w.K)) == B.LMOE_EWORKSPACE
 
 
 def test_status_strings(lib):

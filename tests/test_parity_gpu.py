@@ -104,6 +104,47 @@ def test_standard_decode_batch_sweep(T):
     P.compare(w, make_inputs(w, 8), w.K, tag=f"standard_decode_T{T}")
 
 
+# --- the shared expert at full d ---------------------------------------------
+
+@pytest.mark.parametrize("path", [B.LMOE_PATH_AUTO, TL])
+def test_decode_shared(path):
+    w = WORKLOADS["decode_shared"]
+    P.compare(w, P.gen(w, 0), w.K, path=path, tag=f"decode_shared/path{path}")
+
+
+def test_prefill_shared_sampled():
+    w = WORKLOADS["prefill_shared"]
+    P.compare(w, P.gen(w, 0), w.K, sample=sample_tokens(w.T, 96))
+
+
+@pytest.mark.parametrize("w", [
+    Workload("shared_latent", T=300, d=256, l=64, N=16, K=4, m=128, dtype="bf16", m_shared=192),
+    Workload("shared_latent_f32", T=70, d=128, l=64, N=8, K=2, m=64, dtype="f32", m_shared=64),
+    Workload("shared_standard", T=90, d=256, l=256, N=12, K=2, m=128, dtype="bf16", standard=True, m_shared=128),
+    Workload("shared_standard_f32", T=45, d=128, l=128, N=9, K=3, m=64, dtype="f32", standard=True,
+             m_shared=128),
+    Workload("shared_one_token", T=1, d=256, l=64, N=16, K=3, m=128, dtype="bf16", m_shared=64),
+], ids=lambda w: w.name)
+@pytest.mark.parametrize("path", [B.LMOE_PATH_AUTO, S, TL])
+def test_shared_expert_shapes(w, path):
+    if w.dtype == "f32" and path == S:
+        pytest.skip("the streaming FFN is bf16 only")
+    P.compare(w, make_inputs(w, 9), w.K, path=path, tag=f"{w.name}/path{path}")
+
+
+@pytest.mark.parametrize("path", [S, TL])
+def test_shared_expert_with_zero_w2_is_the_plain_layer(path):
+    """W_s2 = 0: bit-identical to the layer without a shared expert."""
+    w = Workload("shared_zero", T=100, d=256, l=64, N=16, K=4, m=128, dtype="bf16", m_shared=128)
+    inp = P.to_device(make_inputs(w, 10))
+    plain = {k: v for k, v in inp.items() if k not in ("W_s1", "W_s2")}
+    inp["W_s2"] = torch.zeros_like(inp["W_s2"])
+    a = B.forward(inp, w.K, path=path)
+    b = B.forward(plain, w.K, path=path)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
 # --- smaller shapes: several tiles, ragged tails, both FFN paths --------------
 
 SMALL_PREFILL = Workload("small_prefill", T=1000, d=512, l=128, N=64, K=6, m=256, dtype="bf16")
