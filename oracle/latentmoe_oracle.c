@@ -46,6 +46,13 @@
  * Element type of x and the weights: float32 (dtype 0) or bfloat16 bit
  * patterns (dtype 1).  Each element is widened to double at use; every sum is
  * accumulated in double in index order.
+ * Optional FP8 expert weights (experts_fp8 = 1): W1 and W2 hold OCP FP8
+ * E4M3 codes (one byte each: sign, 4 exponent bits with bias 7, 3 mantissa
+ * bits; exponent 0 is subnormal, 0x7F / 0xFF are NaN, no infinities), with
+ * one float32 scale per output row: W1[e][j][i] = e4m3(code) * s1[e*m + j],
+ * W2[e][i][j] = e4m3(code) * s2[e*l + i].  The pages name low-precision
+ * expert weights (NVFP4, MXFP4) without a format; this block-free per-row
+ * FP8 format is a reading.
  *
  * Parity pins: see tests/test_oracle_pins.py.  Every output here is pinned by
  * at least one check that does not re-run this code's formulas: brute-force
@@ -62,6 +69,7 @@ typedef struct {
     int32_t dtype;    /* 0: float32 arrays, 1: bfloat16 bit patterns */
     int32_t standard; /* 1: no projections (requires l == d) */
     int32_t m_shared; /* width of the shared expert, 0: none */
+    int32_t experts_fp8; /* 1: W1, W2 are E4M3 codes with per-row scales */
 } oracle_dims;
 
 static double widen(const void* base, int dtype, size_t i) {
@@ -70,6 +78,25 @@ static double widen(const void* base, int dtype, size_t i) {
     float f;
     memcpy(&f, &bits, sizeof f);
     return (double)f;
+}
+
+/* OCP FP8 E4M3 ("fn"): the value of one code */
+static double e4m3(uint8_t c) {
+    const int sign = c >> 7, ex = (c >> 3) & 15, man = c & 7;
+    double v;
+    if (ex == 15 && man == 7)
+        v = NAN;
+    else if (ex == 0)
+        v = ldexp((double)man, -9); /* subnormal: (man / 8) * 2^-6 */
+    else
+        v = ldexp(1.0 + man / 8.0, ex - 7);
+    return sign ? -v : v;
+}
+
+/* expert weight element i of a row whose scale is row_scale (FP8 mode) */
+static double expert_w(const oracle_dims* D, const void* W, const float* scale, size_t i, size_t row) {
+    if (D->experts_fp8) return e4m3(((const uint8_t*)W)[i]) * (double)scale[row];
+    return widen(W, D->dtype, i);
 }
 
 /* logit order: a outranks b if its logit is larger, or equal with a lower index */
@@ -84,7 +111,7 @@ static int outranks(const double* logit, int a, int b) {
  */
 static void one_token(const oracle_dims* D, int t, const void* x, const void* Wd,
                       const void* Wr, const void* W1, const void* W2, const void* Wu,
-                      const void* Ws1, const void* Ws2,
+                      const void* Ws1, const void* Ws2, const float* s1, const float* s2,
                       const float* bias, const int32_t* forced, double* out_t,
                       int32_t* ids_t, double* gates_t, double* logits_t, double* gap_t,
                       double* work) {
@@ -155,13 +182,13 @@ static void one_token(const oracle_dims* D, int t, const void* x, const void* Wd
         const size_t e = (size_t)ids_t[k];
         for (int j = 0; j < m; ++j) {
             double acc = 0.0;
-            for (int i = 0; i < l; ++i) acc += widen(W1, dt, (e * m + j) * l + i) * z[i];
+            for (int i = 0; i < l; ++i) acc += expert_w(D, W1, s1, (e * m + j) * l + i, e * m + j) * z[i];
             double a = acc > 0.0 ? acc : 0.0;
             h[j] = a * a;
         }
         for (int i = 0; i < l; ++i) {
             double acc = 0.0;
-            for (int j = 0; j < m; ++j) acc += widen(W2, dt, (e * l + i) * m + j) * h[j];
+            for (int j = 0; j < m; ++j) acc += expert_w(D, W2, s2, (e * l + i) * m + j, e * l + i) * h[j];
             s[i] += gates_t[k] * acc;
         }
     }
@@ -201,17 +228,19 @@ static void one_token(const oracle_dims* D, int t, const void* x, const void* Wd
  * the selection:  out [n_sel,d]  ids [n_sel,K]  gates [n_sel,K]
  * logits [n_sel,N]  gap [n_sel]  (gap = K-th minus (K+1)-th largest logit).
  * forced_ids [n_sel,K] or NULL.  Ws1 / Ws2: the shared expert, used only
- * when D->m_shared > 0.  Returns 0, or -1 on bad arguments.
+ * when D->m_shared > 0.  s1 [N*m] / s2 [N*l]: the FP8 expert weights' row
+ * scales, used only when D->experts_fp8.  Returns 0, or -1 on bad arguments.
  */
 int oracle_forward(const oracle_dims* D, const void* x, const void* Wd, const void* Wr,
                    const void* W1, const void* W2, const void* Wu, const void* Ws1,
-                   const void* Ws2, const float* bias,
+                   const void* Ws2, const float* s1, const float* s2, const float* bias,
                    const int32_t* sel, int32_t n_sel, const int32_t* forced_ids,
                    double* out, int32_t* ids, double* gates, double* logits, double* gap) {
     if (!D || !x || !Wr || !W1 || !W2 || !out || !ids || !gates || !logits || !gap) return -1;
     if (D->K < 1 || D->K > D->N || D->T < 0 || n_sel < 0 || D->m_shared < 0) return -1;
     if (D->standard ? (D->l != D->d) : (!Wd || !Wu)) return -1;
     if (D->m_shared > 0 && (!Ws1 || !Ws2)) return -1;
+    if (D->experts_fp8 && (!s1 || !s2)) return -1;
     for (int q = 0; q < n_sel; ++q) {
         int t = sel ? sel[q] : q;
         if (t < 0 || t >= D->T) return -1;
@@ -229,7 +258,7 @@ int oracle_forward(const oracle_dims* D, const void* x, const void* Wd, const vo
 #pragma omp for schedule(dynamic, 1)
             for (int q = 0; q < n_sel; ++q) {
                 int t = sel ? sel[q] : q;
-                one_token(D, t, x, Wd, Wr, W1, W2, Wu, Ws1, Ws2, bias,
+                one_token(D, t, x, Wd, Wr, W1, W2, Wu, Ws1, Ws2, s1, s2, bias,
                           forced_ids ? forced_ids + (size_t)q * D->K : NULL,
                           out + (size_t)q * D->d, ids + (size_t)q * D->K,
                           gates + (size_t)q * D->K, logits + (size_t)q * D->N, gap + q, work);

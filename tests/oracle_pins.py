@@ -25,6 +25,10 @@ What pins what:
   expert       a dense FFN on x evaluated with numpy float64 matmuls; with
                them on, adding the shared expert adds exactly that FFN;
                W_s2 = 0 gives the layer without it bit-exactly
+  FP8 experts  every E4M3 code, decoded by torch.float8_e4m3fn, times a
+               power-of-two row scale is exact in float32: the FP8 layer
+               equals the float32 layer on those weights bit-exactly; with
+               arbitrary row scales, N = K = 1 is a dense FFN in numpy
 """
 from __future__ import annotations
 
@@ -377,6 +381,62 @@ def pin_shared_expert(o):
         assert np.array_equal(run(o, Lz, K)["out"], without), "W_s2 = 0 changed the output"
 
 
+def fp8_decode(codes: np.ndarray) -> np.ndarray:
+    """E4M3 codes -> float64 through torch's float8_e4m3fn (not the oracle's decoder)."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).view(torch.float8_e4m3fn)
+    return t.to(torch.float64).numpy()
+
+
+def fp8_layer(seed, T, d, l, N, m, pow2_scales):
+    """A float32 layer whose expert weights are E4M3 codes with row scales.
+    Codes cycle through every non-NaN code."""
+    r = _rng(seed)
+    L = rand_layer(seed, T, d, l, N, m)
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    L["W1"] = np.resize(r.permutation(codes), N * m * l).reshape(N, m, l)
+    L["W2"] = np.resize(r.permutation(codes), N * l * m).reshape(N, l, m)
+    if pow2_scales:
+        L["W1_scale"] = np.ldexp(1.0, r.integers(-12, -6, N * m)).astype(np.float32)
+        L["W2_scale"] = np.ldexp(1.0, r.integers(-12, -6, N * l)).astype(np.float32)
+    else:
+        L["W1_scale"] = (r.random(N * m) * 1e-3 + 1e-4).astype(np.float32)
+        L["W2_scale"] = (r.random(N * l) * 1e-3 + 1e-4).astype(np.float32)
+    return L
+
+
+def run_fp8(o, L, K, **kw):
+    return o.forward(L["x"], L["W_down"], L["W_router"], L["W1"], L["W2"], L["W_up"], K,
+                     bias=L.get("bias"), W1_scale=L["W1_scale"], W2_scale=L["W2_scale"], **kw)
+
+
+def pin_fp8_experts(o):
+    """FP8 expert weights: decoded by an independent decoder, scaled per row."""
+    # power-of-two scales: code * scale is exact in float32, so the FP8 layer
+    # is the float32 layer on the decoded weights, bit for bit
+    T, d, l, N, m, K = 6, 16, 8, 4, 64, 2
+    L = fp8_layer(41, T, d, l, N, m, pow2_scales=True)
+    ref = dict(L)
+    ref["W1"] = (fp8_decode(L["W1"]) * L["W1_scale"].astype(np.float64).reshape(N, m, 1)).astype(np.float32)
+    ref["W2"] = (fp8_decode(L["W2"]) * L["W2_scale"].astype(np.float64).reshape(N, l, 1)).astype(np.float32)
+    assert np.array_equal(ref["W1"].astype(np.float64), fp8_decode(L["W1"]) * L["W1_scale"].reshape(N, m, 1))
+    a = run_fp8(o, L, K)
+    b = run(o, ref, K)
+    assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["ids"], b["ids"]), \
+        "FP8 layer != float32 layer on the decoded weights"
+    # arbitrary row scales, one expert: a dense FFN evaluated with numpy
+    L = fp8_layer(42, T, d, l, 1, m, pow2_scales=False)
+    w1 = fp8_decode(L["W1"])[0] * L["W1_scale"].astype(np.float64)[:, None]
+    w2 = fp8_decode(L["W2"])[0] * L["W2_scale"].astype(np.float64)[:, None]
+    x = f64(L["x"])
+    z = x @ f64(L["W_down"]).T
+    s = (np.maximum(z @ w1.T, 0.0) ** 2) @ w2.T
+    want = x + s @ f64(L["W_up"]).T
+    got = run_fp8(o, L, 1)["out"]
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-12), "FP8 dense special case differs from numpy"
+
+
 ALL_PINS = [
     pin_routing_bruteforce,
     pin_tie_break,
@@ -390,4 +450,5 @@ ALL_PINS = [
     pin_symmetries,
     pin_selection_and_forced_ids,
     pin_shared_expert,
+    pin_fp8_experts,
 ]

@@ -35,8 +35,10 @@ MUTANTS = {
     "relu_not_squared": ("h[j] = a * a;", "h[j] = a;"),
     "relu_of_square": ("double a = acc > 0.0 ? acc : 0.0;", "double a = acc;"),
     "transposed_W_down": ("widen(Wd, dt, (size_t)j * d + i)", "widen(Wd, dt, (size_t)i * l + j)"),
-    "transposed_W1": ("widen(W1, dt, (e * m + j) * l + i)", "widen(W1, dt, e * m * l + (size_t)i * m + j)"),
-    "transposed_W2": ("widen(W2, dt, (e * l + i) * m + j)", "widen(W2, dt, e * l * m + (size_t)j * l + i)"),
+    "transposed_W1": ("expert_w(D, W1, s1, (e * m + j) * l + i, e * m + j)",
+                      "expert_w(D, W1, s1, e * m * l + (size_t)i * m + j, e * m + j)"),
+    "transposed_W2": ("expert_w(D, W2, s2, (e * l + i) * m + j, e * l + i)",
+                      "expert_w(D, W2, s2, e * l * m + (size_t)j * l + i, e * l + i)"),
     "transposed_W_up": ("widen(Wu, dt, (size_t)n * l + i)", "widen(Wu, dt, (size_t)i * d + n)"),
     "router_from_latent": ("acc += widen(Wr, dt, (size_t)e * d + i) * xt[i];",
                            "acc += widen(Wr, dt, (size_t)e * d + i) * (i < l ? z[i] : 0.0);"),
@@ -60,6 +62,13 @@ MUTANTS = {
                          "acc += widen(Ws1, dt, (size_t)j * d + i) * (i < l ? z[i] : 0.0);"),
     "shared_transposed_Ws1": ("widen(Ws1, dt, (size_t)j * d + i)", "widen(Ws1, dt, (size_t)i * ms + j)"),
     "shared_transposed_Ws2": ("widen(Ws2, dt, (size_t)n * ms + j)", "widen(Ws2, dt, (size_t)j * d + n)"),
+    "fp8_exponent_bias": ("v = ldexp(1.0 + man / 8.0, ex - 7);", "v = ldexp(1.0 + man / 8.0, ex - 8);"),
+    "fp8_mantissa_width": ("v = ldexp(1.0 + man / 8.0, ex - 7);", "v = ldexp(1.0 + man / 16.0, ex - 7);"),
+    "fp8_subnormals_flushed": ("v = ldexp((double)man, -9);", "v = 0.0;"),
+    "fp8_sign_dropped": ("return sign ? -v : v;", "return v;"),
+    "fp8_scale_dropped": ("e4m3(((const uint8_t*)W)[i]) * (double)scale[row]", "e4m3(((const uint8_t*)W)[i])"),
+    "fp8_scale_wrong_row": ("e4m3(((const uint8_t*)W)[i]) * (double)scale[row]",
+                            "e4m3(((const uint8_t*)W)[i]) * (double)scale[row / 2]"),
 }
 
 
