@@ -73,12 +73,20 @@ class Hip:
         return float(ms.value)
 
 
+def expert_bytes(w, A: float) -> float:
+    """W1 and W2 of A experts, read once: elements at the layer's width, or
+    one byte each plus a float32 scale per row for FP8 experts."""
+    if w.experts == "fp8":
+        return A * (2 * w.l * w.m + 4 * (w.l + w.m))
+    return A * 2 * w.l * w.m * w.elem_bytes
+
+
 def algorithmic(w, A: float):
     """Whole-layer algorithmic bytes and flops (A = experts that got rows)."""
     B = w.elem_bytes
     lat = 0 if w.standard else 1
-    nbytes = B * (2 * w.T * w.d + lat * 2 * w.d * w.l + w.d * w.N + A * 2 * w.l * w.m + 2 * w.d * w.m_shared) \
-        + (4 * w.N if w.bias else 0)
+    nbytes = B * (2 * w.T * w.d + lat * 2 * w.d * w.l + w.d * w.N + 2 * w.d * w.m_shared) \
+        + expert_bytes(w, A) + (4 * w.N if w.bias else 0)
     flops = lat * 4 * w.T * w.d * w.l + 2 * w.T * w.d * w.N + 4 * w.T * w.K * w.l * w.m + 4 * w.T * w.d * w.m_shared
     return nbytes, flops
 
@@ -147,7 +155,8 @@ def measure(w, sets, cpu_seconds: float) -> dict:
         d = sets[i % len(sets)][1]
         B.latentmoe_forward(d["x"], d["W_down"], d["W_router"], d["W1"], d["W2"], d["W_up"], w.K, out, dims,
                             router_bias=d["bias"], workspace=ws, stream=stream, events=events,
-                            W_shared1=d.get("W_s1"), W_shared2=d.get("W_s2"))
+                            W_shared1=d.get("W_s1"), W_shared2=d.get("W_s2"),
+                            W1_scale=d.get("W1_scale"), W2_scale=d.get("W2_scale"))
 
     # active experts per weight set (for the algorithmic byte count)
     lay = B.latentmoe_workspace_layout(dims, w.K)
@@ -196,7 +205,7 @@ def measure(w, sets, cpu_seconds: float) -> dict:
 
     # dominant kernel: the expert FFN
     if path == B.LMOE_PATH_STREAM:
-        ffn_bytes = A * 2 * w.l * w.m * w.elem_bytes
+        ffn_bytes = expert_bytes(w, A)
         roof = {"kernel": "ffn_stream_kernel", "bound": "hbm", "achieved": ffn_bytes / (ffn_us * 1e-6) / 1e9,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": None}
     elif w.dtype == "f32":
@@ -206,7 +215,10 @@ def measure(w, sets, cpu_seconds: float) -> dict:
                 "unit": "TFLOP/s", "traffic": None}
     else:
         ffn_flops = 4.0 * w.T * w.K * w.l * w.m
-        roof = {"kernel": "gemm2_kernel<Ffn1>+<Ffn2>", "bound": "mfma",
+        # FP8 weights are decoded to bf16 on the way into LDS: the products
+        # run on the bf16 MFMAs, so the bf16 peak is the bound
+        q = "Q" if w.experts == "fp8" else ""
+        roof = {"kernel": f"gemm2_kernel<Ffn1{q}>+<Ffn2{q}>", "bound": "mfma",
                 "achieved": ffn_flops / (ffn_us * 1e-6) / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "traffic": None}
     roof["traffic"] = measured_traffic(w, roof["kernel"])
@@ -234,7 +246,7 @@ def measure(w, sets, cpu_seconds: float) -> dict:
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "d": w.d, "l": w.l, "N": w.N, "K": w.K, "m": w.m,
-                   "m_shared": w.m_shared, "standard": w.standard, "bias": w.bias, "weight_sets": len(sets),
+                   "m_shared": w.m_shared, "experts": w.experts, "standard": w.standard, "bias": w.bias, "weight_sets": len(sets),
                    "ffn_path": "stream" if path == B.LMOE_PATH_STREAM else "tiled",
                    "parallelism": "single GPU"},
         "roofline": roof,
@@ -294,7 +306,8 @@ def cpu_baseline(w, inp, budget_s: float):
     while True:
         sel = np.arange(n % w.T, n % w.T + chunk, dtype=np.int32) % w.T
         orc.forward(arr["x"], arr["W_down"], arr["W_router"], arr["W1"], arr["W2"], arr["W_up"], w.K,
-                    bias=arr["bias"], standard=w.standard, sel=sel, W_s1=arr.get("W_s1"), W_s2=arr.get("W_s2"))
+                    bias=arr["bias"], standard=w.standard, sel=sel, W_s1=arr.get("W_s1"), W_s2=arr.get("W_s2"),
+                    W1_scale=arr.get("W1_scale"), W2_scale=arr.get("W2_scale"))
         n += chunk
         passes += 1
         el = time.perf_counter() - t0

@@ -39,6 +39,12 @@
  *   router_bias [N] float32, topk_ids [T, K] int32, topk_gates [T, K] float32
  * One element type covers x, the weights and out: float32 or bfloat16.
  * Accumulation is float32; router logits and gates are float32 throughout.
+ * Optional FP8 expert weights (bfloat16 layers, dims.expert_format =
+ * LMOE_EXPERTS_FP8_E4M3, through latentmoe_forward_ex): W1 and W2 hold one
+ * OCP FP8 E4M3 code per element in the same layout, with float32 row scales
+ * W1_scale [N, m] (W1[e][j][:] = code * W1_scale[e][j]) and W2_scale [N, l].
+ * The pages name low-precision expert weights (NVFP4 / MXFP4) without a
+ * format; this per-row FP8 format is a reading.
  *
  * Memory: all tensor pointers are DEVICE pointers owned by the caller.  The
  * library allocates nothing in latentmoe_forward, keeps no pointer after it
@@ -80,6 +86,9 @@ typedef enum { LMOE_F32 = 0, LMOE_BF16 = 1 } lmoe_dtype;
  * same tolerance of the exact layer. */
 typedef enum { LMOE_PATH_AUTO = 0, LMOE_PATH_STREAM = 1, LMOE_PATH_TILED = 2 } lmoe_path;
 
+/* Storage of the routed experts' W1 / W2. */
+typedef enum { LMOE_EXPERTS_DENSE = 0, LMOE_EXPERTS_FP8_E4M3 = 1 } lmoe_expert_format;
+
 typedef struct {
     int32_t T;      /* tokens, >= 1 */
     int32_t d;      /* model width, multiple of 64 */
@@ -89,6 +98,7 @@ typedef struct {
     int32_t dtype;  /* lmoe_dtype */
     int32_t path;   /* lmoe_path */
     int32_t m_shared; /* shared expert width: 0 (none) or a multiple of 64 */
+    int32_t expert_format; /* lmoe_expert_format */
 } lmoe_dims;
 
 /* Bytes of device workspace latentmoe_forward needs for these dims and K
@@ -102,7 +112,8 @@ size_t latentmoe_workspace_bytes(const lmoe_dims* dims, int32_t K);
  * topk_ids / topk_gates: NULL, or caller buffers that receive the selected
  * experts in rank order (largest logit first) and their gates.
  * out must not alias x or any weight.  dims->m_shared must be 0 (the shared
- * expert goes through latentmoe_forward_shared).
+ * expert goes through latentmoe_forward_shared) and dims->expert_format
+ * LMOE_EXPERTS_DENSE (FP8 experts go through latentmoe_forward_ex).
  */
 int latentmoe_forward(const void* x, const void* W_down, const void* W_router,
                       const void* W1, const void* W2, const void* W_up, int32_t K,
@@ -144,6 +155,38 @@ int latentmoe_forward_timed(const void* x, const void* W_down, const void* W_rou
                             int32_t* topk_ids, float* topk_gates,
                             void* workspace, size_t workspace_bytes, void* stream,
                             void* const* events);
+
+/*
+ * The general entry point: every option of the layer in one argument block.
+ * Pointers as in latentmoe_forward; W_shared1 / W_shared2 with
+ * dims->m_shared > 0 (else NULL); W1_scale / W2_scale with
+ * dims->expert_format == LMOE_EXPERTS_FP8_E4M3 (else NULL; 16-byte
+ * aligned); events NULL or as in latentmoe_forward_timed.  The other
+ * forward entry points are this call with the options they do not name
+ * turned off.
+ */
+typedef struct {
+    const void* x;
+    const void* W_down;
+    const void* W_router;
+    const void* W1;
+    const void* W2;
+    const void* W_up;
+    const void* W_shared1;
+    const void* W_shared2;
+    const float* W1_scale;
+    const float* W2_scale;
+    const float* router_bias;
+    void* out;
+    int32_t* topk_ids;
+    float* topk_gates;
+    void* workspace;
+    size_t workspace_bytes;
+    void* stream;
+    void* const* events;
+} lmoe_args;
+
+int latentmoe_forward_ex(const lmoe_args* args, int32_t K, const lmoe_dims* dims);
 
 /* Static text for a status code. */
 const char* latentmoe_status_string(int status);

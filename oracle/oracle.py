@@ -32,9 +32,10 @@ class _Dims(ctypes.Structure):
 
 def build(src: str = SRC, out: str = LIB, extra: Sequence[str] = ()) -> str:
     """Compile the oracle (or a variant source) into a shared library."""
-    cmd = ["gcc", *CFLAGS, *extra, src, "-o", out + ".tmp", "-lm"]
+    tmp = f"{out}.tmp{os.getpid()}"   # one per process: parallel test workers may build at once
+    cmd = ["gcc", *CFLAGS, *extra, src, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(out + ".tmp", out)
+    os.replace(tmp, out)
     return out
 
 

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(PKG, "liblatentmoe.so")
 LMOE_OK, LMOE_EINVAL, LMOE_EUNSUPPORTED, LMOE_EWORKSPACE, LMOE_EHIP = 0, -1, -2, -3, -4
 LMOE_F32, LMOE_BF16 = 0, 1
 LMOE_PATH_AUTO, LMOE_PATH_STREAM, LMOE_PATH_TILED = 0, 1, 2
+LMOE_EXPERTS_DENSE, LMOE_EXPERTS_FP8_E4M3 = 0, 1
 LMOE_N_STAGE_EVENTS = 8
 STAGES = ("proj_router", "topk", "dispatch", "ffn1", "ffn2", "combine", "up")
 
@@ -27,6 +28,7 @@ EXPORTED = (
     "latentmoe_forward",
     "latentmoe_forward_shared",
     "latentmoe_forward_timed",
+    "latentmoe_forward_ex",
     "latentmoe_status_string",
     "latentmoe_last_error",
     "latentmoe_resolved_path",
@@ -35,7 +37,15 @@ EXPORTED = (
 
 
 class lmoe_dims(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_int32) for n in ("T", "d", "l", "N", "m", "dtype", "path", "m_shared")]
+    _fields_ = [(n, ctypes.c_int32)
+                for n in ("T", "d", "l", "N", "m", "dtype", "path", "m_shared", "expert_format")]
+
+
+class lmoe_args(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "x", "W_down", "W_router", "W1", "W2", "W_up", "W_shared1", "W_shared2", "W1_scale", "W2_scale",
+        "router_bias", "out", "topk_ids", "topk_gates", "workspace")] + [
+        ("workspace_bytes", ctypes.c_size_t), ("stream", ctypes.c_void_p), ("events", ctypes.c_void_p)]
 
 
 class lmoe_ws_layout(ctypes.Structure):
@@ -70,6 +80,8 @@ def lib():
         L.latentmoe_forward_timed.restype = ctypes.c_int
         L.latentmoe_forward_timed.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_int32, P,
                                               ctypes.POINTER(lmoe_dims), P, P, P, P, ctypes.c_size_t, P, P]
+        L.latentmoe_forward_ex.restype = ctypes.c_int
+        L.latentmoe_forward_ex.argtypes = [ctypes.POINTER(lmoe_args), ctypes.c_int32, ctypes.POINTER(lmoe_dims)]
         L.latentmoe_status_string.restype = ctypes.c_char_p
         L.latentmoe_status_string.argtypes = [ctypes.c_int]
         L.latentmoe_last_error.restype = ctypes.c_char_p
@@ -83,12 +95,13 @@ def lib():
     return _lib
 
 
-def make_dims(T, d, l, N, m, dtype, path=LMOE_PATH_AUTO, m_shared=0) -> lmoe_dims:
+def make_dims(T, d, l, N, m, dtype, path=LMOE_PATH_AUTO, m_shared=0,
+              expert_format=LMOE_EXPERTS_DENSE) -> lmoe_dims:
     if isinstance(dtype, torch.dtype):
         dtype = LMOE_F32 if dtype == torch.float32 else LMOE_BF16
     elif isinstance(dtype, str):
         dtype = LMOE_F32 if dtype == "f32" else LMOE_BF16
-    return lmoe_dims(T, d, l, N, m, dtype, path, m_shared)
+    return lmoe_dims(T, d, l, N, m, dtype, path, m_shared, expert_format)
 
 
 def latentmoe_workspace_bytes(dims: lmoe_dims, K: int) -> int:
@@ -130,14 +143,15 @@ def _check(rc: int) -> None:
 def latentmoe_forward(x, W_down, W_router, W1, W2, W_up, K: int, out, dims: lmoe_dims,
                       router_bias=None, topk_ids=None, topk_gates=None, workspace=None,
                       workspace_bytes: Optional[int] = None, stream=None, check: bool = True,
-                      events=None, W_shared1=None, W_shared2=None) -> int:
+                      events=None, W_shared1=None, W_shared2=None, W1_scale=None, W2_scale=None) -> int:
     """Call the C entry point with raw device pointers taken from tensors.
 
     `stream`: a torch.cuda.Stream, a raw hipStream_t int, or None for torch's
     current stream.  `events`: None, or a ctypes array of
     LMOE_N_STAGE_EVENTS hipEvent_t handles (calls latentmoe_forward_timed).
     W_shared1 / W_shared2 (with dims.m_shared > 0): calls
-    latentmoe_forward_shared.  Returns the status (raises on failure when
+    latentmoe_forward_shared.  W1_scale / W2_scale (FP8 experts) or
+    dims.expert_format != LMOE_EXPERTS_DENSE: calls latentmoe_forward_ex.  Returns the status (raises on failure when
     check=True).
     """
     if stream is None:
@@ -148,6 +162,15 @@ def latentmoe_forward(x, W_down, W_router, W1, W2, W_up, K: int, out, dims: lmoe
         stream_ptr = stream.cuda_stream
     if workspace_bytes is None:
         workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if W1_scale is not None or W2_scale is not None or dims.expert_format != LMOE_EXPERTS_DENSE:
+        args = lmoe_args(_ptr(x), _ptr(W_down), _ptr(W_router), _ptr(W1), _ptr(W2), _ptr(W_up),
+                         _ptr(W_shared1), _ptr(W_shared2), _ptr(W1_scale), _ptr(W2_scale), _ptr(router_bias),
+                         _ptr(out), _ptr(topk_ids), _ptr(topk_gates), _ptr(workspace), workspace_bytes,
+                         stream_ptr, None if events is None else ctypes.cast(events, ctypes.c_void_p).value)
+        rc = lib().latentmoe_forward_ex(ctypes.byref(args), int(K), ctypes.byref(dims))
+        if check:
+            _check(rc)
+        return rc
     head = (_ptr(x), _ptr(W_down), _ptr(W_router), _ptr(W1), _ptr(W2), _ptr(W_up))
     shared = (_ptr(W_shared1), _ptr(W_shared2))
     tail = (int(K), _ptr(out), ctypes.byref(dims), _ptr(router_bias), _ptr(topk_ids), _ptr(topk_gates),
@@ -168,7 +191,8 @@ def dims_for(inputs: dict, K: int, path: int = LMOE_PATH_AUTO) -> lmoe_dims:
     T, d = x.shape
     N, m, l = W1.shape
     ws1 = inputs.get("W_s1")
-    return make_dims(T, d, l, N, m, x.dtype, path, 0 if ws1 is None else ws1.shape[0])
+    fmt = LMOE_EXPERTS_DENSE if inputs.get("W1_scale") is None else LMOE_EXPERTS_FP8_E4M3
+    return make_dims(T, d, l, N, m, x.dtype, path, 0 if ws1 is None else ws1.shape[0], fmt)
 
 
 def alloc_workspace(dims: lmoe_dims, K: int, device) -> torch.Tensor:
@@ -198,7 +222,8 @@ def forward(inputs: dict, K: int, *, path: int = LMOE_PATH_AUTO, workspace: Opti
     latentmoe_forward(x, inputs.get("W_down"), inputs["W_router"], inputs["W1"], inputs["W2"],
                       inputs.get("W_up"), K, out, dims, router_bias=inputs.get("bias"),
                       topk_ids=ids, topk_gates=gates, workspace=workspace, stream=stream,
-                      W_shared1=inputs.get("W_s1"), W_shared2=inputs.get("W_s2"))
+                      W_shared1=inputs.get("W_s1"), W_shared2=inputs.get("W_s2"),
+                      W1_scale=inputs.get("W1_scale"), W2_scale=inputs.get("W2_scale"))
     if routing:
         return out, ids, gates, workspace
     return out

@@ -35,6 +35,25 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 }
 
 __device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ uint2 ldg8(const void* p) { return *reinterpret_cast<const uint2*>(p); }
+
+// 8 OCP FP8 E4M3 codes (bytes 0..7 of v) -> the 8 equal bfloat16 values
+// (every E4M3 value is exact in bfloat16), with gfx950's
+// v_cvt_scalef32_pk_bf16_fp8 at scale 1.  Device code only.
+__device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint2 v) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, false);
+    const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, true);
+    const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, false);
+    const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, true);
+    return uint4{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                 __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
+#else
+    (void)v;
+    return uint4{0u, 0u, 0u, 0u};
+#endif
+}
 
 constexpr uint4 kZero16 = {0u, 0u, 0u, 0u};
 

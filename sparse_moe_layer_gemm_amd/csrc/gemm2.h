@@ -30,6 +30,8 @@
 // the tiles of one expert (its rows x all column tiles) share one XCD's L2.
 #pragma once
 
+#include <type_traits>
+
 #include "layer.h"
 
 namespace lmoe {
@@ -85,7 +87,7 @@ struct RowCtx<ProjRouter<bf16>> {
     static constexpr bool kRowVal = false;
     __device__ static float row_value(const LayerArgs&, int, int) { return 0.0f; }
     using ColPre = f32x4;
-    __device__ static f32x4 col_load(const LayerArgs& a, int c0) {
+    __device__ static f32x4 col_load(const LayerArgs& a, int, int c0) {
         f32x4 b = {0.0f, 0.0f, 0.0f, 0.0f};
         const int e0 = c0 - (a.standard ? 0 : a.l);
         if (a.bias && e0 >= 0)
@@ -112,7 +114,7 @@ struct RowCtx<Ffn1<bf16>> {
     static constexpr bool kRowVal = false;
     __device__ static float row_value(const LayerArgs&, int, int) { return 0.0f; }
     using ColPre = NoPre;
-    __device__ static NoPre col_load(const LayerArgs&, int) { return NoPre{}; }
+    __device__ static NoPre col_load(const LayerArgs&, int, int) { return NoPre{}; }
     using Pre = NoPre;
     __device__ static NoPre load(const LayerArgs&, int, int, int) { return NoPre{}; }
     __device__ static void store(const LayerArgs& a, int, int slot, int c0, f32x4 v, const NoPre&, const NoPre&,
@@ -130,7 +132,7 @@ struct RowCtx<Ffn2<bf16, bf16>> {
     static constexpr bool kRowVal = true;   // the slot's gate
     __device__ static float row_value(const LayerArgs& a, int, int slot) { return a.gates[a.perm[slot]]; }
     using ColPre = NoPre;
-    __device__ static NoPre col_load(const LayerArgs&, int) { return NoPre{}; }
+    __device__ static NoPre col_load(const LayerArgs&, int, int) { return NoPre{}; }
     using Pre = NoPre;
     __device__ static NoPre load(const LayerArgs&, int, int, int) { return NoPre{}; }
     __device__ static void store(const LayerArgs& a, int, int slot, int c0, f32x4 v, const NoPre&, const NoPre&,
@@ -144,7 +146,7 @@ struct RowCtx<Up<bf16>> {
     static constexpr bool kRowVal = false;
     __device__ static float row_value(const LayerArgs&, int, int) { return 0.0f; }
     using ColPre = NoPre;
-    __device__ static NoPre col_load(const LayerArgs&, int) { return NoPre{}; }
+    __device__ static NoPre col_load(const LayerArgs&, int, int) { return NoPre{}; }
     using Pre = uint2;   // 4 bf16 of the residual row (d is a multiple of 64, so never ragged)
     __device__ static uint2 load(const LayerArgs& a, int, int r, int c0) {
         return *reinterpret_cast<const uint2*>(static_cast<const bf16*>(a.x) + (size_t)r * a.d + c0);
@@ -159,12 +161,54 @@ struct RowCtx<Up<bf16>> {
     }
 };
 
+// FP8 experts: the four columns' row scales (columns of the product are
+// rows of the weight matrix), applied before the problem's own epilogue.
+template <class Q>
+struct QScales {
+    __device__ static f32x4 load(const LayerArgs& a, int e, int c0, int ncols) {
+        f32x4 s = {1.0f, 1.0f, 1.0f, 1.0f};
+        for (int i = 0; i < 4; ++i)
+            if (c0 + i < ncols) s[i] = Q::row_scale(a, e, c0 + i);
+        return s;
+    }
+};
+
+template <>
+struct RowCtx<Ffn1Q> {
+    static constexpr bool kRowVal = false;
+    __device__ static float row_value(const LayerArgs&, int, int) { return 0.0f; }
+    using ColPre = f32x4;
+    __device__ static f32x4 col_load(const LayerArgs& a, int e, int c0) { return QScales<Ffn1Q>::load(a, e, c0, a.m); }
+    using Pre = NoPre;
+    __device__ static NoPre load(const LayerArgs&, int, int, int) { return NoPre{}; }
+    __device__ static void store(const LayerArgs& a, int g, int slot, int c0, f32x4 v, const NoPre& p,
+                                 const f32x4& sc, float rv) {
+        RowCtx<Ffn1<bf16>>::store(a, g, slot, c0, v * sc, p, NoPre{}, rv);
+    }
+};
+
+template <>
+struct RowCtx<Ffn2Q> {
+    static constexpr bool kRowVal = true;   // the slot's gate
+    __device__ static float row_value(const LayerArgs& a, int e, int slot) {
+        return RowCtx<Ffn2<bf16, bf16>>::row_value(a, e, slot);
+    }
+    using ColPre = f32x4;
+    __device__ static f32x4 col_load(const LayerArgs& a, int e, int c0) { return QScales<Ffn2Q>::load(a, e, c0, a.l); }
+    using Pre = NoPre;
+    __device__ static NoPre load(const LayerArgs&, int, int, int) { return NoPre{}; }
+    __device__ static void store(const LayerArgs& a, int g, int slot, int c0, f32x4 v, const NoPre& p,
+                                 const f32x4& sc, float gate) {
+        RowCtx<Ffn2<bf16, bf16>>::store(a, g, slot, c0, v * sc, p, NoPre{}, gate);
+    }
+};
+
 template <>
 struct RowCtx<Shared1<bf16>> {
     static constexpr bool kRowVal = false;
     __device__ static float row_value(const LayerArgs&, int, int) { return 0.0f; }
     using ColPre = NoPre;
-    __device__ static NoPre col_load(const LayerArgs&, int) { return NoPre{}; }
+    __device__ static NoPre col_load(const LayerArgs&, int, int) { return NoPre{}; }
     using Pre = NoPre;
     __device__ static NoPre load(const LayerArgs&, int, int, int) { return NoPre{}; }
     __device__ static void store(const LayerArgs& a, int, int r, int c0, f32x4 v, const NoPre&, const NoPre&,
@@ -182,7 +226,7 @@ struct RowCtx<Shared2<bf16>> {
     static constexpr bool kRowVal = false;
     __device__ static float row_value(const LayerArgs&, int, int) { return 0.0f; }
     using ColPre = NoPre;
-    __device__ static NoPre col_load(const LayerArgs&, int) { return NoPre{}; }
+    __device__ static NoPre col_load(const LayerArgs&, int, int) { return NoPre{}; }
     using Pre = NoPre;
     __device__ static NoPre load(const LayerArgs&, int, int, int) { return NoPre{}; }
     __device__ static void store(const LayerArgs& a, int, int r, int c0, f32x4 v, const NoPre&, const NoPre&,
@@ -203,7 +247,7 @@ struct RowCtx<UpShared<bf16>> {
     static constexpr bool kRowVal = false;
     __device__ static float row_value(const LayerArgs&, int, int) { return 0.0f; }
     using ColPre = NoPre;
-    __device__ static NoPre col_load(const LayerArgs&, int) { return NoPre{}; }
+    __device__ static NoPre col_load(const LayerArgs&, int, int) { return NoPre{}; }
     using Pre = UpSharedPre;
     __device__ static UpSharedPre load(const LayerArgs& a, int, int r, int c0) {
         const size_t i = (size_t)r * a.d + c0;
@@ -269,8 +313,13 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm2_kernel(LayerArgs a, int 
     Tile ct;  // the tile the MFMAs work on
     if (!tile_at(lslot, ct)) return;
     int cslot = lslot;
+    // B rows: bf16, or FP8 E4M3 codes (one byte each) decoded to bf16 when
+    // they are written to LDS, so the LDS layout and the MFMAs are the same
+    using BE = typename P::BElem;
+    constexpr bool kQ = sizeof(BE) == 1;
+    using BStage = typename std::conditional<kQ, uint2, uint4>::type;
     const bf16* ap[S::LA];
-    const bf16* bp[S::LB];
+    const BE* bp[S::LB];
     auto set_rows = [&](const Tile& t) {
 #pragma unroll
         for (int i = 0; i < S::LA; ++i) {
@@ -298,7 +347,8 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm2_kernel(LayerArgs a, int 
         }
     };
 
-    uint4 ra[S::LA], rb[S::LB];
+    uint4 ra[S::LA];
+    BStage rb[S::LB];
     // Staged loads are split in 4 parts (load index i belongs to part i % 4),
     // so that part q of the next k-step can go to LDS, and part q of the
     // k-step after it can be loaded, right after MFMA group q.
@@ -310,7 +360,12 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm2_kernel(LayerArgs a, int 
             if (in_part(i, S::LA, 2 * g) || in_part(i, S::LA, 2 * g + 1)) ra[i] = ldg16(ap[i] + k0);
 #pragma unroll
         for (int i = 0; i < S::LB; ++i)
-            if (in_part(i, S::LB, 2 * g) || in_part(i, S::LB, 2 * g + 1)) rb[i] = ldg16(bp[i] + k0);
+            if (in_part(i, S::LB, 2 * g) || in_part(i, S::LB, 2 * g + 1)) {
+                if constexpr (kQ)
+                    rb[i] = ldg8(bp[i] + k0);
+                else
+                    rb[i] = ldg16(bp[i] + k0);
+            }
     };
     auto swrite_part = [&](int st, int q) {
         uint4* as = As(st);
@@ -325,7 +380,10 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm2_kernel(LayerArgs a, int 
         for (int i = 0; i < S::LB; ++i)
             if (in_part(i, S::LB, q)) {
                 const int r = lrow + S::RSTEP * i;
-                bs[r * 8 + (ch ^ g2_swz(r))] = rb[i];
+                if constexpr (kQ)
+                    bs[r * 8 + (ch ^ g2_swz(r))] = e4m3x8_to_bf16x8(rb[i]);
+                else
+                    bs[r * 8 + (ch ^ g2_swz(r))] = rb[i];
             }
     };
 
@@ -397,7 +455,7 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm2_kernel(LayerArgs a, int 
             if (tid < BM && ct.row0 + tid < ct.row_end) rv = RowCtx<P>::row_value(a, ct.grp, ct.row0 + tid);
         }
         const int c = ct.col0 + 4 * (tid % kUpr);
-        if (c < ncols) colpre = RowCtx<P>::col_load(a, c);
+        if (c < ncols) colpre = RowCtx<P>::col_load(a, ct.grp, c);
     };
     tile_loads();
     static_assert(kEpiRows % 32 == 0 && BM % kEpiRows == 0 && kUpr >= 16, "epilogue tiling");

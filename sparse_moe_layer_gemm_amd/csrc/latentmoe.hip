@@ -85,6 +85,7 @@ struct Plan {
     bool skinny = false;          // projections on the skinny kernel
     int tile_rows = G2Small::BM;
     bool ffn_large = false;       // tiled FFN on G2Large
+    bool fp8 = false;             // FP8 E4M3 expert weights
     int nblk = 1;                 // dispatch blocks
     int ms = 128;                 // streaming FFN m-slice
     int nsplit = 1;               // streaming FFN partial planes
@@ -127,6 +128,15 @@ Plan make_plan(const lmoe_dims* dm, int32_t K) {
         p.status = fail(LMOE_EINVAL, "dtype=%d is not LMOE_F32 or LMOE_BF16", d.dtype);
         return p;
     }
+    if (d.expert_format != LMOE_EXPERTS_DENSE && d.expert_format != LMOE_EXPERTS_FP8_E4M3) {
+        p.status = fail(LMOE_EINVAL, "expert_format=%d is not a lmoe_expert_format", d.expert_format);
+        return p;
+    }
+    if (d.expert_format == LMOE_EXPERTS_FP8_E4M3 && d.dtype != LMOE_BF16) {
+        p.status = fail(LMOE_EUNSUPPORTED, "FP8 experts need a bfloat16 layer");
+        return p;
+    }
+    p.fp8 = d.expert_format == LMOE_EXPERTS_FP8_E4M3;
     if (d.m_shared < 0 || d.m_shared % 64 != 0) {
         p.status = fail(LMOE_EINVAL, "m_shared=%d must be 0 or a positive multiple of 64", d.m_shared);
         return p;
@@ -324,21 +334,31 @@ void launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* events
     if constexpr (sizeof(E) == 2) {
         if (p.path == LMOE_PATH_STREAM) {
             const dim3 g(p.nsplit, a.N);
-            if (p.ms == 128)
-                ffn_stream_kernel<128><<<g, b256, 0, st>>>(a);
+            if (p.fp8)
+                p.ms == 128 ? ffn_stream_kernel<128, true><<<g, b256, 0, st>>>(a)
+                            : ffn_stream_kernel<64, true><<<g, b256, 0, st>>>(a);
             else
-                ffn_stream_kernel<64><<<g, b256, 0, st>>>(a);
+                p.ms == 128 ? ffn_stream_kernel<128, false><<<g, b256, 0, st>>>(a)
+                            : ffn_stream_kernel<64, false><<<g, b256, 0, st>>>(a);
             mark(4);
         } else {
-            if (p.ffn_large) {
-                launch_g2<Ffn1<bf16>, G2Large>(a, (int)mt, cdiv(a.m, G2Large::BN), st);
-                mark(4);
-                launch_g2<Ffn2<bf16, YT>, G2Large>(a, (int)mt, cdiv(a.l, G2Large::BN), st);
-            } else {
-                launch_g2<Ffn1<bf16>, G2Small>(a, (int)mt, cdiv(a.m, G2Small::BN), st);
-                mark(4);
-                launch_g2<Ffn2<bf16, YT>, G2Small>(a, (int)mt, cdiv(a.l, G2Small::BN), st);
-            }
+            auto ffn = [&](auto f1, auto f2) {
+                using F1 = decltype(f1);
+                using F2 = decltype(f2);
+                if (p.ffn_large) {
+                    launch_g2<F1, G2Large>(a, (int)mt, cdiv(a.m, G2Large::BN), st);
+                    mark(4);
+                    launch_g2<F2, G2Large>(a, (int)mt, cdiv(a.l, G2Large::BN), st);
+                } else {
+                    launch_g2<F1, G2Small>(a, (int)mt, cdiv(a.m, G2Small::BN), st);
+                    mark(4);
+                    launch_g2<F2, G2Small>(a, (int)mt, cdiv(a.l, G2Small::BN), st);
+                }
+            };
+            if (p.fp8)
+                ffn(Ffn1Q{}, Ffn2Q{});
+            else
+                ffn(Ffn1<bf16>{}, Ffn2<bf16, YT>{});
         }
     } else {
         gemm_simt_kernel<Ffn1<float>><<<dim3(mt, cdiv(a.m, kSimtN)), b256, 0, st>>>(a);
@@ -410,9 +430,10 @@ int latentmoe_workspace_layout(const lmoe_dims* dims, int32_t K, lmoe_ws_layout*
 }
 
 static int forward_impl(const void* x, const void* W_down, const void* W_router, const void* W1, const void* W2,
-                        const void* W_up, const void* W_s1, const void* W_s2, int32_t K, void* out,
-                        const lmoe_dims* dims, const float* router_bias, int32_t* topk_ids, float* topk_gates,
-                        void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
+                        const void* W_up, const void* W_s1, const void* W_s2, const float* w1s, const float* w2s,
+                        int32_t K, void* out, const lmoe_dims* dims, const float* router_bias,
+                        int32_t* topk_ids, float* topk_gates, void* workspace, size_t workspace_bytes,
+                        void* stream, void* const* events) {
     g_last_error.clear();
     const Plan p = make_plan(dims, K);
     if (p.status != LMOE_OK) return p.status;
@@ -426,6 +447,11 @@ static int forward_impl(const void* x, const void* W_down, const void* W_router,
         return fail(LMOE_EINVAL, "W_shared1 and W_shared2 must be both set when m_shared > 0 and both NULL when "
                                  "m_shared == 0 (m_shared=%d)", d.m_shared);
     if (standard && d.l != d.d) return fail(LMOE_EINVAL, "standard mode (no projections) needs l == d");
+    if (p.fp8 != (w1s != nullptr) || (w1s == nullptr) != (w2s == nullptr))
+        return fail(LMOE_EINVAL, "W1_scale and W2_scale must be both set for FP8 experts and both NULL otherwise");
+    if ((w1s && (reinterpret_cast<uintptr_t>(w1s) & 15) != 0) ||
+        (w2s && (reinterpret_cast<uintptr_t>(w2s) & 15) != 0))
+        return fail(LMOE_EINVAL, "W1_scale and W2_scale must be 16-byte aligned");
     if (!workspace) return fail(LMOE_EWORKSPACE, "workspace is NULL");
     if (workspace_bytes < p.total)
         return fail(LMOE_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, p.total);
@@ -452,6 +478,8 @@ static int forward_impl(const void* x, const void* W_down, const void* W_router,
     a.W_s2 = W_s2;
     a.m_s = d.m_shared;
     a.bias = router_bias;
+    a.w1s = w1s;
+    a.w2s = w2s;
     a.out = out;
     a.T = d.T;
     a.d = d.d;
@@ -501,8 +529,10 @@ int latentmoe_forward(const void* x, const void* W_down, const void* W_router, c
     if (dims && dims->m_shared != 0)
         return fail(LMOE_EINVAL, "m_shared=%d: a shared expert goes through latentmoe_forward_shared",
                     dims->m_shared);
-    return forward_impl(x, W_down, W_router, W1, W2, W_up, nullptr, nullptr, K, out, dims, router_bias, topk_ids,
-                        topk_gates, workspace, workspace_bytes, stream, nullptr);
+    if (dims && dims->expert_format != LMOE_EXPERTS_DENSE)
+        return fail(LMOE_EINVAL, "FP8 experts go through latentmoe_forward_ex");
+    return forward_impl(x, W_down, W_router, W1, W2, W_up, nullptr, nullptr, nullptr, nullptr, K, out, dims,
+                        router_bias, topk_ids, topk_gates, workspace, workspace_bytes, stream, nullptr);
 }
 
 int latentmoe_forward_shared(const void* x, const void* W_down, const void* W_router, const void* W1,
@@ -512,8 +542,10 @@ int latentmoe_forward_shared(const void* x, const void* W_down, const void* W_ro
                              void* stream) {
     if (dims && dims->m_shared <= 0)
         return fail(LMOE_EINVAL, "latentmoe_forward_shared needs m_shared > 0 (got %d)", dims->m_shared);
-    return forward_impl(x, W_down, W_router, W1, W2, W_up, W_shared1, W_shared2, K, out, dims, router_bias,
-                        topk_ids, topk_gates, workspace, workspace_bytes, stream, nullptr);
+    if (dims && dims->expert_format != LMOE_EXPERTS_DENSE)
+        return fail(LMOE_EINVAL, "FP8 experts go through latentmoe_forward_ex");
+    return forward_impl(x, W_down, W_router, W1, W2, W_up, W_shared1, W_shared2, nullptr, nullptr, K, out, dims,
+                        router_bias, topk_ids, topk_gates, workspace, workspace_bytes, stream, nullptr);
 }
 
 int latentmoe_forward_timed(const void* x, const void* W_down, const void* W_router, const void* W1,
@@ -522,8 +554,17 @@ int latentmoe_forward_timed(const void* x, const void* W_down, const void* W_rou
                             int32_t* topk_ids, float* topk_gates, void* workspace, size_t workspace_bytes,
                             void* stream, void* const* events) {
     if (!events) return fail(LMOE_EINVAL, "events is NULL");
-    return forward_impl(x, W_down, W_router, W1, W2, W_up, W_shared1, W_shared2, K, out, dims, router_bias,
-                        topk_ids, topk_gates, workspace, workspace_bytes, stream, events);
+    if (dims && dims->expert_format != LMOE_EXPERTS_DENSE)
+        return fail(LMOE_EINVAL, "FP8 experts go through latentmoe_forward_ex");
+    return forward_impl(x, W_down, W_router, W1, W2, W_up, W_shared1, W_shared2, nullptr, nullptr, K, out, dims,
+                        router_bias, topk_ids, topk_gates, workspace, workspace_bytes, stream, events);
+}
+
+int latentmoe_forward_ex(const lmoe_args* g, int32_t K, const lmoe_dims* dims) {
+    if (!g) return fail(LMOE_EINVAL, "args is NULL");
+    return forward_impl(g->x, g->W_down, g->W_router, g->W1, g->W2, g->W_up, g->W_shared1, g->W_shared2,
+                        g->W1_scale, g->W2_scale, K, g->out, dims, g->router_bias, g->topk_ids, g->topk_gates,
+                        g->workspace, g->workspace_bytes, g->stream, g->events);
 }
 
 const char* latentmoe_status_string(int status) {

@@ -21,6 +21,8 @@ struct LayerArgs {
     const void* W_s1;      // [m_s, d] shared expert, or NULL
     const void* W_s2;      // [d, m_s]
     const float* bias;     // [N] or NULL
+    const float* w1s;      // [N, m] row scales of FP8 W1 (FP8 experts only)
+    const float* w2s;      // [N, l] row scales of FP8 W2
     void* out;             // [T, d]
     int T, d, l, N, m, K;
     int standard;
@@ -56,6 +58,7 @@ struct LayerArgs {
 
 template <class E>
 struct ProjRouter {
+    using BElem = E;   // element type of the B (weight) rows
     __device__ static bool tile(const LayerArgs& a, int bx, int bm, int& grp, int& row0, int& row_end) {
         grp = 0;
         row0 = bx * bm;
@@ -89,6 +92,7 @@ struct ProjRouter {
 // relu(h)^2.  Row r of a tile is slot r; its token is perm[r] / K.
 template <class E>
 struct Ffn1 {
+    using BElem = E;   // element type of the B (weight) rows
     __device__ static bool tile(const LayerArgs& a, int bx, int, int& grp, int& row0, int& row_end) {
         if (bx >= *a.n_tiles) return false;
         const int2 t = a.tiles[bx];
@@ -118,6 +122,7 @@ struct Ffn1 {
 // (so the combine only sums).  YT: storage type of the expert outputs.
 template <class E, class YT>
 struct Ffn2 {
+    using BElem = E;
     __device__ static bool tile(const LayerArgs& a, int bx, int bm, int& grp, int& row0, int& row_end) {
         return Ffn1<E>::tile(a, bx, bm, grp, row0, row_end);
     }
@@ -139,6 +144,7 @@ struct Ffn2 {
 // out = x + W_up s.
 template <class E>
 struct Up {
+    using BElem = E;   // element type of the B (weight) rows
     __device__ static bool tile(const LayerArgs& a, int bx, int bm, int& grp, int& row0, int& row_end) {
         grp = 0;
         row0 = bx * bm;
@@ -163,6 +169,7 @@ struct Up {
 // Shared expert, first product: a_s = relu(W_s1 x)^2 over all tokens.
 template <class E>
 struct Shared1 {
+    using BElem = E;   // element type of the B (weight) rows
     __device__ static bool tile(const LayerArgs& a, int bx, int bm, int& grp, int& row0, int& row_end) {
         return Up<E>::tile(a, bx, bm, grp, row0, row_end);
     }
@@ -185,6 +192,7 @@ struct Shared1 {
 // layer's output is still rounded once (in the up-projection or combine).
 template <class E>
 struct Shared2 {
+    using BElem = E;   // element type of the B (weight) rows
     __device__ static bool tile(const LayerArgs& a, int bx, int bm, int& grp, int& row0, int& row_end) {
         return Up<E>::tile(a, bx, bm, grp, row0, row_end);
     }
@@ -207,6 +215,25 @@ struct UpShared : Up<E> {
         const size_t i = (size_t)r * a.d + c;
         static_cast<E*>(a.out)[i] = from_f32<E>(to_f32(static_cast<const E*>(a.x)[i]) + a.y_s[i] + v);
     }
+};
+
+// The expert FFN with FP8 (E4M3) weights: the same products on bf16
+// activations, the weight rows being one byte per element with one float32
+// scale per row (applied to the row's fp32 dot product in the epilogue).
+struct Ffn1Q : Ffn1<bf16> {
+    using BElem = uint8_t;
+    __device__ static const uint8_t* b_row(const LayerArgs& a, int e, int c) {
+        return static_cast<const uint8_t*>(a.W1) + ((size_t)e * a.m + c) * a.l;
+    }
+    __device__ static float row_scale(const LayerArgs& a, int e, int c) { return a.w1s[(size_t)e * a.m + c]; }
+};
+
+struct Ffn2Q : Ffn2<bf16, bf16> {
+    using BElem = uint8_t;
+    __device__ static const uint8_t* b_row(const LayerArgs& a, int e, int c) {
+        return static_cast<const uint8_t*>(a.W2) + ((size_t)e * a.l + c) * a.m;
+    }
+    __device__ static float row_scale(const LayerArgs& a, int e, int c) { return a.w2s[(size_t)e * a.l + c]; }
 };
 
 }  // namespace lmoe

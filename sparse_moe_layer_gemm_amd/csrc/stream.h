@@ -21,6 +21,8 @@
 //     the slices in a fixed order.
 #pragma once
 
+#include <type_traits>
+
 #include "layer.h"
 
 namespace lmoe {
@@ -147,8 +149,42 @@ __global__ __launch_bounds__(256) void skinny_part_kernel(LayerArgs a, float* pa
     }
 }
 
-template <int MS>
+// The expert weights in 64-wide k blocks: lane group g = lane / 16 takes k =
+// 16g .. 16g+15 of a block, its first 8 terms going to one MFMA and the next
+// 8 to a second (the same grouping of the dot product for both weight
+// formats).  bf16: two 16-byte loads per lane; FP8 E4M3 (Q): one 16-byte load
+// of 16 codes, decoded to bf16 in registers.
+template <bool Q>
+struct W64 {
+    using WT = typename std::conditional<Q, uint8_t, bf16>::type;   // stored weight element
+    uint4 v[Q ? 1 : 2];
+    __device__ __forceinline__ static W64 load(const WT* p) {
+        W64 w;
+        w.v[0] = ldg16(p);
+        if constexpr (!Q) w.v[1] = ldg16(p + 8);
+        return w;
+    }
+    __device__ __forceinline__ static W64 zero() {
+        W64 w;
+#pragma unroll
+        for (int i = 0; i < (Q ? 1 : 2); ++i) w.v[i] = kZero16;
+        return w;
+    }
+    // the 8 terms of half h (0 or 1) as an MFMA fragment
+    __device__ __forceinline__ bf16x8 frag(int h) const {
+        if constexpr (Q)
+            return as_bf16x8(e4m3x8_to_bf16x8(h ? uint2{v[0].z, v[0].w} : uint2{v[0].x, v[0].y}));
+        else
+            return as_bf16x8(v[h]);
+    }
+};
+
+// Q: FP8 E4M3 expert weights (one float32 scale per weight row, applied to
+// that row's fp32 result).
+template <int MS, bool Q>
 __global__ __launch_bounds__(256) void ffn_stream_kernel(LayerArgs a) {
+    using WB = W64<Q>;
+    using WT = typename WB::WT;
     const int ai = blockIdx.y;
     if (ai >= *a.n_active) return;
     const int e = a.active[ai];
@@ -156,41 +192,53 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(LayerArgs a) {
     const int r_begin = a.offsets[e], r_end = a.offsets[e + 1];
     const int l = a.l, m = a.m;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int lr = lane & 15, koff = 8 * (lane >> 4);
-    const bf16* W1e = static_cast<const bf16*>(a.W1) + (size_t)e * m * l;
-    const bf16* W2e = static_cast<const bf16*>(a.W2) + (size_t)e * l * m;
+    const int lr = lane & 15, k16 = 16 * (lane >> 4);
+    const WT* W1e = static_cast<const WT*>(a.W1) + (size_t)e * m * l;
+    const WT* W2e = static_cast<const WT*>(a.W2) + (size_t)e * l * m;
     const bf16* Z = static_cast<const bf16*>(a.z);
     float* Yp = static_cast<float*>(a.ybuf) + (size_t)blockIdx.x * a.T * a.K * l;
 
     constexpr int NB = MS / 16;        // 16-column blocks of the slice
     constexpr int NBW = NB / 4;        // per wave
     constexpr int AST = MS + 8;        // LDS row stride (bf16), padded
+    constexpr int NKB = 2;             // 64-wide k blocks per batch of phase-1 loads
     __shared__ bf16 As[16 * AST];
 
     for (int rc = r_begin; rc < r_end; rc += 16) {
         const int nr = min(16, r_end - rc);
         // ---- phase 1: H[16 x MS] = Z[rows] . W1[e][j0 : j0+MS]^T, reduce over l
         const int my_slot = rc + min(lr, nr - 1);
-        const bf16* zp = Z + (size_t)(a.perm[my_slot] / a.K) * l + koff;
-        const bf16* bp[NBW];
+        const bf16* zp = Z + (size_t)(a.perm[my_slot] / a.K) * l + k16;
+        const WT* bp[NBW];
 #pragma unroll
-        for (int b = 0; b < NBW; ++b) bp[b] = W1e + (size_t)(j0 + (wave + 4 * b) * 16 + lr) * l + koff;
+        for (int b = 0; b < NBW; ++b) bp[b] = W1e + (size_t)(j0 + (wave + 4 * b) * 16 + lr) * l + k16;
         f32x4 acc[NBW];
 #pragma unroll
         for (int b = 0; b < NBW; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int k0 = 0; k0 < l; k0 += 32 * 4) {
-            uint4 zv[4], wv[4][NBW];
+        for (int k0 = 0; k0 < l; k0 += 64 * NKB) {
+            uint4 zv[NKB][2];
+            WB wv[NKB][NBW];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const bool ok = k0 + 32 * u < l;
-                zv[u] = ok ? ldg16(zp + k0 + 32 * u) : kZero16;
+            for (int p = 0; p < NKB; ++p) {
+                const int kb = k0 + 64 * p;
+                const bool ok = kb < l;   // l is a multiple of 64
+                zv[p][0] = ok ? ldg16(zp + kb) : kZero16;
+                zv[p][1] = ok ? ldg16(zp + kb + 8) : kZero16;
 #pragma unroll
-                for (int b = 0; b < NBW; ++b) wv[u][b] = ok ? ldg16(bp[b] + k0 + 32 * u) : kZero16;
+                for (int b = 0; b < NBW; ++b) wv[p][b] = ok ? WB::load(bp[b] + kb) : WB::zero();
             }
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
+            for (int p = 0; p < NKB; ++p)
 #pragma unroll
-                for (int b = 0; b < NBW; ++b) acc[b] = mfma16(as_bf16x8(zv[u]), as_bf16x8(wv[u][b]), acc[b]);
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int b = 0; b < NBW; ++b)
+                        acc[b] = mfma16(as_bf16x8(zv[p][h]), wv[p][b].frag(h), acc[b]);
+        }
+        if constexpr (Q) {
+            // lane's column j0 + (wave + 4b) * 16 + lr: one W1 row scale
+#pragma unroll
+            for (int b = 0; b < NBW; ++b) acc[b] *= a.w1s[(size_t)e * m + j0 + (wave + 4 * b) * 16 + lr];
         }
 #pragma unroll
         for (int b = 0; b < NBW; ++b)
@@ -203,43 +251,58 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(LayerArgs a) {
         // ---- phase 2: Y[16 x l] = A[16 x MS] . W2[e][:, j0 : j0+MS]^T.  The
         // weight fragment is the MFMA's first operand, so lane l holds output
         // columns i0 + 4 (l / 16) .. +3 of row l % 16: one 16-byte store.
-        // Results are kept for kPass passes of 4 blocks and stored together,
-        // since a load issued behind pending stores waits for them to complete.
-        constexpr int KS = MS / 32;
-        constexpr int kPass = 4;   // block passes per batch of stores
-        bf16x8 af[KS];
+        // A pass loads NU blocks of 16 output columns; the results of NP
+        // passes are stored together, since a load issued behind pending
+        // stores waits for them to complete.
+        constexpr int KB = MS / 64;        // 64-wide k blocks of the slice
+        constexpr int NU = 4;              // blocks per pass
+        // passes per batch of stores (FP8: 2, which keeps the decode
+        // registers within two waves per SIMD)
+        constexpr int NP = Q ? 2 : 4;
+        bf16x8 af[KB][2];
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk)
-            af[kk] = *reinterpret_cast<const bf16x8*>(&As[lr * AST + kk * 32 + koff]);
+        for (int q = 0; q < KB; ++q)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                af[q][h] = *reinterpret_cast<const bf16x8*>(&As[lr * AST + 64 * q + k16 + 8 * h]);
         const int nblk = l / 16;
-        // a wave takes blocks wave + 4 (4 it + u), kPass passes it per batch
-        for (int ib0 = wave; ib0 < nblk; ib0 += 16 * kPass) {
-            f32x4 yb[kPass][4];
+        // a wave takes blocks wave + 4 (NU it + u), NP passes it per batch
+        for (int ib0 = wave; ib0 < nblk; ib0 += 4 * NU * NP) {
+            f32x4 yb[NP][NU];
 #pragma unroll
-            for (int it = 0; it < kPass; ++it) {
-                uint4 wv[4][KS];
+            for (int it = 0; it < NP; ++it) {
+                WB wv[NU][KB];
+                f32x4 sc[NU];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int ib = ib0 + 16 * it + 4 * u;
+                for (int u = 0; u < NU; ++u) {
+                    const int ib = ib0 + 4 * (NU * it + u);
                     const bool ok = ib < nblk;
-                    const bf16* p = W2e + (size_t)(ib * 16 + lr) * m + j0 + koff;
+                    const WT* p = W2e + (size_t)(ib * 16 + lr) * m + j0 + k16;
 #pragma unroll
-                    for (int kk = 0; kk < KS; ++kk) wv[u][kk] = ok ? ldg16(p + kk * 32) : kZero16;
+                    for (int q = 0; q < KB; ++q) wv[u][q] = ok ? WB::load(p + 64 * q) : WB::zero();
+                    if constexpr (Q) {
+                        // the lane's 4 output rows ib*16 + 4 (lane/16) .. +3 of W2
+                        sc[u] = ok ? *reinterpret_cast<const f32x4*>(a.w2s + (size_t)e * l + ib * 16 + 4 * (lane >> 4))
+                                   : f32x4{0.f, 0.f, 0.f, 0.f};
+                    }
                 }
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
+                for (int u = 0; u < NU; ++u) {
                     f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int kk = 0; kk < KS; ++kk) y = mfma16(as_bf16x8(wv[u][kk]), af[kk], y);
+                    for (int q = 0; q < KB; ++q)
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) y = mfma16(wv[u][q].frag(h), af[q][h], y);
+                    if constexpr (Q) y *= sc[u];
                     yb[it][u] = y;
                 }
             }
             if (lr < nr) {
 #pragma unroll
-                for (int it = 0; it < kPass; ++it)
+                for (int it = 0; it < NP; ++it)
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const int ib = ib0 + 16 * it + 4 * u;
+                    for (int u = 0; u < NU; ++u) {
+                        const int ib = ib0 + 4 * (NU * it + u);
                         if (ib < nblk)
                             *reinterpret_cast<f32x4*>(&Yp[(size_t)(rc + lr) * l + ib * 16 + 4 * (lane >> 4)]) =
                                 yb[it][u];

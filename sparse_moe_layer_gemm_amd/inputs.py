@@ -25,6 +25,8 @@ operands of every product):
   W_up     [d, l]        out_n = x_n + sum_i W_up[n, i] s_i
   bias     [N] float32 (skewed workload only)
   W_s1     [m_s, d], W_s2 [d, m_s]   shared expert (the *_shared workloads)
+  FP8 experts (the *_fp8 workloads): W1, W2 as uint8 E4M3 codes in the same
+  layout, W1_scale [N, m] and W2_scale [N, l] float32 row scales
 
 Recipe: one CPU torch.Generator seeded with `seed`; draws in the order x,
 W_down, W_router, W1 (one draw of [m, l] per expert, expert 0 first), W2 (one
@@ -33,6 +35,10 @@ shared expert, so the other arrays are the same with or without one).
 Every draw is float32 N(0, 1); weights
 are multiplied by 1/sqrt(fan_in) in float32; for bf16 workloads every array
 except the bias is then rounded to bfloat16 (round-to-nearest-even).
+FP8 experts stand for a checkpoint stored that way: each expert's float32
+draw (the same draw as above) is cut into rows, each row gets the scale
+max|row| / 448 (1 for an all-zero row) and its codes are the row divided by
+that scale, rounded to E4M3 by torch's float8_e4m3fn conversion.
 x ~ N(0, 1) throughout, so routing is near uniform except where the fixed
 logit bias ~ N(0, 1) skews the expert loads.
 """
@@ -58,6 +64,7 @@ class Workload:
     standard: bool = False  # no projections: l == d, z = x, out = x + s
     bias: bool = False      # fixed per-expert logit bias ~ N(0, 1)
     m_shared: int = 0       # shared expert width (0: none)
+    experts: str = "dense"  # routed expert weights: "dense" (the layer's dtype) or "fp8" (E4M3 + row scales)
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -89,7 +96,23 @@ WORKLOADS: Dict[str, Workload] = {
                               m_shared=768),
     "prefill_shared": Workload("prefill_shared", T=16384, d=4096, l=1024, N=512, K=22, m=768, dtype="bf16",
                                m_shared=768),
+    # The decode and prefill layers with FP8 E4M3 routed-expert weights.
+    "decode_fp8": Workload("decode_fp8", T=32, d=4096, l=1024, N=512, K=22, m=768, dtype="bf16",
+                           experts="fp8"),
+    "prefill_fp8": Workload("prefill_fp8", T=16384, d=4096, l=1024, N=512, K=22, m=768, dtype="bf16",
+                            experts="fp8"),
 }
+
+
+E4M3_MAX = 448.0
+
+
+def quantize_rows_e4m3(w: torch.Tensor):
+    """float32 [..., rows, cols] -> (uint8 E4M3 codes, float32 scales [..., rows])."""
+    amax = w.abs().amax(dim=-1)
+    scale = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax))
+    codes = (w / scale.unsqueeze(-1)).to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes.contiguous(), scale.contiguous()
 
 
 def _draw(gen: torch.Generator, shape, scale: Optional[float]) -> torch.Tensor:
@@ -116,14 +139,21 @@ def make_inputs(w: Workload, seed: int = 0, *, x_only_seed: Optional[int] = None
     else:
         out["W_down"] = _draw(gen, (w.l, w.d), 1.0 / math.sqrt(w.d)).to(dt)
     out["W_router"] = _draw(gen, (w.N, w.d), 1.0 / math.sqrt(w.d)).to(dt)
-    W1 = torch.empty((w.N, w.m, w.l), dtype=dt)
-    for e in range(w.N):
-        W1[e] = _draw(gen, (w.m, w.l), 1.0 / math.sqrt(w.l)).to(dt)
-    out["W1"] = W1
-    W2 = torch.empty((w.N, w.l, w.m), dtype=dt)
-    for e in range(w.N):
-        W2[e] = _draw(gen, (w.l, w.m), 1.0 / math.sqrt(w.m)).to(dt)
-    out["W2"] = W2
+    fp8 = w.experts == "fp8"
+    if w.experts not in ("dense", "fp8") or (fp8 and w.dtype != "bf16"):
+        raise ValueError(f"experts={w.experts!r} with dtype={w.dtype!r}")
+    for name, rows, cols in (("W1", w.m, w.l), ("W2", w.l, w.m)):
+        W = torch.empty((w.N, rows, cols), dtype=torch.uint8 if fp8 else dt)
+        S = torch.empty((w.N, rows), dtype=torch.float32) if fp8 else None
+        for e in range(w.N):
+            we = _draw(gen, (rows, cols), 1.0 / math.sqrt(cols))
+            if fp8:
+                W[e], S[e] = quantize_rows_e4m3(we)
+            else:
+                W[e] = we.to(dt)
+        out[name] = W
+        if fp8:
+            out[name + "_scale"] = S
     if w.standard:
         out["W_up"] = None
     else:

@@ -54,7 +54,8 @@ def oracle_arrays(inp):
 def run_oracle(arr, K, sel=None, forced=None):
     return O.forward(arr["x"], arr["W_down"], arr["W_router"], arr["W1"], arr["W2"], arr["W_up"], K,
                      bias=arr["bias"], standard=arr["W_down"] is None, sel=sel, forced_ids=forced,
-                     W_s1=arr.get("W_s1"), W_s2=arr.get("W_s2"))
+                     W_s1=arr.get("W_s1"), W_s2=arr.get("W_s2"),
+                     W1_scale=arr.get("W1_scale"), W2_scale=arr.get("W2_scale"))
 
 
 def expected_dispatch(ids: np.ndarray, N: int):

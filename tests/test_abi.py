@@ -44,7 +44,8 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def dims_of(w, path=B.LMOE_PATH_AUTO):
-    return B.make_dims(w.T, w.d, w.l, w.N, w.m, w.dtype, path, w.m_shared)
+    fmt = B.LMOE_EXPERTS_FP8_E4M3 if w.experts == "fp8" else B.LMOE_EXPERTS_DENSE
+    return B.make_dims(w.T, w.d, w.l, w.N, w.m, w.dtype, path, w.m_shared, fmt)
 
 
 @pytest.mark.parametrize("name", sorted(WORKLOADS))
@@ -147,6 +148,45 @@ def test_shared_expert_argument_checks(lib):
     assert call_shared(d, w.K, W_shared1=None, W_shared2=None) == B.LMOE_EINVAL
     assert call_shared(d, w.K, W_shared2=FAKE + (9 << 30) + 2) == B.LMOE_EINVAL   # misaligned
     assert call_shared(d, w.K, workspace_bytes=B.latentmoe_workspace_bytes(plain, w.K)) == B.LMOE_EWORKSPACE
+
+
+def call_ex(dims, K, **over):
+    args = dict(x=FAKE, W_down=FAKE + (1 << 30), W_router=FAKE + (2 << 30), W1=FAKE + (3 << 30),
+                W2=FAKE + (4 << 30), W_up=FAKE + (5 << 30), out=FAKE + (6 << 30),
+                workspace=FAKE + (7 << 30), workspace_bytes=B.latentmoe_workspace_bytes(dims, K),
+                W1_scale=FAKE + (10 << 30), W2_scale=FAKE + (11 << 30))
+    args.update(over)
+    g = B.lmoe_args(**args)
+    return B.lib().latentmoe_forward_ex(ctypes.byref(g), K, ctypes.byref(dims))
+
+
+def test_fp8_expert_argument_checks(lib):
+    w = WORKLOADS["decode_fp8"]
+    d = dims_of(w)
+    assert d.expert_format == B.LMOE_EXPERTS_FP8_E4M3
+    # the FP8 weights change no workspace region
+    assert B.latentmoe_workspace_bytes(d, w.K) == B.latentmoe_workspace_bytes(dims_of(WORKLOADS["decode"]), w.K)
+    P = ctypes.c_void_p
+    rc = B.lib().latentmoe_forward(P(FAKE), P(FAKE + (1 << 30)), P(FAKE + (2 << 30)), P(FAKE + (3 << 30)),
+                                   P(FAKE + (4 << 30)), P(FAKE + (5 << 30)), w.K, P(FAKE + (6 << 30)),
+                                   ctypes.byref(d), None, None, None, P(FAKE + (7 << 30)),
+                                   ctypes.c_size_t(B.latentmoe_workspace_bytes(d, w.K)), None)
+    assert rc == B.LMOE_EINVAL                                             # FP8 needs the _ex call
+    assert "latentmoe_forward_ex" in B.latentmoe_last_error()
+    assert call_shared(dims_of(w.replace(m_shared=64)), w.K) == B.LMOE_EINVAL
+    assert call_ex(d, w.K, W2_scale=None) == B.LMOE_EINVAL                # both scales or none
+    assert call_ex(d, w.K, W1_scale=None, W2_scale=None) == B.LMOE_EINVAL
+    assert call_ex(d, w.K, W1_scale=FAKE + (10 << 30) + 4) == B.LMOE_EINVAL  # misaligned
+    plain = dims_of(WORKLOADS["decode"])
+    assert call_ex(plain, w.K) == B.LMOE_EINVAL                           # scales without FP8
+    f32 = dims_of(WORKLOADS["tiny_f32"].replace(experts="fp8"))
+    assert call_ex(f32, 4) == B.LMOE_EUNSUPPORTED                         # FP8 experts need bf16
+    bad = dims_of(w)
+    bad.expert_format = 2
+    assert B.latentmoe_workspace_bytes(bad, w.K) == 0
+    assert call_ex(bad, w.K) == B.LMOE_EINVAL
+    assert B.lib().latentmoe_forward_ex(None, w.K, ctypes.byref(d)) == B.LMOE_EINVAL
+    assert call_ex(d, w.K, workspace_bytes=100) == B.LMOE_EWORKSPACE
 
 
 def test_status_strings(lib):

@@ -145,6 +145,75 @@ def test_shared_expert_with_zero_w2_is_the_plain_layer(path):
     assert torch.equal(a, b)
 
 
+# --- FP8 E4M3 routed-expert weights with per-row scales -----------------------
+
+@pytest.mark.parametrize("path", [B.LMOE_PATH_AUTO, TL])
+def test_decode_fp8(path):
+    w = WORKLOADS["decode_fp8"]
+    P.compare(w, P.gen(w, 0), w.K, path=path, tag=f"decode_fp8/path{path}")
+
+
+def test_prefill_fp8_sampled():
+    w = WORKLOADS["prefill_fp8"]
+    P.compare(w, P.gen(w, 0), w.K, sample=sample_tokens(w.T, 96))
+
+
+FP8_SHAPES = [
+    Workload("fp8_latent", T=300, d=256, l=64, N=16, K=4, m=128, dtype="bf16", experts="fp8"),
+    Workload("fp8_m192", T=37, d=512, l=256, N=64, K=8, m=192, dtype="bf16", experts="fp8"),
+    Workload("fp8_large_tiles", T=2048, d=256, l=128, N=16, K=4, m=320, dtype="bf16", experts="fp8"),
+    Workload("fp8_standard", T=90, d=256, l=256, N=12, K=2, m=128, dtype="bf16", standard=True, experts="fp8"),
+    Workload("fp8_shared", T=100, d=256, l=64, N=16, K=4, m=128, dtype="bf16", m_shared=128, experts="fp8"),
+    Workload("fp8_one_token", T=1, d=256, l=64, N=16, K=3, m=128, dtype="bf16", experts="fp8"),
+]
+
+
+@pytest.mark.parametrize("w", FP8_SHAPES, ids=lambda w: w.name)
+@pytest.mark.parametrize("path", [B.LMOE_PATH_AUTO, S, TL])
+def test_fp8_shapes(w, path):
+    P.compare(w, make_inputs(w, 11), w.K, path=path, tag=f"{w.name}/path{path}")
+
+
+def every_code_inputs(w: Workload, seed: int):
+    """FP8 inputs whose codes run through every non-NaN E4M3 code (so every
+    decode the kernels do is exercised) with power-of-two row scales."""
+    inp = make_inputs(w, seed)
+    g = torch.Generator().manual_seed(seed + 1)
+    codes = torch.tensor([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=torch.uint8)
+    for name, rows in (("W1", w.m), ("W2", w.l)):
+        n = inp[name].numel()
+        perm = codes[torch.randperm(codes.numel(), generator=g)]
+        inp[name] = perm.repeat(n // perm.numel() + 1)[:n].reshape(inp[name].shape).contiguous()
+        # codes reach 448: scales 2^-14 .. 2^-10 keep the weights below 0.5
+        inp[name + "_scale"] = torch.ldexp(torch.ones(w.N, rows),
+                                           torch.randint(-14, -9, (w.N, rows), generator=g).float())
+    return inp
+
+
+@pytest.mark.parametrize("path", [S, TL])
+def test_fp8_every_code(path):
+    w = Workload("fp8_every_code", T=120, d=256, l=128, N=16, K=4, m=128, dtype="bf16", experts="fp8")
+    P.compare(w, every_code_inputs(w, 12), w.K, path=path, tag=f"fp8_every_code/path{path}")
+
+
+@pytest.mark.parametrize("path", [S, TL])
+def test_fp8_layer_is_the_bf16_layer_on_decoded_weights(path):
+    """With power-of-two row scales every decoded weight code * scale is a
+    bfloat16 value and scaling a float32 dot product by the scale is exact,
+    so the FP8 layer equals, bit for bit, the bf16 layer on those weights."""
+    w = Workload("fp8_pow2", T=120, d=256, l=128, N=16, K=4, m=128, dtype="bf16", experts="fp8")
+    inp = every_code_inputs(w, 13)
+    dense = dict(inp)
+    for name in ("W1", "W2"):
+        dec = inp[name].view(torch.float8_e4m3fn).float() * dense.pop(name + "_scale").unsqueeze(-1)
+        dense[name] = dec.to(torch.bfloat16)
+        assert torch.equal(dense[name].float(), dec)
+    a = B.forward(P.to_device(inp), w.K, path=path)
+    b = B.forward(P.to_device(dense), w.K, path=path)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
 # --- smaller shapes: several tiles, ragged tails, both FFN paths --------------
 
 SMALL_PREFILL = Workload("small_prefill", T=1000, d=512, l=128, N=64, K=6, m=256, dtype="bf16")
