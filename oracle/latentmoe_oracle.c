@@ -37,12 +37,25 @@
  *      the routed one (10100.com article section 3.3, the shared-expert
  *      stream).  Its width m_shared and its activation (the routed experts'
  *      squared ReLU) are readings: the pages give neither.
+ *   8. Optional zero-computation experts (10100.com article section 3.2,
+ *      after MoE++): n_zero + n_copy + n_const extra expert ids N, N+1, ...
+ *      (zero experts first, then copy, then constant) that the router scores
+ *      like the others (W_router and bias have a row for each) and that take
+ *      part in the softmax, the top-K and the renormalisation like the
+ *      others.  Selected, they add g * y to s with y = 0 (zero expert: the
+ *      token's input to this expert is dropped), y = z (copy expert: the
+ *      identity on the expert's input) or y = c_q (constant expert: the
+ *      input replaced by its own vector c_q of width l).  That they live
+ *      where the routed experts live (in l, their input being z) is the
+ *      reading taken; the pages describe them for a plain MoE.
  * Standard mode (no projections, l == d): z = x and out = x + s, the plain
  * MoE of 10100.com Figure 3a (plus the shared expert when present).
  *
  * Storage (row-major; the reduction index is the fastest one):
- *   x [T,d]  W_down [l,d]  W_router [N,d]  W1 [N,m,l]  W2 [N,l,m]  W_up [d,l]
- *   Ws1 [m_shared,d]  Ws2 [d,m_shared]  bias [N] float32 or NULL.
+ *   x [T,d]  W_down [l,d]  W_router [Nr,d]  W1 [N,m,l]  W2 [N,l,m]  W_up [d,l]
+ *   Ws1 [m_shared,d]  Ws2 [d,m_shared]  bias [Nr] float32 or NULL
+ *   zc [n_const,l] (constant experts' vectors, the layer's element type)
+ * with Nr = N + n_zero + n_copy + n_const routed ids.
  * Element type of x and the weights: float32 (dtype 0) or bfloat16 bit
  * patterns (dtype 1).  Each element is widened to double at use; every sum is
  * accumulated in double in index order.
@@ -70,7 +83,11 @@ typedef struct {
     int32_t standard; /* 1: no projections (requires l == d) */
     int32_t m_shared; /* width of the shared expert, 0: none */
     int32_t experts_fp8; /* 1: W1, W2 are E4M3 codes with per-row scales */
+    int32_t n_zero, n_copy, n_const; /* zero-computation experts (ids N ...) */
 } oracle_dims;
+
+/* routed ids: the FFN experts and the zero-computation experts */
+static int routed_ids(const oracle_dims* D) { return D->N + D->n_zero + D->n_copy + D->n_const; }
 
 static double widen(const void* base, int dtype, size_t i) {
     if (dtype == 0) return (double)((const float*)base)[i];
@@ -99,6 +116,22 @@ static double expert_w(const oracle_dims* D, const void* W, const float* scale, 
     return widen(W, D->dtype, i);
 }
 
+/*
+ * Step 8: zero-computation expert q (counted from id N: zero experts, then
+ * copy, then constant) with gate g adds g * y to s.
+ */
+static void zero_computation_expert(const oracle_dims* D, int q, const double* z, const void* zc,
+                                    double g, double* s) {
+    if (q < D->n_zero) return; /* zero expert: y = 0 */
+    q -= D->n_zero;
+    if (q < D->n_copy) { /* copy expert: y = z */
+        for (int i = 0; i < D->l; ++i) s[i] += g * z[i];
+        return;
+    }
+    q -= D->n_copy; /* constant expert q: y = c_q */
+    for (int i = 0; i < D->l; ++i) s[i] += g * widen(zc, D->dtype, (size_t)q * D->l + i);
+}
+
 /* logit order: a outranks b if its logit is larger, or equal with a lower index */
 static int outranks(const double* logit, int a, int b) {
     return logit[a] > logit[b] || (logit[a] == logit[b] && a < b);
@@ -112,17 +145,18 @@ static int outranks(const double* logit, int a, int b) {
 static void one_token(const oracle_dims* D, int t, const void* x, const void* Wd,
                       const void* Wr, const void* W1, const void* W2, const void* Wu,
                       const void* Ws1, const void* Ws2, const float* s1, const float* s2,
-                      const float* bias, const int32_t* forced, double* out_t,
+                      const void* zc, const float* bias, const int32_t* forced, double* out_t,
                       int32_t* ids_t, double* gates_t, double* logits_t, double* gap_t,
                       double* work) {
     const int d = D->d, l = D->l, N = D->N, K = D->K, m = D->m, dt = D->dtype;
+    const int Nr = routed_ids(D);
     double* xt = work;            /* [d] */
     double* z = xt + d;           /* [l] */
-    double* p = z + l;            /* [N] */
-    double* h = p + N;            /* [m] */
+    double* p = z + l;            /* [Nr] */
+    double* h = p + Nr;           /* [m] */
     double* s = h + m;            /* [l] */
     double* hs = s + l;           /* [m_shared] */
-    char* chosen = (char*)(hs + D->m_shared); /* [N] */
+    char* chosen = (char*)(hs + D->m_shared); /* [Nr] */
 
     for (int i = 0; i < d; ++i) xt[i] = widen(x, dt, (size_t)t * d + i);
 
@@ -137,33 +171,33 @@ static void one_token(const oracle_dims* D, int t, const void* x, const void* Wd
         }
     }
 
-    /* step 2: router logits at full d */
-    for (int e = 0; e < N; ++e) {
+    /* step 2: router logits at full d, one per routed id */
+    for (int e = 0; e < Nr; ++e) {
         double acc = 0.0;
         for (int i = 0; i < d; ++i) acc += widen(Wr, dt, (size_t)e * d + i) * xt[i];
         if (bias) acc += (double)bias[e];
         logits_t[e] = acc;
     }
 
-    /* step 3a: softmax over all N, max subtracted */
+    /* step 3a: softmax over all Nr routed ids, max subtracted */
     double mx = logits_t[0];
-    for (int e = 1; e < N; ++e) if (logits_t[e] > mx) mx = logits_t[e];
+    for (int e = 1; e < Nr; ++e) if (logits_t[e] > mx) mx = logits_t[e];
     double den = 0.0;
-    for (int e = 0; e < N; ++e) { p[e] = exp(logits_t[e] - mx); den += p[e]; }
-    for (int e = 0; e < N; ++e) p[e] /= den;
+    for (int e = 0; e < Nr; ++e) { p[e] = exp(logits_t[e] - mx); den += p[e]; }
+    for (int e = 0; e < Nr; ++e) p[e] /= den;
 
-    /* step 3b: the K best experts in rank order (largest logit, then lowest index) */
-    memset(chosen, 0, (size_t)N);
+    /* step 3b: the K best ids in rank order (largest logit, then lowest index) */
+    memset(chosen, 0, (size_t)Nr);
     for (int k = 0; k < K; ++k) {
         int best = -1;
-        for (int e = 0; e < N; ++e)
+        for (int e = 0; e < Nr; ++e)
             if (!chosen[e] && (best < 0 || outranks(logits_t, e, best))) best = e;
         chosen[best] = 1;
         ids_t[k] = best;
     }
-    if (K < N) {
+    if (K < Nr) {
         int next = -1;
-        for (int e = 0; e < N; ++e)
+        for (int e = 0; e < Nr; ++e)
             if (!chosen[e] && (next < 0 || outranks(logits_t, e, next))) next = e;
         *gap_t = logits_t[ids_t[K - 1]] - logits_t[next];
     } else {
@@ -180,6 +214,10 @@ static void one_token(const oracle_dims* D, int t, const void* x, const void* Wd
     for (int i = 0; i < l; ++i) s[i] = 0.0;
     for (int k = 0; k < K; ++k) {
         const size_t e = (size_t)ids_t[k];
+        if (ids_t[k] >= N) {
+            zero_computation_expert(D, ids_t[k] - N, z, zc, gates_t[k], s);
+            continue;
+        }
         for (int j = 0; j < m; ++j) {
             double acc = 0.0;
             for (int i = 0; i < l; ++i) acc += expert_w(D, W1, s1, (e * m + j) * l + i, e * m + j) * z[i];
@@ -226,18 +264,21 @@ static void one_token(const oracle_dims* D, int t, const void* x, const void* Wd
  * oracle_forward: evaluate `n_sel` tokens (token indices in `sel`, or the
  * first n_sel tokens when sel is NULL).  Outputs are indexed by position in
  * the selection:  out [n_sel,d]  ids [n_sel,K]  gates [n_sel,K]
- * logits [n_sel,N]  gap [n_sel]  (gap = K-th minus (K+1)-th largest logit).
+ * logits [n_sel,Nr]  gap [n_sel]  (gap = K-th minus (K+1)-th largest logit).
  * forced_ids [n_sel,K] or NULL.  Ws1 / Ws2: the shared expert, used only
  * when D->m_shared > 0.  s1 [N*m] / s2 [N*l]: the FP8 expert weights' row
- * scales, used only when D->experts_fp8.  Returns 0, or -1 on bad arguments.
+ * scales, used only when D->experts_fp8.  zc [n_const*l]: the constant
+ * experts' vectors, used only when D->n_const > 0.  Returns 0, or -1 on bad
+ * arguments.
  */
 int oracle_forward(const oracle_dims* D, const void* x, const void* Wd, const void* Wr,
                    const void* W1, const void* W2, const void* Wu, const void* Ws1,
-                   const void* Ws2, const float* s1, const float* s2, const float* bias,
-                   const int32_t* sel, int32_t n_sel, const int32_t* forced_ids,
+                   const void* Ws2, const float* s1, const float* s2, const void* zc,
+                   const float* bias, const int32_t* sel, int32_t n_sel, const int32_t* forced_ids,
                    double* out, int32_t* ids, double* gates, double* logits, double* gap) {
     if (!D || !x || !Wr || !W1 || !W2 || !out || !ids || !gates || !logits || !gap) return -1;
-    if (D->K < 1 || D->K > D->N || D->T < 0 || n_sel < 0 || D->m_shared < 0) return -1;
+    if (D->n_zero < 0 || D->n_copy < 0 || D->n_const < 0 || (D->n_const > 0 && !zc)) return -1;
+    if (D->K < 1 || D->K > routed_ids(D) || D->T < 0 || n_sel < 0 || D->m_shared < 0) return -1;
     if (D->standard ? (D->l != D->d) : (!Wd || !Wu)) return -1;
     if (D->m_shared > 0 && (!Ws1 || !Ws2)) return -1;
     if (D->experts_fp8 && (!s1 || !s2)) return -1;
@@ -246,7 +287,7 @@ int oracle_forward(const oracle_dims* D, const void* x, const void* Wd, const vo
         if (t < 0 || t >= D->T) return -1;
     }
     const size_t work_doubles =
-        (size_t)D->d + 2 * (size_t)D->l + D->N + D->m + D->m_shared + (D->N + 7) / 8 + 1;
+        (size_t)D->d + 2 * (size_t)D->l + routed_ids(D) + D->m + D->m_shared + (routed_ids(D) + 7) / 8 + 1;
     int bad = 0;
 #pragma omp parallel
     {
@@ -258,10 +299,10 @@ int oracle_forward(const oracle_dims* D, const void* x, const void* Wd, const vo
 #pragma omp for schedule(dynamic, 1)
             for (int q = 0; q < n_sel; ++q) {
                 int t = sel ? sel[q] : q;
-                one_token(D, t, x, Wd, Wr, W1, W2, Wu, Ws1, Ws2, s1, s2, bias,
+                one_token(D, t, x, Wd, Wr, W1, W2, Wu, Ws1, Ws2, s1, s2, zc, bias,
                           forced_ids ? forced_ids + (size_t)q * D->K : NULL,
                           out + (size_t)q * D->d, ids + (size_t)q * D->K,
-                          gates + (size_t)q * D->K, logits + (size_t)q * D->N, gap + q, work);
+                          gates + (size_t)q * D->K, logits + (size_t)q * routed_ids(D), gap + q, work);
             }
             free(work);
         }

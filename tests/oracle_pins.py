@@ -29,6 +29,13 @@ What pins what:
                power-of-two row scale is exact in float32: the FP8 layer
                equals the float32 layer on those weights bit-exactly; with
                arbitrary row scales, N = K = 1 is a dense FFN in numpy
+  zero-        a dense-mask evaluation in numpy (every routed id's output
+  computation  for every token, weighted by a [T, Nr] gate matrix that is
+  experts      zero off the top K); K = 1 special cases with closed forms:
+               a zero expert gives x exactly, a copy expert x + W_up W_down x
+               (2x exactly in standard mode), a constant expert x + W_up c;
+               zero-computation experts that never win leave the layer
+               bit-exactly as without them
 """
 from __future__ import annotations
 
@@ -437,6 +444,88 @@ def pin_fp8_experts(o):
     assert np.allclose(got, want, rtol=1e-12, atol=1e-12), "FP8 dense special case differs from numpy"
 
 
+def zc_layer(seed, T, d, l, N, m, nz, nc, nk, *, standard=False):
+    """A float32 layer with N FFN experts followed by nz zero, nc copy and nk
+    constant experts (router rows for all of them)."""
+    Nr = N + nz + nc + nk
+    L = rand_layer(seed, T, d, l, Nr, m, standard=standard)
+    L["W1"] = np.ascontiguousarray(L["W1"][:N])
+    L["W2"] = np.ascontiguousarray(L["W2"][:N])
+    L["zc_const"] = _rng(seed + 1000).standard_normal((nk, l)).astype(np.float32) if nk else None
+    L["n_zero"], L["n_copy"] = nz, nc
+    return L
+
+
+def run_zc(o, L, K, **kw):
+    return run(o, L, K, n_zero=L["n_zero"], n_copy=L["n_copy"], zc_const=L["zc_const"], **kw)
+
+
+def np_dense_mask(L, K):
+    """The layer with zero-computation experts, evaluated densely in numpy."""
+    x = f64(L["x"])
+    N, nz, nc = L["W1"].shape[0], L["n_zero"], L["n_copy"]
+    standard = L["W_down"] is None
+    z = x if standard else x @ f64(L["W_down"]).T
+    lg = np_logits(L)
+    T, Nr = lg.shape
+    G = np.zeros((T, Nr))
+    for t in range(T):
+        top = sorted(range(Nr), key=lambda e: (-lg[t, e], e))[:K]
+        p = softmax(lg[t])
+        G[t, top] = p[top] / p[top].sum()
+    Y = np.zeros((T, Nr, z.shape[1]))
+    for e in range(N):
+        Y[:, e] = (np.maximum(z @ f64(L["W1"][e]).T, 0.0) ** 2) @ f64(L["W2"][e]).T
+    for q in range(nc):
+        Y[:, N + nz + q] = z
+    if L["zc_const"] is not None:
+        for q in range(L["zc_const"].shape[0]):
+            Y[:, N + nz + nc + q] = f64(L["zc_const"][q])
+    s = np.einsum("te,tel->tl", G, Y)
+    return x + (s if standard else s @ f64(L["W_up"]).T), G
+
+
+def pin_zero_computation_experts(o):
+    """Zero, copy and constant experts among the routed ids."""
+    # dense mask, latent and standard mode, every kind present
+    for standard in (False, True):
+        L = zc_layer(51, T=9, d=16, l=16 if standard else 8, N=5, m=12, nz=2, nc=2, nk=3, standard=standard)
+        for K in (3, 6):
+            got = run_zc(o, L, K)
+            want, G = np_dense_mask(L, K)
+            for t in range(L["x"].shape[0]):
+                assert set(got["ids"][t].tolist()) == set(np.nonzero(G[t])[0].tolist()), "selection"
+            assert np.allclose(got["out"], want, rtol=1e-11, atol=1e-12), "dense-mask evaluation differs"
+    # K = 1 with one routed id made to win by its bias: closed forms
+    T, d, l, N, m = 7, 16, 8, 4, 12
+
+    def winner(L, e):
+        Nr = L["W_router"].shape[0]
+        L["bias"] = np.full(Nr, -40.0, np.float32)
+        L["bias"][e] = 40.0
+        return L
+
+    L = winner(zc_layer(52, T, d, l, N, m, 1, 1, 2), N)              # the zero expert
+    got = run_zc(o, L, 1)
+    x64 = f64(L["x"])
+    assert np.array_equal(got["ids"][:, 0], np.full(T, N)) and np.array_equal(got["out"], x64), "zero expert"
+    L = winner(zc_layer(52, T, d, l, N, m, 1, 1, 2), N + 1)          # the copy expert
+    want = x64 + (x64 @ f64(L["W_down"]).T) @ f64(L["W_up"]).T
+    assert np.allclose(run_zc(o, L, 1)["out"], want, rtol=1e-12, atol=1e-13), "copy expert"
+    L = winner(zc_layer(52, T, d, l, N, m, 1, 1, 2), N + 3)          # the second constant expert
+    want = x64 + np.outer(np.ones(T), f64(L["zc_const"][1]) @ f64(L["W_up"]).T)
+    assert np.allclose(run_zc(o, L, 1)["out"], want, rtol=1e-12, atol=1e-13), "constant expert"
+    L = winner(zc_layer(53, T, d, d, N, m, 1, 1, 0, standard=True), N + 1)   # copy, standard mode
+    assert np.array_equal(run_zc(o, L, 1)["out"], 2.0 * f64(L["x"])), "standard-mode copy expert"
+    # zero-computation experts that never win change nothing
+    L = zc_layer(54, T, d, l, N, m, 2, 1, 1)
+    L["bias"] = np.zeros(N + 4, np.float32)
+    L["bias"][N:] = -1e30
+    plain = dict(L, W_router=np.ascontiguousarray(L["W_router"][:N]), bias=L["bias"][:N].copy())
+    a, b = run_zc(o, L, 3), run(o, plain, 3)
+    assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["ids"], b["ids"]), "losing experts changed out"
+
+
 ALL_PINS = [
     pin_routing_bruteforce,
     pin_tie_break,
@@ -451,4 +540,5 @@ ALL_PINS = [
     pin_selection_and_forced_ids,
     pin_shared_expert,
     pin_fp8_experts,
+    pin_zero_computation_experts,
 ]

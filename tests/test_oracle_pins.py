@@ -69,6 +69,14 @@ MUTANTS = {
     "fp8_scale_dropped": ("e4m3(((const uint8_t*)W)[i]) * (double)scale[row]", "e4m3(((const uint8_t*)W)[i])"),
     "fp8_scale_wrong_row": ("e4m3(((const uint8_t*)W)[i]) * (double)scale[row]",
                             "e4m3(((const uint8_t*)W)[i]) * (double)scale[row / 2]"),
+    "zc_not_selectable": ("        for (int e = 0; e < Nr; ++e)\n            if (!chosen[e] && (best < 0",
+                          "        for (int e = 0; e < N; ++e)\n            if (!chosen[e] && (best < 0"),
+    "zc_zero_acts_as_copy": ("if (q < D->n_zero) return;", "if (q < 0) return;"),
+    "zc_copy_outputs_x": ("zero_computation_expert(D, ids_t[k] - N, z, zc, gates_t[k], s);",
+                          "zero_computation_expert(D, ids_t[k] - N, xt, zc, gates_t[k], s);"),
+    "zc_copy_gate_dropped": ("s[i] += g * z[i];", "s[i] += z[i];"),
+    "zc_const_first_only": ("q -= D->n_copy; /* constant", "q = 0; /* constant"),
+    "zc_const_gate_dropped": ("s[i] += g * widen(zc,", "s[i] += widen(zc,"),
 }
 
 
