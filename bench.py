@@ -81,13 +81,16 @@ def expert_bytes(w, A: float) -> float:
     return A * 2 * w.l * w.m * w.elem_bytes
 
 
-def algorithmic(w, A: float):
-    """Whole-layer algorithmic bytes and flops (A = experts that got rows)."""
+def algorithmic(w, A: float, R: float):
+    """Whole-layer algorithmic bytes and flops (A = FFN experts that got rows,
+    R = (token, rank) pairs routed to FFN experts: T*K without
+    zero-computation experts)."""
     B = w.elem_bytes
     lat = 0 if w.standard else 1
-    nbytes = B * (2 * w.T * w.d + lat * 2 * w.d * w.l + w.d * w.N + 2 * w.d * w.m_shared) \
-        + expert_bytes(w, A) + (4 * w.N if w.bias else 0)
-    flops = lat * 4 * w.T * w.d * w.l + 2 * w.T * w.d * w.N + 4 * w.T * w.K * w.l * w.m + 4 * w.T * w.d * w.m_shared
+    Nr = w.N + w.n_zc
+    nbytes = B * (2 * w.T * w.d + lat * 2 * w.d * w.l + w.d * Nr + 2 * w.d * w.m_shared + w.n_const * w.l) \
+        + expert_bytes(w, A) + (4 * Nr if w.bias else 0)
+    flops = lat * 4 * w.T * w.d * w.l + 2 * w.T * w.d * Nr + 4 * R * w.l * w.m + 4 * w.T * w.d * w.m_shared
     return nbytes, flops
 
 
@@ -143,7 +146,7 @@ def measure(w, sets, cpu_seconds: float) -> dict:
 
     args = ARGS
     dev = torch.device("cuda:0")
-    dims = B.dims_for(sets[0][1], w.K, args.path)
+    dims = B.dims_for(sets[0][1], w.K, args.path, w.n_zero, w.n_copy)
     path = B.latentmoe_resolved_path(dims, w.K)
     ws = B.alloc_workspace(dims, w.K, dev)
     out = torch.empty_like(sets[0][1]["x"])
@@ -156,16 +159,19 @@ def measure(w, sets, cpu_seconds: float) -> dict:
         B.latentmoe_forward(d["x"], d["W_down"], d["W_router"], d["W1"], d["W2"], d["W_up"], w.K, out, dims,
                             router_bias=d["bias"], workspace=ws, stream=stream, events=events,
                             W_shared1=d.get("W_s1"), W_shared2=d.get("W_s2"),
-                            W1_scale=d.get("W1_scale"), W2_scale=d.get("W2_scale"))
+                            W1_scale=d.get("W1_scale"), W2_scale=d.get("W2_scale"), zc_const=d.get("zc_const"))
 
-    # active experts per weight set (for the algorithmic byte count)
+    # active FFN experts and FFN rows per weight set (for the algorithmic counts)
     lay = B.latentmoe_workspace_layout(dims, w.K)
-    active = []
+    active, rows = [], []
     for i in range(len(sets)):
         step(i)
         torch.cuda.synchronize()
-        active.append(int(ws[lay.n_active:lay.n_active + 4].cpu().numpy().view(np.int32)[0]))
+        raw = ws.cpu().numpy()
+        active.append(int(raw[lay.n_active:lay.n_active + 4].view(np.int32)[0]))
+        rows.append(int(raw[lay.offsets + 4 * w.N:lay.offsets + 4 * w.N + 4].view(np.int32)[0]))
     A = float(np.mean(active))
+    R = float(np.mean(rows))
 
     for i in range(args.warmup):
         step(i)
@@ -201,7 +207,7 @@ def measure(w, sets, cpu_seconds: float) -> dict:
         for si, name in enumerate(B.STAGES):
             stages[name] = float(np.mean([hip.elapsed_ms(ev[si], ev[si + 1]) for ev in ev_all])) * 1e3
     copy_gbs = copy_bandwidth(torch, dev)
-    lay_bytes, lay_flops = algorithmic(w, A)
+    lay_bytes, lay_flops = algorithmic(w, A, R)
 
     # dominant kernel: the expert FFN
     if path == B.LMOE_PATH_STREAM:
@@ -209,12 +215,12 @@ def measure(w, sets, cpu_seconds: float) -> dict:
         roof = {"kernel": "ffn_stream_kernel", "bound": "hbm", "achieved": ffn_bytes / (ffn_us * 1e-6) / 1e9,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": None}
     elif w.dtype == "f32":
-        ffn_flops = 4.0 * w.T * w.K * w.l * w.m
+        ffn_flops = 4.0 * R * w.l * w.m
         roof = {"kernel": "gemm_simt_kernel<Ffn1>+<Ffn2>", "bound": "alu",
                 "achieved": ffn_flops / (ffn_us * 1e-6) / 1e12, "peak": FP32_VECTOR_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "traffic": None}
     else:
-        ffn_flops = 4.0 * w.T * w.K * w.l * w.m
+        ffn_flops = 4.0 * R * w.l * w.m
         # FP8 weights are decoded to bf16 on the way into LDS: the products
         # run on the bf16 MFMAs, so the bf16 peak is the bound
         q = "Q" if w.experts == "fp8" else ""
@@ -246,12 +252,14 @@ def measure(w, sets, cpu_seconds: float) -> dict:
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "d": w.d, "l": w.l, "N": w.N, "K": w.K, "m": w.m,
-                   "m_shared": w.m_shared, "experts": w.experts, "standard": w.standard, "bias": w.bias, "weight_sets": len(sets),
+                   "m_shared": w.m_shared, "experts": w.experts, "n_zero": w.n_zero, "n_copy": w.n_copy,
+                   "n_const": w.n_const, "standard": w.standard, "bias": w.bias, "weight_sets": len(sets),
                    "ffn_path": "stream" if path == B.LMOE_PATH_STREAM else "tiled",
                    "parallelism": "single GPU"},
         "roofline": roof,
         "cpu_baseline": cpu,
         "layer": {"algorithmic_bytes": lay_bytes, "algorithmic_flops": lay_flops, "active_experts": A,
+                  "ffn_rows": R,
                   "roofline_frac": layer_frac, "stage_us": stages},
     }
     return line
@@ -307,7 +315,8 @@ def cpu_baseline(w, inp, budget_s: float):
         sel = np.arange(n % w.T, n % w.T + chunk, dtype=np.int32) % w.T
         orc.forward(arr["x"], arr["W_down"], arr["W_router"], arr["W1"], arr["W2"], arr["W_up"], w.K,
                     bias=arr["bias"], standard=w.standard, sel=sel, W_s1=arr.get("W_s1"), W_s2=arr.get("W_s2"),
-                    W1_scale=arr.get("W1_scale"), W2_scale=arr.get("W2_scale"))
+                    W1_scale=arr.get("W1_scale"), W2_scale=arr.get("W2_scale"),
+                    n_zero=w.n_zero, n_copy=w.n_copy, zc_const=arr.get("zc_const"))
         n += chunk
         passes += 1
         el = time.perf_counter() - t0

@@ -45,6 +45,17 @@
  * W1_scale [N, m] (W1[e][j][:] = code * W1_scale[e][j]) and W2_scale [N, l].
  * The pages name low-precision expert weights (NVFP4 / MXFP4) without a
  * format; this per-row FP8 format is a reading.
+ * Optional zero-computation experts (through latentmoe_forward_ex; after
+ * MoE++, 10100.com article, section 3.2): dims.n_zero zero experts,
+ * dims.n_copy copy experts and dims.n_const constant experts take the
+ * routed ids N, N+1, ... in that order (Nr = N + n_zero + n_copy + n_const
+ * ids in all).  The router scores all Nr ids (W_router [Nr, d], router_bias
+ * [Nr]) and softmax, top-K and renormalisation run over all of them.  A
+ * selected zero expert adds nothing to s, a copy expert adds g * z (its
+ * input), constant expert q adds g * zc_const[q] (zc_const [n_const, l] in
+ * the layer's element type).  That they sit among the latent experts (input
+ * z, output in l) is a reading: the pages describe them for a plain MoE.
+ * topk_ids then range over [0, Nr).
  *
  * Memory: all tensor pointers are DEVICE pointers owned by the caller.  The
  * library allocates nothing in latentmoe_forward, keeps no pointer after it
@@ -93,12 +104,15 @@ typedef struct {
     int32_t T;      /* tokens, >= 1 */
     int32_t d;      /* model width, multiple of 64 */
     int32_t l;      /* latent width, multiple of 64; == d in standard mode */
-    int32_t N;      /* experts, 1 .. 2048 */
+    int32_t N;      /* FFN experts, 1 .. 2048 */
     int32_t m;      /* expert hidden width, multiple of 64 */
     int32_t dtype;  /* lmoe_dtype */
     int32_t path;   /* lmoe_path */
     int32_t m_shared; /* shared expert width: 0 (none) or a multiple of 64 */
     int32_t expert_format; /* lmoe_expert_format */
+    int32_t n_zero;  /* zero-computation experts: zero, copy, constant (>= 0, */
+    int32_t n_copy;  /* N + n_zero + n_copy + n_const <= 2048); all 0 except */
+    int32_t n_const; /* through latentmoe_forward_ex */
 } lmoe_dims;
 
 /* Bytes of device workspace latentmoe_forward needs for these dims and K
@@ -161,6 +175,7 @@ int latentmoe_forward_timed(const void* x, const void* W_down, const void* W_rou
  * Pointers as in latentmoe_forward; W_shared1 / W_shared2 with
  * dims->m_shared > 0 (else NULL); W1_scale / W2_scale with
  * dims->expert_format == LMOE_EXPERTS_FP8_E4M3 (else NULL; 16-byte
+ * aligned); zc_const [n_const, l] with dims->n_const > 0 (else NULL; 16-byte
  * aligned); events NULL or as in latentmoe_forward_timed.  The other
  * forward entry points are this call with the options they do not name
  * turned off.
@@ -176,6 +191,7 @@ typedef struct {
     const void* W_shared2;
     const float* W1_scale;
     const float* W2_scale;
+    const void* zc_const;
     const float* router_bias;
     void* out;
     int32_t* topk_ids;
@@ -202,12 +218,13 @@ int latentmoe_resolved_path(const lmoe_dims* dims, int32_t K);
  * Where the dispatch arrays live inside the workspace after a forward (byte
  * offsets from the workspace base), so that callers and tests can inspect the
  * token -> expert permutation:
- *   counts   [N]      int32  rows routed to each expert
- *   offsets  [N + 1]  int32  exclusive prefix sum of counts
+ *   counts   [Nr]     int32  rows routed to each id (Nr = N without
+ *                            zero-computation experts)
+ *   offsets  [Nr + 1] int32  exclusive prefix sum of counts
  *   perm     [T*K]    int32  slot -> flat pair index t*K + k; the slots of one
  *                            expert are contiguous and in increasing pair order
  *   slot_of  [T*K]    int32  flat pair index -> slot (the inverse of perm)
- *   n_active [1]      int32  experts with at least one row
+ *   n_active [1]      int32  FFN experts (ids < N) with at least one row
  */
 typedef struct {
     size_t counts, offsets, perm, slot_of, n_active;

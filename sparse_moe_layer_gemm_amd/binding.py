@@ -38,13 +38,14 @@ EXPORTED = (
 
 class lmoe_dims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32)
-                for n in ("T", "d", "l", "N", "m", "dtype", "path", "m_shared", "expert_format")]
+                for n in ("T", "d", "l", "N", "m", "dtype", "path", "m_shared", "expert_format",
+                          "n_zero", "n_copy", "n_const")]
 
 
 class lmoe_args(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "x", "W_down", "W_router", "W1", "W2", "W_up", "W_shared1", "W_shared2", "W1_scale", "W2_scale",
-        "router_bias", "out", "topk_ids", "topk_gates", "workspace")] + [
+        "zc_const", "router_bias", "out", "topk_ids", "topk_gates", "workspace")] + [
         ("workspace_bytes", ctypes.c_size_t), ("stream", ctypes.c_void_p), ("events", ctypes.c_void_p)]
 
 
@@ -96,12 +97,12 @@ def lib():
 
 
 def make_dims(T, d, l, N, m, dtype, path=LMOE_PATH_AUTO, m_shared=0,
-              expert_format=LMOE_EXPERTS_DENSE) -> lmoe_dims:
+              expert_format=LMOE_EXPERTS_DENSE, n_zero=0, n_copy=0, n_const=0) -> lmoe_dims:
     if isinstance(dtype, torch.dtype):
         dtype = LMOE_F32 if dtype == torch.float32 else LMOE_BF16
     elif isinstance(dtype, str):
         dtype = LMOE_F32 if dtype == "f32" else LMOE_BF16
-    return lmoe_dims(T, d, l, N, m, dtype, path, m_shared, expert_format)
+    return lmoe_dims(T, d, l, N, m, dtype, path, m_shared, expert_format, n_zero, n_copy, n_const)
 
 
 def latentmoe_workspace_bytes(dims: lmoe_dims, K: int) -> int:
@@ -143,15 +144,17 @@ def _check(rc: int) -> None:
 def latentmoe_forward(x, W_down, W_router, W1, W2, W_up, K: int, out, dims: lmoe_dims,
                       router_bias=None, topk_ids=None, topk_gates=None, workspace=None,
                       workspace_bytes: Optional[int] = None, stream=None, check: bool = True,
-                      events=None, W_shared1=None, W_shared2=None, W1_scale=None, W2_scale=None) -> int:
+                      events=None, W_shared1=None, W_shared2=None, W1_scale=None, W2_scale=None,
+                      zc_const=None) -> int:
     """Call the C entry point with raw device pointers taken from tensors.
 
     `stream`: a torch.cuda.Stream, a raw hipStream_t int, or None for torch's
     current stream.  `events`: None, or a ctypes array of
     LMOE_N_STAGE_EVENTS hipEvent_t handles (calls latentmoe_forward_timed).
     W_shared1 / W_shared2 (with dims.m_shared > 0): calls
-    latentmoe_forward_shared.  W1_scale / W2_scale (FP8 experts) or
-    dims.expert_format != LMOE_EXPERTS_DENSE: calls latentmoe_forward_ex.  Returns the status (raises on failure when
+    latentmoe_forward_shared.  FP8 experts (W1_scale / W2_scale) or
+    zero-computation experts (dims.n_zero / n_copy / n_const, zc_const):
+    calls latentmoe_forward_ex.  Returns the status (raises on failure when
     check=True).
     """
     if stream is None:
@@ -162,9 +165,12 @@ def latentmoe_forward(x, W_down, W_router, W1, W2, W_up, K: int, out, dims: lmoe
         stream_ptr = stream.cuda_stream
     if workspace_bytes is None:
         workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    if W1_scale is not None or W2_scale is not None or dims.expert_format != LMOE_EXPERTS_DENSE:
+    ex = (W1_scale is not None or W2_scale is not None or zc_const is not None
+          or dims.expert_format != LMOE_EXPERTS_DENSE or (dims.n_zero | dims.n_copy | dims.n_const) != 0)
+    if ex:
         args = lmoe_args(_ptr(x), _ptr(W_down), _ptr(W_router), _ptr(W1), _ptr(W2), _ptr(W_up),
-                         _ptr(W_shared1), _ptr(W_shared2), _ptr(W1_scale), _ptr(W2_scale), _ptr(router_bias),
+                         _ptr(W_shared1), _ptr(W_shared2), _ptr(W1_scale), _ptr(W2_scale), _ptr(zc_const),
+                         _ptr(router_bias),
                          _ptr(out), _ptr(topk_ids), _ptr(topk_gates), _ptr(workspace), workspace_bytes,
                          stream_ptr, None if events is None else ctypes.cast(events, ctypes.c_void_p).value)
         rc = lib().latentmoe_forward_ex(ctypes.byref(args), int(K), ctypes.byref(dims))
@@ -186,13 +192,21 @@ def latentmoe_forward(x, W_down, W_router, W1, W2, W_up, K: int, out, dims: lmoe
     return rc
 
 
-def dims_for(inputs: dict, K: int, path: int = LMOE_PATH_AUTO) -> lmoe_dims:
+def dims_for(inputs: dict, K: int, path: int = LMOE_PATH_AUTO, n_zero: int = 0, n_copy: int = 0) -> lmoe_dims:
+    """dims of the layer held in `inputs`.  The split of the zero-computation
+    experts into kinds is not in the arrays: n_zero and n_copy give it (the
+    constant experts are the rows of inputs["zc_const"])."""
     x, W1 = inputs["x"], inputs["W1"]
     T, d = x.shape
     N, m, l = W1.shape
     ws1 = inputs.get("W_s1")
+    zc = inputs.get("zc_const")
+    n_const = 0 if zc is None else zc.shape[0]
+    if inputs["W_router"].shape[0] != N + n_zero + n_copy + n_const:
+        raise ValueError(f"W_router has {inputs['W_router'].shape[0]} rows for N={N} + {n_zero} zero + "
+                         f"{n_copy} copy + {n_const} constant experts")
     fmt = LMOE_EXPERTS_DENSE if inputs.get("W1_scale") is None else LMOE_EXPERTS_FP8_E4M3
-    return make_dims(T, d, l, N, m, x.dtype, path, 0 if ws1 is None else ws1.shape[0], fmt)
+    return make_dims(T, d, l, N, m, x.dtype, path, 0 if ws1 is None else ws1.shape[0], fmt, n_zero, n_copy, n_const)
 
 
 def alloc_workspace(dims: lmoe_dims, K: int, device) -> torch.Tensor:
@@ -203,14 +217,16 @@ def alloc_workspace(dims: lmoe_dims, K: int, device) -> torch.Tensor:
 
 
 def forward(inputs: dict, K: int, *, path: int = LMOE_PATH_AUTO, workspace: Optional[torch.Tensor] = None,
-            out: Optional[torch.Tensor] = None, routing: bool = False, stream=None):
-    """Run the layer on device tensors `inputs` (keys as in inputs.make_inputs).
+            out: Optional[torch.Tensor] = None, routing: bool = False, stream=None, n_zero: int = 0,
+            n_copy: int = 0):
+    """Run the layer on device tensors `inputs` (keys as in inputs.make_inputs;
+    n_zero / n_copy: the zero-computation experts' split, as in dims_for).
 
     Allocates `out` (and the workspace, routing buffers) with torch when not
     given.  Returns out, or (out, ids, gates, workspace) when routing=True.
     """
     x = inputs["x"]
-    dims = dims_for(inputs, K, path)
+    dims = dims_for(inputs, K, path, n_zero, n_copy)
     if workspace is None:
         workspace = alloc_workspace(dims, K, x.device)
     if out is None:
@@ -223,7 +239,8 @@ def forward(inputs: dict, K: int, *, path: int = LMOE_PATH_AUTO, workspace: Opti
                       inputs.get("W_up"), K, out, dims, router_bias=inputs.get("bias"),
                       topk_ids=ids, topk_gates=gates, workspace=workspace, stream=stream,
                       W_shared1=inputs.get("W_s1"), W_shared2=inputs.get("W_s2"),
-                      W1_scale=inputs.get("W1_scale"), W2_scale=inputs.get("W2_scale"))
+                      W1_scale=inputs.get("W1_scale"), W2_scale=inputs.get("W2_scale"),
+                      zc_const=inputs.get("zc_const"))
     if routing:
         return out, ids, gates, workspace
     return out

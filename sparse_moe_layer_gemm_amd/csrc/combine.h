@@ -6,11 +6,30 @@
 // The expert outputs sit in `nsplit` partial planes (the streaming FFN's
 // m-slices; 1 for the tiled FFN) of [T*K, l] each.  `gated`: multiply by the
 // gate here (streaming FFN) or not (the tiled FFN already did).
+// Zero-computation experts (ids >= n_ffn) have no expert output.  Their
+// slots are the last ones (ids sort after the FFN experts), so a rank is
+// theirs when its slot is at or past offsets[n_ffn]; such ranks read the
+// planes' zero row (the loads of all ranks stay unconditional), and a second
+// pass over just those ranks adds their own g * y: nothing for a zero expert,
+// g * z for a copy expert, g * its vector for a constant expert (MoE++'s
+// three kinds: 10100.com article, section 3.2).
 #pragma once
 
 #include "layer.h"
 
 namespace lmoe {
+
+// g * y of zero-computation expert q (counted from id n_ffn) for the VPC
+// columns from c0 of token t, added to acc.
+template <class E, int VPC>
+__device__ inline void zc_add(const LayerArgs& a, int q, int t, int c0, float g, float* acc) {
+    if (q < a.n_zero) return;   // zero expert: y = 0
+    q -= a.n_zero;
+    const E* y = q < a.n_copy ? static_cast<const E*>(a.z) + (size_t)t * a.l + c0                 // copy: z
+                              : static_cast<const E*>(a.zc) + (size_t)(q - a.n_copy) * a.l + c0;  // constant
+#pragma unroll
+    for (int i = 0; i < VPC; ++i) acc[i] = fmaf(g, to_f32(y[i]), acc[i]);
+}
 
 // Work item = (token t, 16-byte column chunk q of its l values): VPC = 8
 // values for bf16 expert outputs, 4 for fp32.  A workgroup of 256 threads
@@ -30,7 +49,7 @@ __global__ __launch_bounds__(256) void combine_kernel(LayerArgs a, int nsplit, i
     const int g = (int)threadIdx.x / IPB;
     const bool live = item < a.T * cpt;
     const int t = live ? item / cpt : 0, c0 = (live ? item % cpt : 0) * VPC;
-    const size_t plane = (size_t)a.T * a.K * a.l;
+    const size_t plane = y_plane_elems(a);
     const YT* Y = static_cast<const YT*>(a.ybuf) + c0;
     float acc[VPC];
 #pragma unroll
@@ -38,9 +57,15 @@ __global__ __launch_bounds__(256) void combine_kernel(LayerArgs a, int nsplit, i
     if (live) {
         const int* so = a.slot_of + (size_t)t * a.K;
         const float* gt = a.gates + (size_t)t * a.K;
+        const int nf = a.N > a.n_ffn ? a.offsets[a.n_ffn] : INT_MAX;   // FFN slots: [0, nf)
+        const size_t zrow = (size_t)a.T * a.K;
+        unsigned long long zranks = 0;   // ranks of zero-computation experts (K <= 64)
 #pragma unroll 4
         for (int k = g; k < a.K; k += RS) {
-            const YT* yp = Y + (size_t)so[k] * a.l;
+            const int sl = so[k];
+            const bool z = sl >= nf;
+            zranks |= (unsigned long long)z << k;
+            const YT* yp = Y + (z ? zrow : (size_t)sl) * a.l;
             uint4 raw = ldg16(yp);
             float part[VPC];
             if constexpr (VPC == 8) {
@@ -66,6 +91,12 @@ __global__ __launch_bounds__(256) void combine_kernel(LayerArgs a, int nsplit, i
             const float gk = gated ? gt[k] : 1.0f;
 #pragma unroll
             for (int i = 0; i < VPC; ++i) acc[i] = fmaf(gk, part[i], acc[i]);
+        }
+        const int* idk = a.ids + (size_t)t * a.K;
+        while (zranks) {
+            const int k = __builtin_ctzll(zranks);
+            zranks &= zranks - 1;
+            zc_add<E, VPC>(a, idk[k] - a.n_ffn, t, c0, gt[k], acc);
         }
     }
     if constexpr (RS > 1) {

@@ -86,6 +86,7 @@ struct Plan {
     int tile_rows = G2Small::BM;
     bool ffn_large = false;       // tiled FFN on G2Large
     bool fp8 = false;             // FP8 E4M3 expert weights
+    int nr = 0;                   // routed ids: FFN and zero-computation experts
     int nblk = 1;                 // dispatch blocks
     int ms = 128;                 // streaming FFN m-slice
     int nsplit = 1;               // streaming FFN partial planes
@@ -112,12 +113,15 @@ Plan make_plan(const lmoe_dims* dm, int32_t K) {
         p.status = fail(LMOE_EINVAL, "d=%d, l=%d, m=%d must be positive multiples of 64", d.d, d.l, d.m);
         return p;
     }
-    if (d.N < 1 || d.N > kMaxExperts) {
-        p.status = fail(LMOE_EINVAL, "N=%d must be in [1, %d]", d.N, kMaxExperts);
+    if (d.N < 1 || d.n_zero < 0 || d.n_copy < 0 || d.n_const < 0 ||
+        (long long)d.N + d.n_zero + d.n_copy + d.n_const > kMaxExperts) {
+        p.status = fail(LMOE_EINVAL, "N=%d >= 1 and n_zero=%d, n_copy=%d, n_const=%d >= 0 with at most %d ids in all",
+                        d.N, d.n_zero, d.n_copy, d.n_const, kMaxExperts);
         return p;
     }
-    if (K < 1 || K > d.N || K > kMaxK) {
-        p.status = fail(LMOE_EINVAL, "K=%d must be in [1, min(N=%d, %d)]", K, d.N, kMaxK);
+    p.nr = d.N + d.n_zero + d.n_copy + d.n_const;
+    if (K < 1 || K > p.nr || K > kMaxK) {
+        p.status = fail(LMOE_EINVAL, "K=%d must be in [1, min(Nr=%d, %d)]", K, p.nr, kMaxK);
         return p;
     }
     if ((long long)d.T * K > (1ll << 30)) {
@@ -176,32 +180,32 @@ Plan make_plan(const lmoe_dims* dm, int32_t K) {
         return at;
     };
     p.z = take((size_t)d.T * d.l * p.es);
-    p.logits = take((size_t)d.T * d.N * 4);
+    p.logits = take((size_t)d.T * p.nr * 4);
     p.ids = take((size_t)TK * 4);
     p.gates = take((size_t)TK * 4);
-    p.counts = take((size_t)d.N * 4);
-    p.offsets = take((size_t)(d.N + 1) * 4);
+    p.counts = take((size_t)p.nr * 4);
+    p.offsets = take((size_t)(p.nr + 1) * 4);
     p.perm = take((size_t)TK * 4);
     p.slot_of = take((size_t)TK * 4);
-    p.blk_counts = take((size_t)p.nblk * d.N * 4);
-    p.blk_offsets = take((size_t)p.nblk * d.N * 4);
+    p.blk_counts = take((size_t)p.nblk * p.nr * 4);
+    p.blk_offsets = take((size_t)p.nblk * p.nr * 4);
     p.tiles = take((size_t)p.max_tiles * 8);
     p.n_tiles = take(4);
     p.active = take((size_t)d.N * 4);
     p.n_active = take(4);
     if (p.path == LMOE_PATH_STREAM) {
         p.abuf = take(0);
-        p.ybuf = take((size_t)p.nsplit * TK * d.l * 4);
+        p.ybuf = take((size_t)p.nsplit * (TK + 1) * d.l * 4);   // + the zero row of each plane
     } else {
         p.abuf = take((size_t)TK * d.m * p.es);
-        p.ybuf = take((size_t)TK * d.l * p.es);
+        p.ybuf = take((size_t)(TK + 1) * d.l * p.es);
     }
     p.s = take((size_t)d.T * d.l * p.es);
     // partial tiles of the split projection, for either mode (standard mode,
     // W_down == NULL, is only known at the call: N instead of l + N columns)
     size_t part_bytes = 0;
     if (p.skinny)
-        part_bytes = std::max(proj_part_floats(d.l + d.N, d.T), proj_part_floats(d.N, d.T)) * d.T * 4;
+        part_bytes = std::max(proj_part_floats(d.l + p.nr, d.T), proj_part_floats(p.nr, d.T)) * d.T * 4;
     p.part = take(part_bytes);
     p.a_s = take((size_t)d.T * d.m_shared * p.es);
     p.y_s = take(d.m_shared > 0 ? (size_t)d.T * d.d * 4 : 0);
@@ -309,12 +313,17 @@ void launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* events
             else
                 topk_kernel<NPL><<<dim3(cdiv(a.T, 4)), b256, 0, st>>>(a);
         };
+        // logits per lane: the smallest tier that holds the routed ids
         if (a.N <= 256)
             launch_topk(std::integral_constant<int, 4>{});
         else if (a.N <= 512)
             launch_topk(std::integral_constant<int, 8>{});
+        else if (a.N <= 768)
+            launch_topk(std::integral_constant<int, 12>{});
         else if (a.N <= 1024)
             launch_topk(std::integral_constant<int, 16>{});
+        else if (a.N <= 1536)
+            launch_topk(std::integral_constant<int, 24>{});
         else
             launch_topk(std::integral_constant<int, 32>{});
     }
@@ -333,7 +342,7 @@ void launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* events
     const unsigned mt = (unsigned)p.max_tiles;
     if constexpr (sizeof(E) == 2) {
         if (p.path == LMOE_PATH_STREAM) {
-            const dim3 g(p.nsplit, a.N);
+            const dim3 g(p.nsplit, a.n_ffn);
             if (p.fp8)
                 p.ms == 128 ? ffn_stream_kernel<128, true><<<g, b256, 0, st>>>(a)
                             : ffn_stream_kernel<64, true><<<g, b256, 0, st>>>(a);
@@ -431,7 +440,7 @@ int latentmoe_workspace_layout(const lmoe_dims* dims, int32_t K, lmoe_ws_layout*
 
 static int forward_impl(const void* x, const void* W_down, const void* W_router, const void* W1, const void* W2,
                         const void* W_up, const void* W_s1, const void* W_s2, const float* w1s, const float* w2s,
-                        int32_t K, void* out, const lmoe_dims* dims, const float* router_bias,
+                        const void* zc_const, int32_t K, void* out, const lmoe_dims* dims, const float* router_bias,
                         int32_t* topk_ids, float* topk_gates, void* workspace, size_t workspace_bytes,
                         void* stream, void* const* events) {
     g_last_error.clear();
@@ -452,6 +461,8 @@ static int forward_impl(const void* x, const void* W_down, const void* W_router,
     if ((w1s && (reinterpret_cast<uintptr_t>(w1s) & 15) != 0) ||
         (w2s && (reinterpret_cast<uintptr_t>(w2s) & 15) != 0))
         return fail(LMOE_EINVAL, "W1_scale and W2_scale must be 16-byte aligned");
+    if ((d.n_const > 0) != (zc_const != nullptr))
+        return fail(LMOE_EINVAL, "zc_const must be set when n_const > 0 and NULL otherwise (n_const=%d)", d.n_const);
     if (!workspace) return fail(LMOE_EWORKSPACE, "workspace is NULL");
     if (workspace_bytes < p.total)
         return fail(LMOE_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, p.total);
@@ -460,7 +471,7 @@ static int forward_impl(const void* x, const void* W_down, const void* W_router,
     if (overlaps(out, xbytes, workspace, p.total)) return fail(LMOE_EINVAL, "out must not alias the workspace");
     if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
         return fail(LMOE_EINVAL, "workspace must be 256-byte aligned");
-    const void* ptrs[] = {x, W_down, W_router, W1, W2, W_up, W_s1, W_s2, out};
+    const void* ptrs[] = {x, W_down, W_router, W1, W2, W_up, W_s1, W_s2, zc_const, out};
     for (const void* q : ptrs)
         if (q && (reinterpret_cast<uintptr_t>(q) & 15) != 0)
             return fail(LMOE_EINVAL, "tensor pointers must be 16-byte aligned");
@@ -484,7 +495,11 @@ static int forward_impl(const void* x, const void* W_down, const void* W_router,
     a.T = d.T;
     a.d = d.d;
     a.l = d.l;
-    a.N = d.N;
+    a.N = p.nr;
+    a.n_ffn = d.N;
+    a.n_zero = d.n_zero;
+    a.n_copy = d.n_copy;
+    a.zc = zc_const;
     a.m = d.m;
     a.K = K;
     a.standard = standard ? 1 : 0;
@@ -510,6 +525,8 @@ static int forward_impl(const void* x, const void* W_down, const void* W_router,
     a.a_s = d.m_shared > 0 ? ws + p.a_s : nullptr;
     a.y_s = d.m_shared > 0 ? reinterpret_cast<float*>(ws + p.y_s) : nullptr;
     a.tile_rows = p.tile_rows;
+    a.y_planes = p.nsplit;
+    a.y_row_bytes = d.l * (p.path == LMOE_PATH_STREAM ? 4 : (int)p.es);
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
@@ -522,6 +539,16 @@ static int forward_impl(const void* x, const void* W_down, const void* W_router,
     return LMOE_OK;
 }
 
+// The entry points other than latentmoe_forward_ex take no FP8 experts and
+// no zero-computation experts.
+static int plain_options_only(const lmoe_dims* dims) {
+    if (dims && dims->expert_format != LMOE_EXPERTS_DENSE)
+        return fail(LMOE_EINVAL, "FP8 experts go through latentmoe_forward_ex");
+    if (dims && (dims->n_zero | dims->n_copy | dims->n_const) != 0)
+        return fail(LMOE_EINVAL, "zero-computation experts go through latentmoe_forward_ex");
+    return LMOE_OK;
+}
+
 int latentmoe_forward(const void* x, const void* W_down, const void* W_router, const void* W1, const void* W2,
                       const void* W_up, int32_t K, void* out, const lmoe_dims* dims, const float* router_bias,
                       int32_t* topk_ids, float* topk_gates, void* workspace, size_t workspace_bytes,
@@ -529,9 +556,8 @@ int latentmoe_forward(const void* x, const void* W_down, const void* W_router, c
     if (dims && dims->m_shared != 0)
         return fail(LMOE_EINVAL, "m_shared=%d: a shared expert goes through latentmoe_forward_shared",
                     dims->m_shared);
-    if (dims && dims->expert_format != LMOE_EXPERTS_DENSE)
-        return fail(LMOE_EINVAL, "FP8 experts go through latentmoe_forward_ex");
-    return forward_impl(x, W_down, W_router, W1, W2, W_up, nullptr, nullptr, nullptr, nullptr, K, out, dims,
+    if (const int rc = plain_options_only(dims)) return rc;
+    return forward_impl(x, W_down, W_router, W1, W2, W_up, nullptr, nullptr, nullptr, nullptr, nullptr, K, out, dims,
                         router_bias, topk_ids, topk_gates, workspace, workspace_bytes, stream, nullptr);
 }
 
@@ -542,9 +568,8 @@ int latentmoe_forward_shared(const void* x, const void* W_down, const void* W_ro
                              void* stream) {
     if (dims && dims->m_shared <= 0)
         return fail(LMOE_EINVAL, "latentmoe_forward_shared needs m_shared > 0 (got %d)", dims->m_shared);
-    if (dims && dims->expert_format != LMOE_EXPERTS_DENSE)
-        return fail(LMOE_EINVAL, "FP8 experts go through latentmoe_forward_ex");
-    return forward_impl(x, W_down, W_router, W1, W2, W_up, W_shared1, W_shared2, nullptr, nullptr, K, out, dims,
+    if (const int rc = plain_options_only(dims)) return rc;
+    return forward_impl(x, W_down, W_router, W1, W2, W_up, W_shared1, W_shared2, nullptr, nullptr, nullptr, K, out, dims,
                         router_bias, topk_ids, topk_gates, workspace, workspace_bytes, stream, nullptr);
 }
 
@@ -554,16 +579,15 @@ int latentmoe_forward_timed(const void* x, const void* W_down, const void* W_rou
                             int32_t* topk_ids, float* topk_gates, void* workspace, size_t workspace_bytes,
                             void* stream, void* const* events) {
     if (!events) return fail(LMOE_EINVAL, "events is NULL");
-    if (dims && dims->expert_format != LMOE_EXPERTS_DENSE)
-        return fail(LMOE_EINVAL, "FP8 experts go through latentmoe_forward_ex");
-    return forward_impl(x, W_down, W_router, W1, W2, W_up, W_shared1, W_shared2, nullptr, nullptr, K, out, dims,
+    if (const int rc = plain_options_only(dims)) return rc;
+    return forward_impl(x, W_down, W_router, W1, W2, W_up, W_shared1, W_shared2, nullptr, nullptr, nullptr, K, out, dims,
                         router_bias, topk_ids, topk_gates, workspace, workspace_bytes, stream, events);
 }
 
 int latentmoe_forward_ex(const lmoe_args* g, int32_t K, const lmoe_dims* dims) {
     if (!g) return fail(LMOE_EINVAL, "args is NULL");
     return forward_impl(g->x, g->W_down, g->W_router, g->W1, g->W2, g->W_up, g->W_shared1, g->W_shared2,
-                        g->W1_scale, g->W2_scale, K, g->out, dims, g->router_bias, g->topk_ids, g->topk_gates,
+                        g->W1_scale, g->W2_scale, g->zc_const, K, g->out, dims, g->router_bias, g->topk_ids, g->topk_gates,
                         g->workspace, g->workspace_bytes, g->stream, g->events);
 }
 

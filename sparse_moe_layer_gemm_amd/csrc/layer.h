@@ -14,17 +14,20 @@ struct LayerArgs {
     // caller tensors
     const void* x;         // [T, d]
     const void* W_down;    // [l, d] or NULL (standard mode)
-    const void* W_router;  // [N, d]
+    const void* W_router;  // [N, d]: one row per routed id
     const void* W1;        // [N, m, l]
     const void* W2;        // [N, l, m]
     const void* W_up;      // [d, l] or NULL (standard mode)
     const void* W_s1;      // [m_s, d] shared expert, or NULL
     const void* W_s2;      // [d, m_s]
     const float* bias;     // [N] or NULL
+    const void* zc;        // [n_const, l] constant experts' vectors, or NULL
     const float* w1s;      // [N, m] row scales of FP8 W1 (FP8 experts only)
     const float* w2s;      // [N, l] row scales of FP8 W2
     void* out;             // [T, d]
-    int T, d, l, N, m, K;
+    int T, d, l, N, m, K;  // N: routed ids (FFN experts, then zero-computation experts)
+    int n_ffn;             // FFN experts: ids < n_ffn have W1 / W2
+    int n_zero, n_copy;    // zero experts, then copy experts, then constant experts
     int standard;
     int m_s;               // shared expert width (0: none)
     // workspace
@@ -50,7 +53,14 @@ struct LayerArgs {
     void* a_s;             // [T, m_s] relu(W_s1 x)^2 (shared expert)
     float* y_s;            // [T, d] W_s2 a_s, float32 (shared expert)
     int tile_rows;         // rows per grouped-GEMM tile
+    int y_planes;          // partial planes of ybuf (the streaming FFN's m-slices; 1 for the tiled FFN)
+    int y_row_bytes;       // bytes of one ybuf row (l elements)
 };
+
+// Elements of one ybuf plane: a row per slot and one more (row T*K), kept at
+// zero when there are zero-computation experts, whose ranks read it in place
+// of an expert output.
+__device__ inline size_t y_plane_elems(const LayerArgs& a) { return ((size_t)a.T * a.K + 1) * a.l; }
 
 // ---------------------------------------------------------------------------
 // z = W_down x and logits = W_router x (+ bias), one product over the

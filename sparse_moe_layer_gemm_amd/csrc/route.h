@@ -222,37 +222,50 @@ __device__ inline int block_excl_scan(int* v, int n, int* wsum) {
     return total;
 }
 
-// From per-expert counts in LDS `cnt`: counts, offsets, the active-expert
-// list and the grouped-GEMM tile list in global memory; the exclusive offsets
-// are also left in LDS `off`.  tmp, wsum: LDS scratch.
+// From per-id counts in LDS `cnt`: counts, offsets, the active-expert list
+// and the grouped-GEMM tile list in global memory; the exclusive offsets are
+// also left in LDS `off`.  Only FFN experts (ids < n_ffn) are active or get
+// tiles: the zero-computation experts' slots (the last ones) are never run.
+// tmp, wsum: LDS scratch.
 __device__ inline void finish_scan(const LayerArgs& a, const int* cnt, int* off, int* tmp, int* wsum) {
     const int N = a.N;
     for (int e = threadIdx.x; e < N; e += blockDim.x) {
         const int c = cnt[e];
         a.counts[e] = c;
         off[e] = c;
-        tmp[e] = c > 0 ? 1 : 0;
+        tmp[e] = (c > 0 && e < a.n_ffn) ? 1 : 0;
     }
     __syncthreads();
     const int total = block_excl_scan(off, N, wsum);
     const int n_act = block_excl_scan(tmp, N, wsum);
     for (int e = threadIdx.x; e < N; e += blockDim.x) {
         a.offsets[e] = off[e];
-        if (cnt[e] > 0) a.active[tmp[e]] = e;
+        if (cnt[e] > 0 && e < a.n_ffn) a.active[tmp[e]] = e;
     }
     if (threadIdx.x == 0) {
         a.offsets[N] = total;
         *a.n_active = n_act;
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < N; e += blockDim.x) tmp[e] = cdiv(cnt[e], a.tile_rows);
+    for (int e = threadIdx.x; e < N; e += blockDim.x) tmp[e] = e < a.n_ffn ? cdiv(cnt[e], a.tile_rows) : 0;
     __syncthreads();
     const int ntiles = block_excl_scan(tmp, N, wsum);
     for (int e = threadIdx.x; e < N; e += blockDim.x) {
-        const int nt = cdiv(cnt[e], a.tile_rows), base = tmp[e], o = off[e];
+        const int nt = e < a.n_ffn ? cdiv(cnt[e], a.tile_rows) : 0, base = tmp[e], o = off[e];
         for (int i = 0; i < nt; ++i) a.tiles[base + i] = make_int2(e, o + i * a.tile_rows);
     }
     if (threadIdx.x == 0) *a.n_tiles = ntiles;
+    // the zero row of every expert-output plane (row T*K), read by the
+    // combine for zero-computation experts
+    if (a.N > a.n_ffn) {
+        const int per_row = a.y_row_bytes / 16;
+        const size_t rows = (size_t)a.T * a.K;
+        for (int i = threadIdx.x; i < a.y_planes * per_row; i += blockDim.x) {
+            const size_t p = (size_t)(i / per_row);
+            char* row = static_cast<char*>(a.ybuf) + (p * (rows + 1) + rows) * a.y_row_bytes;
+            reinterpret_cast<uint4*>(row)[i % per_row] = kZero16;
+        }
+    }
     __syncthreads();
 }
 

@@ -196,7 +196,7 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(LayerArgs a) {
     const WT* W1e = static_cast<const WT*>(a.W1) + (size_t)e * m * l;
     const WT* W2e = static_cast<const WT*>(a.W2) + (size_t)e * l * m;
     const bf16* Z = static_cast<const bf16*>(a.z);
-    float* Yp = static_cast<float*>(a.ybuf) + (size_t)blockIdx.x * a.T * a.K * l;
+    float* Yp = static_cast<float*>(a.ybuf) + (size_t)blockIdx.x * y_plane_elems(a);
 
     constexpr int NB = MS / 16;        // 16-column blocks of the slice
     constexpr int NBW = NB / 4;        // per wave

@@ -27,11 +27,16 @@ operands of every product):
   W_s1     [m_s, d], W_s2 [d, m_s]   shared expert (the *_shared workloads)
   FP8 experts (the *_fp8 workloads): W1, W2 as uint8 E4M3 codes in the same
   layout, W1_scale [N, m] and W2_scale [N, l] float32 row scales
+  zero-computation experts (the *_zc workloads): W_router (and bias) get
+  n_zero + n_copy + n_const more rows; zc_const [n_const, l]
 
 Recipe: one CPU torch.Generator seeded with `seed`; draws in the order x,
 W_down, W_router, W1 (one draw of [m, l] per expert, expert 0 first), W2 (one
 [l, m] draw per expert), W_up, bias, W_s1, W_s2 (the last two only for a
-shared expert, so the other arrays are the same with or without one).
+shared expert, so the other arrays are the same with or without one), then
+for zero-computation experts their router rows, their bias entries and the
+constant vectors (zc_const ~ N(0, 1), the scale of z), appended so that the
+rest of the layer is the same with or without them.
 Every draw is float32 N(0, 1); weights
 are multiplied by 1/sqrt(fan_in) in float32; for bf16 workloads every array
 except the bias is then rounded to bfloat16 (round-to-nearest-even).
@@ -65,6 +70,13 @@ class Workload:
     bias: bool = False      # fixed per-expert logit bias ~ N(0, 1)
     m_shared: int = 0       # shared expert width (0: none)
     experts: str = "dense"  # routed expert weights: "dense" (the layer's dtype) or "fp8" (E4M3 + row scales)
+    n_zero: int = 0         # zero-computation experts (ids N ...): zero,
+    n_copy: int = 0         # copy
+    n_const: int = 0        # and constant experts
+
+    @property
+    def n_zc(self) -> int:
+        return self.n_zero + self.n_copy + self.n_const
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -101,6 +113,14 @@ WORKLOADS: Dict[str, Workload] = {
                            experts="fp8"),
     "prefill_fp8": Workload("prefill_fp8", T=16384, d=4096, l=1024, N=512, K=22, m=768, dtype="bf16",
                             experts="fp8"),
+    # The decode and prefill layers with 64 zero-computation experts besides
+    # the 512 FFN experts (32 zero, 16 copy, 16 constant): about 11 % of the
+    # top-22 picks skip the FFN (the pages report LongCat's average activated
+    # parameters ~10 % below the maximum; the split is a choice).
+    "decode_zc": Workload("decode_zc", T=32, d=4096, l=1024, N=512, K=22, m=768, dtype="bf16",
+                          n_zero=32, n_copy=16, n_const=16),
+    "prefill_zc": Workload("prefill_zc", T=16384, d=4096, l=1024, N=512, K=22, m=768, dtype="bf16",
+                           n_zero=32, n_copy=16, n_const=16),
 }
 
 
@@ -126,7 +146,9 @@ def make_inputs(w: Workload, seed: int = 0, *, x_only_seed: Optional[int] = None
     """Draw the inputs of workload `w` on the CPU.
 
     Returns a dict with keys x, W_down, W_router, W1, W2, W_up, bias (None
-    where the workload has no such array), and W_s1, W_s2 for a shared expert.  Arrays are contiguous CPU tensors
+    where the workload has no such array), W_s1, W_s2 for a shared expert,
+    W1_scale, W2_scale for FP8 experts and zc_const for zero-computation
+    experts.  Arrays are contiguous CPU tensors
     in the workload's storage dtype; bias stays float32.
     """
     gen = torch.Generator(device="cpu")
@@ -162,6 +184,12 @@ def make_inputs(w: Workload, seed: int = 0, *, x_only_seed: Optional[int] = None
     if w.m_shared > 0:
         out["W_s1"] = _draw(gen, (w.m_shared, w.d), 1.0 / math.sqrt(w.d)).to(dt)
         out["W_s2"] = _draw(gen, (w.d, w.m_shared), 1.0 / math.sqrt(w.m_shared)).to(dt)
+    if w.n_zc > 0:
+        zr = _draw(gen, (w.n_zc, w.d), 1.0 / math.sqrt(w.d)).to(dt)
+        out["W_router"] = torch.cat([out["W_router"], zr]).contiguous()
+        if w.bias:
+            out["bias"] = torch.cat([out["bias"], _draw(gen, (w.n_zc,), None)]).contiguous()
+        out["zc_const"] = _draw(gen, (w.n_const, w.l), None).to(dt) if w.n_const > 0 else None
     if x_only_seed is not None:
         g2 = torch.Generator(device="cpu")
         g2.manual_seed(x_only_seed)

@@ -51,11 +51,12 @@ def oracle_arrays(inp):
     return {k: (None if v is None else (v.numpy() if k == "bias" else as_numpy_bits(v))) for k, v in inp.items()}
 
 
-def run_oracle(arr, K, sel=None, forced=None):
+def run_oracle(arr, K, sel=None, forced=None, n_zero=0, n_copy=0):
     return O.forward(arr["x"], arr["W_down"], arr["W_router"], arr["W1"], arr["W2"], arr["W_up"], K,
                      bias=arr["bias"], standard=arr["W_down"] is None, sel=sel, forced_ids=forced,
                      W_s1=arr.get("W_s1"), W_s2=arr.get("W_s2"),
-                     W1_scale=arr.get("W1_scale"), W2_scale=arr.get("W2_scale"))
+                     W1_scale=arr.get("W1_scale"), W2_scale=arr.get("W2_scale"),
+                     n_zero=n_zero, n_copy=n_copy, zc_const=arr.get("zc_const"))
 
 
 def expected_dispatch(ids: np.ndarray, N: int):
@@ -84,18 +85,19 @@ def read_dispatch(ws: torch.Tensor, dims, K: int, T: int, N: int):
 def compare(w: Workload, inp, K: int, path: int = B.LMOE_PATH_AUTO, sample: Optional[Sequence[int]] = None,
             check_dispatch: bool = True, tag: str = "") -> dict:
     """Run GPU and oracle on `inp` (CPU tensors) and assert parity."""
-    T, N = w.T, w.N
-    log(f"[parity] {tag or w.name}: T={T} d={w.d} l={w.l} N={N} K={K} m={w.m} {w.dtype} path={path}")
+    T, N = w.T, w.N + w.n_zc   # N: routed ids
+    zc = dict(n_zero=w.n_zero, n_copy=w.n_copy)
+    log(f"[parity] {tag or w.name}: T={T} d={w.d} l={w.l} N={w.N}+{w.n_zc} K={K} m={w.m} {w.dtype} path={path}")
     dinp = to_device(inp)
-    dims = B.dims_for(dinp, K, path)
-    out, ids, gates, ws = B.forward(dinp, K, path=path, routing=True)
+    dims = B.dims_for(dinp, K, path, **zc)
+    out, ids, gates, ws = B.forward(dinp, K, path=path, routing=True, **zc)
     torch.cuda.synchronize()
     out_g = out.float().cpu().numpy().astype(np.float64)
     ids_g = ids.cpu().numpy()
     gates_g = gates.cpu().numpy().astype(np.float64)
     arr = oracle_arrays(inp)
     sel = np.arange(T, dtype=np.int32) if sample is None else np.asarray(sample, np.int32)
-    ref = run_oracle(arr, K, sel=sel)
+    ref = run_oracle(arr, K, sel=sel, **zc)
 
     # ids: sets equal outside the tie band
     near = ref["gap"] < TIE_BAND
@@ -110,7 +112,7 @@ def compare(w: Workload, inp, K: int, path: int = B.LMOE_PATH_AUTO, sample: Opti
     ref_gates = {}
     if mism:
         mq = np.asarray(mism)
-        fr = run_oracle(arr, K, sel=sel[mq], forced=ids_g[sel[mq]])
+        fr = run_oracle(arr, K, sel=sel[mq], forced=ids_g[sel[mq]], **zc)
         ref_out[mq] = fr["out"]
         for i, q in enumerate(mq):
             ref_gates[q] = dict(zip(fr["ids"][i].tolist(), fr["gates"][i].tolist()))
@@ -154,7 +156,7 @@ def compare(w: Workload, inp, K: int, path: int = B.LMOE_PATH_AUTO, sample: Opti
         assert np.array_equal(offsets, eo), "offsets"
         assert np.array_equal(perm, ep), "perm"
         assert np.array_equal(slot_of, es), "slot_of"
-        assert n_active == int((ec > 0).sum())
+        assert n_active == int((ec[:w.N] > 0).sum())   # FFN experts only
     rep["out"] = out
     rep["ids"] = ids_g
     return rep

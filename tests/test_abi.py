@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def dims_of(w, path=B.LMOE_PATH_AUTO):
     fmt = B.LMOE_EXPERTS_FP8_E4M3 if w.experts == "fp8" else B.LMOE_EXPERTS_DENSE
-    return B.make_dims(w.T, w.d, w.l, w.N, w.m, w.dtype, path, w.m_shared, fmt)
+    return B.make_dims(w.T, w.d, w.l, w.N, w.m, w.dtype, path, w.m_shared, fmt, w.n_zero, w.n_copy, w.n_const)
 
 
 @pytest.mark.parametrize("name", sorted(WORKLOADS))
@@ -187,6 +187,34 @@ def test_fp8_expert_argument_checks(lib):
     assert call_ex(bad, w.K) == B.LMOE_EINVAL
     assert B.lib().latentmoe_forward_ex(None, w.K, ctypes.byref(d)) == B.LMOE_EINVAL
     assert call_ex(d, w.K, workspace_bytes=100) == B.LMOE_EWORKSPACE
+
+
+def test_zero_computation_argument_checks(lib):
+    w = WORKLOADS["decode_zc"]
+    d = dims_of(w)
+    ZC = FAKE + (12 << 30)
+    # the dispatch counts cover every routed id
+    lay = B.latentmoe_workspace_layout(d, w.K)
+    assert lay.offsets - lay.counts >= 4 * (w.N + w.n_zc)
+    P = ctypes.c_void_p
+    rc = B.lib().latentmoe_forward(P(FAKE), P(FAKE + (1 << 30)), P(FAKE + (2 << 30)), P(FAKE + (3 << 30)),
+                                   P(FAKE + (4 << 30)), P(FAKE + (5 << 30)), w.K, P(FAKE + (6 << 30)),
+                                   ctypes.byref(d), None, None, None, P(FAKE + (7 << 30)),
+                                   ctypes.c_size_t(B.latentmoe_workspace_bytes(d, w.K)), None)
+    assert rc == B.LMOE_EINVAL and "latentmoe_forward_ex" in B.latentmoe_last_error()
+    nofp8 = dict(W1_scale=None, W2_scale=None)
+    assert call_ex(d, w.K, **nofp8) == B.LMOE_EINVAL                       # constants need zc_const
+    assert call_ex(d, w.K, zc_const=ZC + 8, **nofp8) == B.LMOE_EINVAL      # misaligned
+    no_const = dims_of(w.replace(n_const=0))
+    assert call_ex(no_const, w.K, zc_const=ZC, **nofp8) == B.LMOE_EINVAL   # zc_const without constants
+    for bad in (dict(n_zero=-1), dict(n_copy=-2), dict(n_const=-1), dict(n_zero=2048 - 512)):
+        bd = dims_of(w.replace(**bad))
+        assert B.latentmoe_workspace_bytes(bd, w.K) == 0
+    # K may exceed N (zero-computation ids count) but not N + n_zc
+    small = w.replace(N=8, K=20, n_zero=6, n_copy=4, n_const=2)
+    assert B.latentmoe_workspace_bytes(dims_of(small), 20) > 0
+    assert B.latentmoe_workspace_bytes(dims_of(small), 21) == 0
+    assert call_ex(d, w.K, zc_const=ZC, workspace_bytes=64, **nofp8) == B.LMOE_EWORKSPACE
 
 
 def test_status_strings(lib):

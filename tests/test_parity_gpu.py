@@ -214,6 +214,98 @@ def test_fp8_layer_is_the_bf16_layer_on_decoded_weights(path):
     assert torch.equal(a, b)
 
 
+# --- zero-computation experts (zero, copy, constant) --------------------------
+
+def zc_forward(w, inp, path, **kw):
+    return B.forward(inp, w.K, path=path, n_zero=w.n_zero, n_copy=w.n_copy, **kw)
+
+
+@pytest.mark.parametrize("path", [B.LMOE_PATH_AUTO, TL])
+def test_decode_zc(path):
+    w = WORKLOADS["decode_zc"]
+    P.compare(w, P.gen(w, 0), w.K, path=path, tag=f"decode_zc/path{path}")
+
+
+def test_prefill_zc_sampled():
+    w = WORKLOADS["prefill_zc"]
+    P.compare(w, P.gen(w, 0), w.K, sample=sample_tokens(w.T, 96))
+
+
+ZC_SHAPES = [
+    Workload("zc_latent", T=300, d=256, l=64, N=16, K=4, m=128, dtype="bf16", n_zero=4, n_copy=2, n_const=2),
+    Workload("zc_standard", T=90, d=256, l=256, N=12, K=3, m=128, dtype="bf16", standard=True,
+             n_zero=2, n_copy=2, n_const=2),
+    Workload("zc_f32", T=70, d=128, l=64, N=8, K=3, m=64, dtype="f32", n_zero=1, n_copy=1, n_const=1),
+    Workload("zc_every_id", T=20, d=256, l=64, N=6, K=10, m=64, dtype="bf16", n_zero=2, n_copy=1, n_const=1),
+    Workload("zc_zero_only", T=200, d=256, l=64, N=16, K=6, m=128, dtype="bf16", n_zero=16),
+    Workload("zc_one_token", T=1, d=256, l=64, N=16, K=5, m=128, dtype="bf16", n_zero=2, n_copy=2, n_const=2),
+    Workload("zc_fp8_shared_bias", T=150, d=256, l=64, N=16, K=4, m=128, dtype="bf16", bias=True, m_shared=64,
+             experts="fp8", n_zero=3, n_copy=3, n_const=3),
+]
+
+
+@pytest.mark.parametrize("w", ZC_SHAPES, ids=lambda w: w.name)
+@pytest.mark.parametrize("path", [B.LMOE_PATH_AUTO, S, TL])
+def test_zc_shapes(w, path):
+    if w.dtype == "f32" and path == S:
+        pytest.skip("the streaming FFN is bf16 only")
+    P.compare(w, make_inputs(w, 14), w.K, path=path, tag=f"{w.name}/path{path}")
+
+
+def one_winner(w, e, seed):
+    """Inputs of w (K = 1) whose router bias makes routed id e win for every token."""
+    inp = make_inputs(w.replace(bias=True), seed)
+    bias = torch.full_like(inp["bias"], -40.0)
+    bias[e] = 40.0
+    inp["bias"] = bias
+    return P.to_device(inp)
+
+
+@pytest.mark.parametrize("path", [S, TL])
+@pytest.mark.parametrize("standard", [False, True])
+def test_zero_expert_gives_x(path, standard):
+    w = Workload("zc_k1", T=80, d=256, l=256 if standard else 64, N=16, K=1, m=128, dtype="bf16",
+                 standard=standard, n_zero=2, n_copy=2, n_const=2)
+    inp = one_winner(w, w.N + 1, 15)
+    out, ids, gates, _ = zc_forward(w, inp, path, routing=True)
+    torch.cuda.synchronize()
+    assert torch.all(ids == w.N + 1) and torch.all(gates == 1.0)
+    assert torch.equal(out, inp["x"])
+
+
+@pytest.mark.parametrize("path", [S, TL])
+def test_standard_copy_and_constant_experts(path):
+    """Standard mode, K = 1: a copy expert gives 2x, constant expert q gives
+    x + c_q, each rounded once."""
+    w = Workload("zc_k1_std", T=80, d=256, l=256, N=16, K=1, m=128, dtype="bf16", standard=True,
+                 n_zero=1, n_copy=1, n_const=3)
+    inp = one_winner(w, w.N + 1, 16)
+    out = zc_forward(w, inp, path)
+    torch.cuda.synchronize()
+    assert torch.equal(out, (2.0 * inp["x"].float()).to(torch.bfloat16))
+    inp = one_winner(w, w.N + 3, 16)
+    out = zc_forward(w, inp, path)
+    torch.cuda.synchronize()
+    want = (inp["x"].float() + inp["zc_const"][1].float()).to(torch.bfloat16)
+    assert torch.equal(out, want)
+
+
+def test_losing_zc_experts_change_nothing():
+    """Zero-computation experts whose logits never win: bit-identical to the
+    layer without them (gates depend only on the kept logits)."""
+    w = Workload("zc_lose", T=200, d=256, l=64, N=16, K=4, m=128, dtype="bf16", bias=True,
+                 n_zero=2, n_copy=2, n_const=2)
+    inp = make_inputs(w, 17)
+    inp["bias"][w.N:] = -1e30
+    plain = {k: v for k, v in inp.items() if k != "zc_const"}
+    plain["W_router"] = inp["W_router"][:w.N].contiguous()
+    plain["bias"] = inp["bias"][:w.N].contiguous()
+    a = zc_forward(w, P.to_device(inp), TL)
+    b = B.forward(P.to_device(plain), w.K, path=TL)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
 # --- smaller shapes: several tiles, ragged tails, both FFN paths --------------
 
 SMALL_PREFILL = Workload("small_prefill", T=1000, d=512, l=128, N=64, K=6, m=256, dtype="bf16")
