@@ -59,13 +59,22 @@
  * Element type of x and the weights: float32 (dtype 0) or bfloat16 bit
  * patterns (dtype 1).  Each element is widened to double at use; every sum is
  * accumulated in double in index order.
- * Optional FP8 expert weights (experts_fp8 = 1): W1 and W2 hold OCP FP8
+ * Optional FP8 expert weights (expert_format = 1): W1 and W2 hold OCP FP8
  * E4M3 codes (one byte each: sign, 4 exponent bits with bias 7, 3 mantissa
  * bits; exponent 0 is subnormal, 0x7F / 0xFF are NaN, no infinities), with
  * one float32 scale per output row: W1[e][j][i] = e4m3(code) * s1[e*m + j],
  * W2[e][i][j] = e4m3(code) * s2[e*l + i].  The pages name low-precision
  * expert weights (NVFP4, MXFP4) without a format; this block-free per-row
  * FP8 format is a reading.
+ * Optional MXFP4 expert weights (expert_format = 2; the OCP microscaling
+ * format the pages name): W1 and W2 hold E2M1 codes (4 bits: sign, 2
+ * exponent bits with bias 1, 1 mantissa bit; exponent 0 is subnormal; no
+ * infinities or NaN), two per byte with the even element in the low nibble,
+ * so W1 is [N, m, l/2] bytes and W2 [N, l, m/2]; every 32 consecutive
+ * elements along the reduction index share one E8M0 scale byte (2^(b-127),
+ * 0xFF is NaN): s1 [N, m, l/32] and s2 [N, l, m/32] bytes.  Element i of the
+ * flattened matrix is e2m1(nibble i) * e8m0(scale byte i / 32).  The nibble
+ * order and the block's direction are readings.
  *
  * Parity pins: see tests/test_oracle_pins.py.  Every output here is pinned by
  * at least one check that does not re-run this code's formulas: brute-force
@@ -82,7 +91,7 @@ typedef struct {
     int32_t dtype;    /* 0: float32 arrays, 1: bfloat16 bit patterns */
     int32_t standard; /* 1: no projections (requires l == d) */
     int32_t m_shared; /* width of the shared expert, 0: none */
-    int32_t experts_fp8; /* 1: W1, W2 are E4M3 codes with per-row scales */
+    int32_t expert_format; /* 0: the layer's dtype, 1: E4M3 + row scales, 2: MXFP4 */
     int32_t n_zero, n_copy, n_const; /* zero-computation experts (ids N ...) */
 } oracle_dims;
 
@@ -110,9 +119,23 @@ static double e4m3(uint8_t c) {
     return sign ? -v : v;
 }
 
-/* expert weight element i of a row whose scale is row_scale (FP8 mode) */
-static double expert_w(const oracle_dims* D, const void* W, const float* scale, size_t i, size_t row) {
-    if (D->experts_fp8) return e4m3(((const uint8_t*)W)[i]) * (double)scale[row];
+/* OCP MX E2M1 (FP4): the value of one 4-bit code */
+static double e2m1(int c) {
+    const int ex = (c >> 1) & 3, man = c & 1;
+    const double v = ex == 0 ? 0.5 * man : ldexp(1.0 + 0.5 * man, ex - 1);
+    return (c & 8) ? -v : v;
+}
+
+/* OCP MX E8M0 block scale: 2^(b - 127); 0xFF is NaN */
+static double e8m0(uint8_t b) { return b == 0xFF ? NAN : ldexp(1.0, (int)b - 127); }
+
+/* element i of a flattened expert weight matrix (row `row` holds it) */
+static double expert_w(const oracle_dims* D, const void* W, const void* scale, size_t i, size_t row) {
+    if (D->expert_format == 1) return e4m3(((const uint8_t*)W)[i]) * (double)((const float*)scale)[row];
+    if (D->expert_format == 2) {
+        const uint8_t byte = ((const uint8_t*)W)[i >> 1];
+        return e2m1((i & 1) ? byte >> 4 : byte & 15) * e8m0(((const uint8_t*)scale)[i >> 5]);
+    }
     return widen(W, D->dtype, i);
 }
 
@@ -144,7 +167,7 @@ static int outranks(const double* logit, int a, int b) {
  */
 static void one_token(const oracle_dims* D, int t, const void* x, const void* Wd,
                       const void* Wr, const void* W1, const void* W2, const void* Wu,
-                      const void* Ws1, const void* Ws2, const float* s1, const float* s2,
+                      const void* Ws1, const void* Ws2, const void* s1, const void* s2,
                       const void* zc, const float* bias, const int32_t* forced, double* out_t,
                       int32_t* ids_t, double* gates_t, double* logits_t, double* gap_t,
                       double* work) {
@@ -266,14 +289,15 @@ static void one_token(const oracle_dims* D, int t, const void* x, const void* Wd
  * the selection:  out [n_sel,d]  ids [n_sel,K]  gates [n_sel,K]
  * logits [n_sel,Nr]  gap [n_sel]  (gap = K-th minus (K+1)-th largest logit).
  * forced_ids [n_sel,K] or NULL.  Ws1 / Ws2: the shared expert, used only
- * when D->m_shared > 0.  s1 [N*m] / s2 [N*l]: the FP8 expert weights' row
- * scales, used only when D->experts_fp8.  zc [n_const*l]: the constant
+ * when D->m_shared > 0.  s1 / s2: the expert weights' scales (FP8: float32
+ * [N*m] / [N*l]; MXFP4: bytes [N*m*l/32] / [N*l*m/32]), used only when
+ * D->expert_format != 0.  zc [n_const*l]: the constant
  * experts' vectors, used only when D->n_const > 0.  Returns 0, or -1 on bad
  * arguments.
  */
 int oracle_forward(const oracle_dims* D, const void* x, const void* Wd, const void* Wr,
                    const void* W1, const void* W2, const void* Wu, const void* Ws1,
-                   const void* Ws2, const float* s1, const float* s2, const void* zc,
+                   const void* Ws2, const void* s1, const void* s2, const void* zc,
                    const float* bias, const int32_t* sel, int32_t n_sel, const int32_t* forced_ids,
                    double* out, int32_t* ids, double* gates, double* logits, double* gap) {
     if (!D || !x || !Wr || !W1 || !W2 || !out || !ids || !gates || !logits || !gap) return -1;
@@ -281,7 +305,8 @@ int oracle_forward(const oracle_dims* D, const void* x, const void* Wd, const vo
     if (D->K < 1 || D->K > routed_ids(D) || D->T < 0 || n_sel < 0 || D->m_shared < 0) return -1;
     if (D->standard ? (D->l != D->d) : (!Wd || !Wu)) return -1;
     if (D->m_shared > 0 && (!Ws1 || !Ws2)) return -1;
-    if (D->experts_fp8 && (!s1 || !s2)) return -1;
+    if (D->expert_format < 0 || D->expert_format > 2 || (D->expert_format != 0 && (!s1 || !s2))) return -1;
+    if (D->expert_format == 2 && (D->l % 32 != 0 || D->m % 32 != 0)) return -1;
     for (int q = 0; q < n_sel; ++q) {
         int t = sel ? sel[q] : q;
         if (t < 0 || t >= D->T) return -1;

@@ -27,7 +27,7 @@ CFLAGS = ["-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-fPIC", "-s
 
 class _Dims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32)
-                for n in ("T", "d", "l", "N", "K", "m", "dtype", "standard", "m_shared", "experts_fp8",
+                for n in ("T", "d", "l", "N", "K", "m", "dtype", "standard", "m_shared", "expert_format",
                           "n_zero", "n_copy", "n_const")]
 
 
@@ -71,7 +71,9 @@ class Oracle:
         W2 [N,l,m], W_up [d,l]; bias float32 [N] or None; the shared expert
         W_s1 [m_s,d] and W_s2 [d,m_s], or None for none.  FP8 experts: W1 and
         W2 as uint8 E4M3 codes with float32 row scales W1_scale [N,m] and
-        W2_scale [N,l].  Zero-computation experts: n_zero zero and n_copy copy
+        W2_scale [N,l].  MXFP4 experts: W1 [N,m,l/2] and W2 [N,l,m/2] uint8
+        (two E2M1 codes per byte, even element in the low nibble) with uint8
+        E8M0 block scales W1_scale [N,m,l/32] and W2_scale [N,l,m/32].  Zero-computation experts: n_zero zero and n_copy copy
         experts and zc_const [n_const, l] (same dtype as x) constant experts
         take the routed ids N, N+1, ... in that order; W_router (and bias)
         then have N + n_zero + n_copy + n_const rows (Nr).
@@ -83,9 +85,13 @@ class Oracle:
         if dtype == 1 and x.dtype != np.uint16:
             raise TypeError("x must be float32 or uint16 (bf16 bits)")
         T, d = x.shape
+        fp8 = W1_scale is not None
+        if fp8 != (W2_scale is not None):
+            raise ValueError("W1_scale and W2_scale come together")
+        mx = fp8 and np.asarray(W1_scale).dtype == np.uint8   # MXFP4: byte scales
         N = W1.shape[0]
         m = W1.shape[1]
-        l = W1.shape[2]
+        l = W1.shape[2] * (2 if mx else 1)
         n_const = 0 if zc_const is None else int(zc_const.shape[0])
         Nr = N + n_zero + n_copy + n_const
         if W_router.shape[0] != Nr:
@@ -93,9 +99,6 @@ class Oracle:
         if (W_s1 is None) != (W_s2 is None):
             raise ValueError("W_s1 and W_s2 come together")
         ms = 0 if W_s1 is None else int(W_s1.shape[0])
-        fp8 = W1_scale is not None
-        if fp8 != (W2_scale is not None):
-            raise ValueError("W1_scale and W2_scale come together")
         if fp8 and (W1.dtype != np.uint8 or W2.dtype != np.uint8):
             raise TypeError("FP8 expert weights are uint8 E4M3 codes")
         arrs = [x, W_down, W_router, W1, W2, W_up, W_s1, W_s2, zc_const]
@@ -117,11 +120,17 @@ class Oracle:
         if forced_ids is not None:
             forced_ids = np.ascontiguousarray(np.asarray(forced_ids, dtype=np.int32))
             assert forced_ids.shape == (n, K)
-        if fp8:
+        if mx:
+            W1_scale = np.ascontiguousarray(W1_scale)
+            W2_scale = np.ascontiguousarray(W2_scale, dtype=np.uint8)
+            assert W1.shape == (N, m, l // 2) and W2.shape == (N, l, m // 2)
+            assert W1_scale.size == N * m * l // 32 and W2_scale.size == N * l * m // 32
+        elif fp8:
             W1_scale = np.ascontiguousarray(W1_scale, dtype=np.float32)
             W2_scale = np.ascontiguousarray(W2_scale, dtype=np.float32)
             assert W1_scale.size == N * m and W2_scale.size == N * l
-        D = _Dims(T, d, l, N, K, m, dtype, 1 if standard else 0, ms, 1 if fp8 else 0, n_zero, n_copy, n_const)
+        D = _Dims(T, d, l, N, K, m, dtype, 1 if standard else 0, ms, 2 if mx else (1 if fp8 else 0),
+                  n_zero, n_copy, n_const)
         out = np.empty((n, d), np.float64)
         ids = np.empty((n, K), np.int32)
         gates = np.empty((n, K), np.float64)

@@ -29,6 +29,11 @@ What pins what:
                power-of-two row scale is exact in float32: the FP8 layer
                equals the float32 layer on those weights bit-exactly; with
                arbitrary row scales, N = K = 1 is a dense FFN in numpy
+  MXFP4        E2M1 codes decoded by a table of the OCP MX element values,
+  experts      E8M0 scales by numpy ldexp, blocks by numpy repeat: the MXFP4
+               layer equals the float32 layer on those weights bit-exactly
+               (every byte value appears, the scales differ per block); N = K
+               = 1 is a dense FFN in numpy
   zero-        a dense-mask evaluation in numpy (every routed id's output
   computation  for every token, weighted by a [T, Nr] gate matrix that is
   experts      zero off the top K); K = 1 special cases with closed forms:
@@ -444,6 +449,51 @@ def pin_fp8_experts(o):
     assert np.allclose(got, want, rtol=1e-12, atol=1e-12), "FP8 dense special case differs from numpy"
 
 
+# the eight E2M1 magnitudes of the OCP Microscaling spec, by code & 7
+E2M1_VALUES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def mx_decode(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """MXFP4 -> float64: codes [..., rows, cols/2] (even element in the low
+    nibble), scales [..., rows, cols/32] E8M0 bytes."""
+    nib = np.stack([codes & 15, codes >> 4], axis=-1).reshape(*codes.shape[:-1], 2 * codes.shape[-1])
+    val = np.where(nib & 8, -1.0, 1.0) * E2M1_VALUES[nib & 7]
+    return val * np.repeat(np.ldexp(1.0, scales.astype(np.int64) - 127), 32, axis=-1)
+
+
+def mx_layer(seed, T, d, l, N, m):
+    """A float32 layer whose expert weights are MXFP4: every byte value as
+    codes, block scales 2^-11 .. 2^-4 varying per block."""
+    r = _rng(seed)
+    L = rand_layer(seed, T, d, l, N, m)
+    L["W1"] = np.resize(r.permutation(256).astype(np.uint8), N * m * l // 2).reshape(N, m, l // 2)
+    L["W2"] = np.resize(r.permutation(256).astype(np.uint8), N * l * m // 2).reshape(N, l, m // 2)
+    L["W1_scale"] = r.integers(116, 124, (N, m, l // 32)).astype(np.uint8)
+    L["W2_scale"] = r.integers(116, 124, (N, l, m // 32)).astype(np.uint8)
+    return L
+
+
+def pin_mxfp4_experts(o):
+    """MXFP4 expert weights, decoded independently."""
+    T, d, l, N, m, K = 6, 16, 64, 4, 64, 2
+    L = mx_layer(61, T, d, l, N, m)
+    ref = dict(L)
+    ref["W1"] = mx_decode(L["W1"], L["W1_scale"]).astype(np.float32)
+    ref["W2"] = mx_decode(L["W2"], L["W2_scale"]).astype(np.float32)
+    assert np.array_equal(ref["W1"].astype(np.float64), mx_decode(L["W1"], L["W1_scale"]))
+    a = run_fp8(o, L, K)
+    b = run(o, ref, K)
+    assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["ids"], b["ids"]), \
+        "MXFP4 layer != float32 layer on the decoded weights"
+    L = mx_layer(62, T, d, l, 1, m)
+    w1 = mx_decode(L["W1"], L["W1_scale"])[0]
+    w2 = mx_decode(L["W2"], L["W2_scale"])[0]
+    x = f64(L["x"])
+    s = (np.maximum((x @ f64(L["W_down"]).T) @ w1.T, 0.0) ** 2) @ w2.T
+    want = x + s @ f64(L["W_up"]).T
+    assert np.allclose(run_fp8(o, L, 1)["out"], want, rtol=1e-12, atol=1e-12), "MXFP4 dense case differs from numpy"
+
+
 def zc_layer(seed, T, d, l, N, m, nz, nc, nk, *, standard=False):
     """A float32 layer with N FFN experts followed by nz zero, nc copy and nk
     constant experts (router rows for all of them)."""
@@ -541,4 +591,5 @@ ALL_PINS = [
     pin_shared_expert,
     pin_fp8_experts,
     pin_zero_computation_experts,
+    pin_mxfp4_experts,
 ]

@@ -66,9 +66,17 @@ MUTANTS = {
     "fp8_mantissa_width": ("v = ldexp(1.0 + man / 8.0, ex - 7);", "v = ldexp(1.0 + man / 16.0, ex - 7);"),
     "fp8_subnormals_flushed": ("v = ldexp((double)man, -9);", "v = 0.0;"),
     "fp8_sign_dropped": ("return sign ? -v : v;", "return v;"),
-    "fp8_scale_dropped": ("e4m3(((const uint8_t*)W)[i]) * (double)scale[row]", "e4m3(((const uint8_t*)W)[i])"),
-    "fp8_scale_wrong_row": ("e4m3(((const uint8_t*)W)[i]) * (double)scale[row]",
-                            "e4m3(((const uint8_t*)W)[i]) * (double)scale[row / 2]"),
+    "fp8_scale_dropped": ("e4m3(((const uint8_t*)W)[i]) * (double)((const float*)scale)[row]",
+                          "e4m3(((const uint8_t*)W)[i])"),
+    "fp8_scale_wrong_row": ("e4m3(((const uint8_t*)W)[i]) * (double)((const float*)scale)[row]",
+                            "e4m3(((const uint8_t*)W)[i]) * (double)((const float*)scale)[row / 2]"),
+    "mx_nibbles_swapped": ("e2m1((i & 1) ? byte >> 4 : byte & 15)", "e2m1((i & 1) ? byte & 15 : byte >> 4)"),
+    "mx_block_of_16": ("e8m0(((const uint8_t*)scale)[i >> 5])", "e8m0(((const uint8_t*)scale)[(i >> 4) % 64])"),
+    "mx_scale_per_row": ("e8m0(((const uint8_t*)scale)[i >> 5])", "e8m0(((const uint8_t*)scale)[row])"),
+    "mx_fp4_bias_2": ("ldexp(1.0 + 0.5 * man, ex - 1)", "ldexp(1.0 + 0.5 * man, ex - 2)"),
+    "mx_fp4_subnormal_dropped": ("ex == 0 ? 0.5 * man :", "ex == 0 ? 0.0 :"),
+    "mx_fp4_sign_dropped": ("return (c & 8) ? -v : v;", "return v;"),
+    "mx_e8m0_bias_128": ("ldexp(1.0, (int)b - 127)", "ldexp(1.0, (int)b - 128)"),
     "zc_not_selectable": ("        for (int e = 0; e < Nr; ++e)\n            if (!chosen[e] && (best < 0",
                           "        for (int e = 0; e < N; ++e)\n            if (!chosen[e] && (best < 0"),
     "zc_zero_acts_as_copy": ("if (q < D->n_zero) return;", "if (q < 0) return;"),
