@@ -74,10 +74,13 @@ class Hip:
 
 
 def expert_bytes(w, A: float) -> float:
-    """W1 and W2 of A experts, read once: elements at the layer's width, or
-    one byte each plus a float32 scale per row for FP8 experts."""
+    """W1 and W2 of A experts, read once: elements at the layer's width; FP8:
+    one byte each plus a float32 scale per row; MXFP4: half a byte each plus
+    a scale byte per 32."""
     if w.experts == "fp8":
         return A * (2 * w.l * w.m + 4 * (w.l + w.m))
+    if w.experts == "mxfp4":   # half a byte per code, a scale byte per 32 elements
+        return A * 2 * w.l * w.m * (0.5 + 1.0 / 32)
     return A * 2 * w.l * w.m * w.elem_bytes
 
 
@@ -223,7 +226,7 @@ def measure(w, sets, cpu_seconds: float) -> dict:
         ffn_flops = 4.0 * R * w.l * w.m
         # FP8 weights are decoded to bf16 on the way into LDS: the products
         # run on the bf16 MFMAs, so the bf16 peak is the bound
-        q = "Q" if w.experts == "fp8" else ""
+        q = {"dense": "", "fp8": "Q", "mxfp4": "X"}[w.experts]
         roof = {"kernel": f"gemm2_kernel<Ffn1{q}>+<Ffn2{q}>", "bound": "mfma",
                 "achieved": ffn_flops / (ffn_us * 1e-6) / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "traffic": None}

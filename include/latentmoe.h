@@ -45,6 +45,15 @@
  * W1_scale [N, m] (W1[e][j][:] = code * W1_scale[e][j]) and W2_scale [N, l].
  * The pages name low-precision expert weights (NVFP4 / MXFP4) without a
  * format; this per-row FP8 format is a reading.
+ * Optional MXFP4 expert weights (bfloat16 layers, dims.expert_format =
+ * LMOE_EXPERTS_MXFP4, through latentmoe_forward_ex), the OCP microscaling
+ * format the pages name (zhichai.net section 4 and 10100.com section 2):
+ * W1 [N, m, l/2] and W2 [N, l, m/2] bytes hold two E2M1 codes each (sign,
+ * 2 exponent bits with bias 1, 1 mantissa bit), the even element in the low
+ * nibble; W1_scale [N, m, l/32] and W2_scale [N, l, m/32] bytes hold one
+ * E8M0 scale (2^(b-127), b in 1 .. 254) per 32 consecutive elements along
+ * the reduction index: weight = e2m1(code) * 2^(b-127).  The nibble order,
+ * the blocks' direction and the scale range are readings.
  * Optional zero-computation experts (through latentmoe_forward_ex; after
  * MoE++, 10100.com article, section 3.2): dims.n_zero zero experts,
  * dims.n_copy copy experts and dims.n_const constant experts take the
@@ -98,7 +107,7 @@ typedef enum { LMOE_F32 = 0, LMOE_BF16 = 1 } lmoe_dtype;
 typedef enum { LMOE_PATH_AUTO = 0, LMOE_PATH_STREAM = 1, LMOE_PATH_TILED = 2 } lmoe_path;
 
 /* Storage of the routed experts' W1 / W2. */
-typedef enum { LMOE_EXPERTS_DENSE = 0, LMOE_EXPERTS_FP8_E4M3 = 1 } lmoe_expert_format;
+typedef enum { LMOE_EXPERTS_DENSE = 0, LMOE_EXPERTS_FP8_E4M3 = 1, LMOE_EXPERTS_MXFP4 = 2 } lmoe_expert_format;
 
 typedef struct {
     int32_t T;      /* tokens, >= 1 */
@@ -173,9 +182,8 @@ int latentmoe_forward_timed(const void* x, const void* W_down, const void* W_rou
 /*
  * The general entry point: every option of the layer in one argument block.
  * Pointers as in latentmoe_forward; W_shared1 / W_shared2 with
- * dims->m_shared > 0 (else NULL); W1_scale / W2_scale with
- * dims->expert_format == LMOE_EXPERTS_FP8_E4M3 (else NULL; 16-byte
- * aligned); zc_const [n_const, l] with dims->n_const > 0 (else NULL; 16-byte
+ * dims->m_shared > 0 (else NULL); W1_scale / W2_scale with FP8 or MXFP4
+ * experts (else NULL; FP8 float32 scales 16-byte aligned); zc_const [n_const, l] with dims->n_const > 0 (else NULL; 16-byte
  * aligned); events NULL or as in latentmoe_forward_timed.  The other
  * forward entry points are this call with the options they do not name
  * turned off.
@@ -189,8 +197,8 @@ typedef struct {
     const void* W_up;
     const void* W_shared1;
     const void* W_shared2;
-    const float* W1_scale;
-    const float* W2_scale;
+    const void* W1_scale;   /* FP8: float32 row scales; MXFP4: E8M0 block scale bytes */
+    const void* W2_scale;
     const void* zc_const;
     const float* router_bias;
     void* out;

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(PKG, "liblatentmoe.so")
 LMOE_OK, LMOE_EINVAL, LMOE_EUNSUPPORTED, LMOE_EWORKSPACE, LMOE_EHIP = 0, -1, -2, -3, -4
 LMOE_F32, LMOE_BF16 = 0, 1
 LMOE_PATH_AUTO, LMOE_PATH_STREAM, LMOE_PATH_TILED = 0, 1, 2
-LMOE_EXPERTS_DENSE, LMOE_EXPERTS_FP8_E4M3 = 0, 1
+LMOE_EXPERTS_DENSE, LMOE_EXPERTS_FP8_E4M3, LMOE_EXPERTS_MXFP4 = 0, 1, 2
 LMOE_N_STAGE_EVENTS = 8
 STAGES = ("proj_router", "topk", "dispatch", "ffn1", "ffn2", "combine", "up")
 
@@ -199,13 +199,19 @@ def dims_for(inputs: dict, K: int, path: int = LMOE_PATH_AUTO, n_zero: int = 0, 
     x, W1 = inputs["x"], inputs["W1"]
     T, d = x.shape
     N, m, l = W1.shape
+    s1 = inputs.get("W1_scale")
+    if s1 is None:
+        fmt = LMOE_EXPERTS_DENSE
+    elif s1.dtype == torch.uint8:   # E8M0 block scales: two E2M1 codes per byte
+        fmt, l = LMOE_EXPERTS_MXFP4, 2 * l
+    else:
+        fmt = LMOE_EXPERTS_FP8_E4M3
     ws1 = inputs.get("W_s1")
     zc = inputs.get("zc_const")
     n_const = 0 if zc is None else zc.shape[0]
     if inputs["W_router"].shape[0] != N + n_zero + n_copy + n_const:
         raise ValueError(f"W_router has {inputs['W_router'].shape[0]} rows for N={N} + {n_zero} zero + "
                          f"{n_copy} copy + {n_const} constant experts")
-    fmt = LMOE_EXPERTS_DENSE if inputs.get("W1_scale") is None else LMOE_EXPERTS_FP8_E4M3
     return make_dims(T, d, l, N, m, x.dtype, path, 0 if ws1 is None else ws1.shape[0], fmt, n_zero, n_copy, n_const)
 
 

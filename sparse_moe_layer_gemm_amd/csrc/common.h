@@ -36,6 +36,8 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 
 __device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ uint2 ldg8(const void* p) { return *reinterpret_cast<const uint2*>(p); }
+__device__ __forceinline__ uint32_t ldg4(const void* p) { return *reinterpret_cast<const uint32_t*>(p); }
+__device__ __forceinline__ uint32_t ldg1(const void* p) { return *static_cast<const uint8_t*>(p); }
 
 // 8 OCP FP8 E4M3 codes (bytes 0..7 of v) -> the 8 equal bfloat16 values
 // (every E4M3 value is exact in bfloat16), with gfx950's
@@ -51,6 +53,29 @@ __device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint2 v) {
                  __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
 #else
     (void)v;
+    return uint4{0u, 0u, 0u, 0u};
+#endif
+}
+
+// An OCP E8M0 block scale byte b (1 .. 254) as the float32 2^(b - 127).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t b) { return __uint_as_float(b << 23); }
+
+// 8 OCP E2M1 (FP4) codes -- the nibbles of v, element 0 in the low nibble of
+// byte 0 -- times the block scale sc, as 8 bfloat16 (exact: an E2M1 value
+// times a power of two), with gfx950's v_cvt_scalef32_pk_bf16_fp4.  Device
+// code only.
+__device__ __forceinline__ uint4 fp4x8_to_bf16x8(uint32_t v, float sc) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, sc, 0);
+    const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, sc, 1);
+    const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, sc, 2);
+    const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, sc, 3);
+    return uint4{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                 __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
+#else
+    (void)v;
+    (void)sc;
     return uint4{0u, 0u, 0u, 0u};
 #endif
 }

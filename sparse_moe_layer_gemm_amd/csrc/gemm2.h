@@ -203,6 +203,13 @@ struct RowCtx<Ffn2Q> {
     }
 };
 
+// MXFP4 experts: the block scales are applied when the codes are decoded,
+// so the epilogues are the bf16 problems' own.
+template <>
+struct RowCtx<Ffn1X> : RowCtx<Ffn1<bf16>> {};
+template <>
+struct RowCtx<Ffn2X> : RowCtx<Ffn2<bf16, bf16>> {};
+
 template <>
 struct RowCtx<Shared1<bf16>> {
     static constexpr bool kRowVal = false;
@@ -313,23 +320,42 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm2_kernel(LayerArgs a, int 
     Tile ct;  // the tile the MFMAs work on
     if (!tile_at(lslot, ct)) return;
     int cslot = lslot;
-    // B rows: bf16, or FP8 E4M3 codes (one byte each) decoded to bf16 when
-    // they are written to LDS, so the LDS layout and the MFMAs are the same
+    // B rows: bf16; FP8 E4M3 codes (one byte each); or MXFP4 (two E2M1
+    // codes per byte, a scale byte per 32 elements) -- the codes are decoded
+    // to bf16 when they are written to LDS, so the LDS layout and the MFMAs
+    // are the same.  A thread stages 8 elements of a row per k-step: 16
+    // bytes, 8 code bytes, or 4 code bytes and their scale byte.
     using BE = typename P::BElem;
-    constexpr bool kQ = sizeof(BE) == 1;
-    using BStage = typename std::conditional<kQ, uint2, uint4>::type;
+    constexpr int kFmt = std::is_same<BE, MxFp4>::value ? 2 : (sizeof(BE) == 1 ? 1 : 0);
+    using BStage = typename std::conditional<kFmt == 0, uint4, uint2>::type;
+    using BPtr = typename std::conditional<kFmt == 0, const bf16*, const uint8_t*>::type;
     const bf16* ap[S::LA];
-    const BE* bp[S::LB];
+    BPtr bp[kFmt == 2 ? 1 : S::LB];
+    // MXFP4: the loading tile's expert's code and scale bytes, and each
+    // staged row's byte offset within the expert (32-bit: fewer registers)
+    const uint8_t* xc = nullptr;
+    const uint8_t* xs = nullptr;
+    uint32_t bo[kFmt == 2 ? S::LB : 1];
     auto set_rows = [&](const Tile& t) {
 #pragma unroll
         for (int i = 0; i < S::LA; ++i) {
             const int r = t.row0 + lrow + S::RSTEP * i;
             ap[i] = P::a_row(a, t.grp, r < t.row_end ? r : t.row0) + ch * 8;
         }
+        if constexpr (kFmt == 2) {
+            xc = P::x_codes(a, t.grp);
+            xs = P::x_scales(a, t.grp);
 #pragma unroll
-        for (int i = 0; i < S::LB; ++i) {
-            const int c = t.col0 + lrow + S::RSTEP * i;
-            bp[i] = P::b_row(a, t.grp, c < ncols ? c : t.col0) + ch * 8;
+            for (int i = 0; i < S::LB; ++i) {
+                const int c = t.col0 + lrow + S::RSTEP * i;
+                bo[i] = (uint32_t)(c < ncols ? c : t.col0) * (uint32_t)(nk * (kG2K / 2)) + ch * 4;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < S::LB; ++i) {
+                const int c = t.col0 + lrow + S::RSTEP * i;
+                bp[i] = P::b_row(a, t.grp, c < ncols ? c : t.col0) + ch * 8;
+            }
         }
     };
     set_rows(ct);
@@ -361,10 +387,14 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm2_kernel(LayerArgs a, int 
 #pragma unroll
         for (int i = 0; i < S::LB; ++i)
             if (in_part(i, S::LB, 2 * g) || in_part(i, S::LB, 2 * g + 1)) {
-                if constexpr (kQ)
+                if constexpr (kFmt == 2) {
+                    const uint32_t o = bo[i] + k0 / 2;
+                    rb[i] = uint2{ldg4(xc + o), ldg1(xs + (o >> 4))};
+                } else if constexpr (kFmt == 1) {
                     rb[i] = ldg8(bp[i] + k0);
-                else
+                } else {
                     rb[i] = ldg16(bp[i] + k0);
+                }
             }
     };
     auto swrite_part = [&](int st, int q) {
@@ -380,7 +410,9 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm2_kernel(LayerArgs a, int 
         for (int i = 0; i < S::LB; ++i)
             if (in_part(i, S::LB, q)) {
                 const int r = lrow + S::RSTEP * i;
-                if constexpr (kQ)
+                if constexpr (kFmt == 2)
+                    bs[r * 8 + (ch ^ g2_swz(r))] = fp4x8_to_bf16x8(rb[i].x, e8m0_to_f32(rb[i].y));
+                else if constexpr (kFmt == 1)
                     bs[r * 8 + (ch ^ g2_swz(r))] = e4m3x8_to_bf16x8(rb[i]);
                 else
                     bs[r * 8 + (ch ^ g2_swz(r))] = rb[i];

@@ -85,7 +85,7 @@ struct Plan {
     bool skinny = false;          // projections on the skinny kernel
     int tile_rows = G2Small::BM;
     bool ffn_large = false;       // tiled FFN on G2Large
-    bool fp8 = false;             // FP8 E4M3 expert weights
+    int wfmt = 0;                 // expert weights: 0 dense, 1 FP8 E4M3 rows, 2 MXFP4
     int nr = 0;                   // routed ids: FFN and zero-computation experts
     int nblk = 1;                 // dispatch blocks
     int ms = 128;                 // streaming FFN m-slice
@@ -132,15 +132,20 @@ Plan make_plan(const lmoe_dims* dm, int32_t K) {
         p.status = fail(LMOE_EINVAL, "dtype=%d is not LMOE_F32 or LMOE_BF16", d.dtype);
         return p;
     }
-    if (d.expert_format != LMOE_EXPERTS_DENSE && d.expert_format != LMOE_EXPERTS_FP8_E4M3) {
+    if (d.expert_format != LMOE_EXPERTS_DENSE && d.expert_format != LMOE_EXPERTS_FP8_E4M3 &&
+        d.expert_format != LMOE_EXPERTS_MXFP4) {
         p.status = fail(LMOE_EINVAL, "expert_format=%d is not a lmoe_expert_format", d.expert_format);
         return p;
     }
-    if (d.expert_format == LMOE_EXPERTS_FP8_E4M3 && d.dtype != LMOE_BF16) {
-        p.status = fail(LMOE_EUNSUPPORTED, "FP8 experts need a bfloat16 layer");
+    if (d.expert_format != LMOE_EXPERTS_DENSE && d.dtype != LMOE_BF16) {
+        p.status = fail(LMOE_EUNSUPPORTED, "FP8 / MXFP4 experts need a bfloat16 layer");
         return p;
     }
-    p.fp8 = d.expert_format == LMOE_EXPERTS_FP8_E4M3;
+    p.wfmt = d.expert_format == LMOE_EXPERTS_FP8_E4M3 ? 1 : (d.expert_format == LMOE_EXPERTS_MXFP4 ? 2 : 0);
+    if (p.wfmt == 2 && (long long)d.m * d.l / 2 >= (1ll << 31)) {
+        p.status = fail(LMOE_EUNSUPPORTED, "MXFP4 experts of more than 2^31 code bytes (m=%d, l=%d)", d.m, d.l);
+        return p;
+    }
     if (d.m_shared < 0 || d.m_shared % 64 != 0) {
         p.status = fail(LMOE_EINVAL, "m_shared=%d must be 0 or a positive multiple of 64", d.m_shared);
         return p;
@@ -343,12 +348,19 @@ void launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* events
     if constexpr (sizeof(E) == 2) {
         if (p.path == LMOE_PATH_STREAM) {
             const dim3 g(p.nsplit, a.n_ffn);
-            if (p.fp8)
-                p.ms == 128 ? ffn_stream_kernel<128, true><<<g, b256, 0, st>>>(a)
-                            : ffn_stream_kernel<64, true><<<g, b256, 0, st>>>(a);
+            auto stream = [&](auto fmt) {
+                constexpr int F = decltype(fmt)::value;
+                p.ms == 128 ? ffn_stream_kernel<128, F><<<g, b256, 0, st>>>(a)
+                            : ffn_stream_kernel<64, F><<<g, b256, 0, st>>>(a);
+            };
+            if (p.wfmt == 1)
+                stream(std::integral_constant<int, 1>{});
+            else if (p.wfmt == 2 && p.ms == 128 && a.l % (64 * kMxNKB) == 0 && a.m % 128 == 0)
+                ffn_stream_kernel<128, 2, true><<<g, b256, 0, st>>>(a);   // vector scale loads
+            else if (p.wfmt == 2)
+                stream(std::integral_constant<int, 2>{});
             else
-                p.ms == 128 ? ffn_stream_kernel<128, false><<<g, b256, 0, st>>>(a)
-                            : ffn_stream_kernel<64, false><<<g, b256, 0, st>>>(a);
+                stream(std::integral_constant<int, 0>{});
             mark(4);
         } else {
             auto ffn = [&](auto f1, auto f2) {
@@ -364,8 +376,10 @@ void launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* events
                     launch_g2<F2, G2Small>(a, (int)mt, cdiv(a.l, G2Small::BN), st);
                 }
             };
-            if (p.fp8)
+            if (p.wfmt == 1)
                 ffn(Ffn1Q{}, Ffn2Q{});
+            else if (p.wfmt == 2)
+                ffn(Ffn1X{}, Ffn2X{});
             else
                 ffn(Ffn1<bf16>{}, Ffn2<bf16, YT>{});
         }
@@ -439,7 +453,7 @@ int latentmoe_workspace_layout(const lmoe_dims* dims, int32_t K, lmoe_ws_layout*
 }
 
 static int forward_impl(const void* x, const void* W_down, const void* W_router, const void* W1, const void* W2,
-                        const void* W_up, const void* W_s1, const void* W_s2, const float* w1s, const float* w2s,
+                        const void* W_up, const void* W_s1, const void* W_s2, const void* w1s, const void* w2s,
                         const void* zc_const, int32_t K, void* out, const lmoe_dims* dims, const float* router_bias,
                         int32_t* topk_ids, float* topk_gates, void* workspace, size_t workspace_bytes,
                         void* stream, void* const* events) {
@@ -456,11 +470,11 @@ static int forward_impl(const void* x, const void* W_down, const void* W_router,
         return fail(LMOE_EINVAL, "W_shared1 and W_shared2 must be both set when m_shared > 0 and both NULL when "
                                  "m_shared == 0 (m_shared=%d)", d.m_shared);
     if (standard && d.l != d.d) return fail(LMOE_EINVAL, "standard mode (no projections) needs l == d");
-    if (p.fp8 != (w1s != nullptr) || (w1s == nullptr) != (w2s == nullptr))
-        return fail(LMOE_EINVAL, "W1_scale and W2_scale must be both set for FP8 experts and both NULL otherwise");
-    if ((w1s && (reinterpret_cast<uintptr_t>(w1s) & 15) != 0) ||
-        (w2s && (reinterpret_cast<uintptr_t>(w2s) & 15) != 0))
-        return fail(LMOE_EINVAL, "W1_scale and W2_scale must be 16-byte aligned");
+    if ((p.wfmt != 0) != (w1s != nullptr) || (w1s == nullptr) != (w2s == nullptr))
+        return fail(LMOE_EINVAL, "W1_scale and W2_scale must be both set for FP8 / MXFP4 experts and both NULL "
+                                 "otherwise");
+    if (p.wfmt == 1 && ((reinterpret_cast<uintptr_t>(w1s) & 15) != 0 || (reinterpret_cast<uintptr_t>(w2s) & 15) != 0))
+        return fail(LMOE_EINVAL, "FP8 W1_scale and W2_scale must be 16-byte aligned");
     if ((d.n_const > 0) != (zc_const != nullptr))
         return fail(LMOE_EINVAL, "zc_const must be set when n_const > 0 and NULL otherwise (n_const=%d)", d.n_const);
     if (!workspace) return fail(LMOE_EWORKSPACE, "workspace is NULL");
@@ -489,8 +503,10 @@ static int forward_impl(const void* x, const void* W_down, const void* W_router,
     a.W_s2 = W_s2;
     a.m_s = d.m_shared;
     a.bias = router_bias;
-    a.w1s = w1s;
-    a.w2s = w2s;
+    a.w1s = p.wfmt == 1 ? static_cast<const float*>(w1s) : nullptr;
+    a.w2s = p.wfmt == 1 ? static_cast<const float*>(w2s) : nullptr;
+    a.w1x = p.wfmt == 2 ? static_cast<const uint8_t*>(w1s) : nullptr;
+    a.w2x = p.wfmt == 2 ? static_cast<const uint8_t*>(w2s) : nullptr;
     a.out = out;
     a.T = d.T;
     a.d = d.d;
@@ -539,11 +555,11 @@ static int forward_impl(const void* x, const void* W_down, const void* W_router,
     return LMOE_OK;
 }
 
-// The entry points other than latentmoe_forward_ex take no FP8 experts and
+// The entry points other than latentmoe_forward_ex take no FP8 / MXFP4 experts and
 // no zero-computation experts.
 static int plain_options_only(const lmoe_dims* dims) {
     if (dims && dims->expert_format != LMOE_EXPERTS_DENSE)
-        return fail(LMOE_EINVAL, "FP8 experts go through latentmoe_forward_ex");
+        return fail(LMOE_EINVAL, "FP8 / MXFP4 experts go through latentmoe_forward_ex");
     if (dims && (dims->n_zero | dims->n_copy | dims->n_const) != 0)
         return fail(LMOE_EINVAL, "zero-computation experts go through latentmoe_forward_ex");
     return LMOE_OK;

@@ -24,6 +24,8 @@ struct LayerArgs {
     const void* zc;        // [n_const, l] constant experts' vectors, or NULL
     const float* w1s;      // [N, m] row scales of FP8 W1 (FP8 experts only)
     const float* w2s;      // [N, l] row scales of FP8 W2
+    const uint8_t* w1x;    // [N, m, l/32] E8M0 block scales of MXFP4 W1 (MXFP4 experts only)
+    const uint8_t* w2x;    // [N, l, m/32] E8M0 block scales of MXFP4 W2
     void* out;             // [T, d]
     int T, d, l, N, m, K;  // N: routed ids (FFN experts, then zero-computation experts)
     int n_ffn;             // FFN experts: ids < n_ffn have W1 / W2
@@ -244,6 +246,29 @@ struct Ffn2Q : Ffn2<bf16, bf16> {
         return static_cast<const uint8_t*>(a.W2) + ((size_t)e * a.l + c) * a.m;
     }
     __device__ static float row_scale(const LayerArgs& a, int e, int c) { return a.w2s[(size_t)e * a.l + c]; }
+};
+
+// The expert FFN with MXFP4 weights: two E2M1 codes per byte, one E8M0
+// scale per 32 elements along the reduction.  x_codes / x_scales give an
+// expert's code and scale bytes; within an expert, the scale of the
+// 32-element block holding code byte o is scale byte o / 16 (a row of n
+// elements has n / 2 code bytes and n / 32 scale bytes).
+struct MxFp4 {};   // BElem tag of MXFP4 weight rows
+
+struct Ffn1X : Ffn1<bf16> {
+    using BElem = MxFp4;
+    __device__ static const uint8_t* x_codes(const LayerArgs& a, int e) {
+        return static_cast<const uint8_t*>(a.W1) + (size_t)e * a.m * (a.l / 2);
+    }
+    __device__ static const uint8_t* x_scales(const LayerArgs& a, int e) { return a.w1x + (size_t)e * a.m * (a.l / 32); }
+};
+
+struct Ffn2X : Ffn2<bf16, bf16> {
+    using BElem = MxFp4;
+    __device__ static const uint8_t* x_codes(const LayerArgs& a, int e) {
+        return static_cast<const uint8_t*>(a.W2) + (size_t)e * a.l * (a.m / 2);
+    }
+    __device__ static const uint8_t* x_scales(const LayerArgs& a, int e) { return a.w2x + (size_t)e * a.l * (a.m / 32); }
 };
 
 }  // namespace lmoe

@@ -151,40 +151,68 @@ __global__ __launch_bounds__(256) void skinny_part_kernel(LayerArgs a, float* pa
 
 // The expert weights in 64-wide k blocks: lane group g = lane / 16 takes k =
 // 16g .. 16g+15 of a block, its first 8 terms going to one MFMA and the next
-// 8 to a second (the same grouping of the dot product for both weight
-// formats).  bf16: two 16-byte loads per lane; FP8 E4M3 (Q): one 16-byte load
-// of 16 codes, decoded to bf16 in registers.
-template <bool Q>
-struct W64 {
-    using WT = typename std::conditional<Q, uint8_t, bf16>::type;   // stored weight element
-    uint4 v[Q ? 1 : 2];
-    __device__ __forceinline__ static W64 load(const WT* p) {
-        W64 w;
-        w.v[0] = ldg16(p);
-        if constexpr (!Q) w.v[1] = ldg16(p + 8);
-        return w;
+// 8 to a second (the same grouping of the dot product for every weight
+// format).  W64<F>::load takes the element offset of the lane's first term
+// in the flattened weight matrix.
+//   F = 0, bf16: two 16-byte loads per lane.
+//   F = 1, FP8 E4M3: one 16-byte load of 16 codes, decoded to bf16 in
+//          registers (the row scale is applied to the fp32 result).
+//   F = 2, MXFP4: one 8-byte load of 16 E2M1 codes and their block's E8M0
+//          scale byte (16 consecutive terms lie in one 32-element block),
+//          decoded and scaled to bf16 in registers.
+// MXFP4: 64-wide k blocks per batch of phase-1 loads
+constexpr int kMxNKB = 4;
+
+template <int F>
+struct W64;
+
+template <>
+struct W64<0> {
+    uint4 v[2];
+    __device__ __forceinline__ static W64 load(const void* W, const uint8_t*, size_t off) {
+        const bf16* p = static_cast<const bf16*>(W) + off;
+        return W64{{ldg16(p), ldg16(p + 8)}};
     }
-    __device__ __forceinline__ static W64 zero() {
-        W64 w;
-#pragma unroll
-        for (int i = 0; i < (Q ? 1 : 2); ++i) w.v[i] = kZero16;
-        return w;
+    __device__ __forceinline__ static W64 zero() { return W64{{kZero16, kZero16}}; }
+    __device__ __forceinline__ bf16x8 frag(int h) const { return as_bf16x8(v[h]); }
+};
+
+template <>
+struct W64<1> {
+    uint4 v;
+    __device__ __forceinline__ static W64 load(const void* W, const uint8_t*, size_t off) {
+        return W64{ldg16(static_cast<const uint8_t*>(W) + off)};
     }
-    // the 8 terms of half h (0 or 1) as an MFMA fragment
+    __device__ __forceinline__ static W64 zero() { return W64{kZero16}; }
     __device__ __forceinline__ bf16x8 frag(int h) const {
-        if constexpr (Q)
-            return as_bf16x8(e4m3x8_to_bf16x8(h ? uint2{v[0].z, v[0].w} : uint2{v[0].x, v[0].y}));
-        else
-            return as_bf16x8(v[h]);
+        return as_bf16x8(e4m3x8_to_bf16x8(h ? uint2{v.z, v.w} : uint2{v.x, v.y}));
     }
 };
 
-// Q: FP8 E4M3 expert weights (one float32 scale per weight row, applied to
-// that row's fp32 result).
-template <int MS, bool Q>
+template <>
+struct W64<2> {
+    uint2 c;
+    float s;
+    __device__ __forceinline__ static W64 load(const void* W, const uint8_t* S, size_t off) {
+        return W64{ldg8(static_cast<const uint8_t*>(W) + off / 2), e8m0_to_f32(ldg1(S + off / 32))};
+    }
+    // the codes only, with a scale byte loaded beforehand
+    __device__ __forceinline__ static W64 load(const void* W, size_t off, uint32_t scale_byte) {
+        return W64{ldg8(static_cast<const uint8_t*>(W) + off / 2), e8m0_to_f32(scale_byte & 0xffu)};
+    }
+    __device__ __forceinline__ static W64 zero() { return W64{uint2{0u, 0u}, 1.0f}; }
+    __device__ __forceinline__ bf16x8 frag(int h) const { return as_bf16x8(fp4x8_to_bf16x8(h ? c.y : c.x, s)); }
+};
+
+// F: the expert weights' format (0 bf16, 1 FP8 E4M3 with one float32 scale
+// per weight row applied to that row's fp32 result, 2 MXFP4).  VS (MXFP4
+// with l % (64 kMxNKB) == 0, m % 128 == 0, MS == 128): the scale bytes of a
+// lane's row are loaded as one vector per batch (2 kMxNKB bytes in phase 1,
+// 4 in phase 2) instead of one byte per block.
+template <int MS, int F, bool VS = false>
 __global__ __launch_bounds__(256) void ffn_stream_kernel(LayerArgs a) {
-    using WB = W64<Q>;
-    using WT = typename WB::WT;
+    static_assert(!VS || (F == 2 && MS == 128), "vector scale loads: MXFP4 with 128-wide slices");
+    using WB = W64<F>;
     const int ai = blockIdx.y;
     if (ai >= *a.n_active) return;
     const int e = a.active[ai];
@@ -193,15 +221,15 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(LayerArgs a) {
     const int l = a.l, m = a.m;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int lr = lane & 15, k16 = 16 * (lane >> 4);
-    const WT* W1e = static_cast<const WT*>(a.W1) + (size_t)e * m * l;
-    const WT* W2e = static_cast<const WT*>(a.W2) + (size_t)e * l * m;
     const bf16* Z = static_cast<const bf16*>(a.z);
     float* Yp = static_cast<float*>(a.ybuf) + (size_t)blockIdx.x * y_plane_elems(a);
 
     constexpr int NB = MS / 16;        // 16-column blocks of the slice
     constexpr int NBW = NB / 4;        // per wave
     constexpr int AST = MS + 8;        // LDS row stride (bf16), padded
-    constexpr int NKB = 2;             // 64-wide k blocks per batch of phase-1 loads
+    // 64-wide k blocks per batch of phase-1 loads (MXFP4 loads move a
+    // quarter of the bf16 bytes per block: more blocks per batch)
+    constexpr int NKB = F == 2 ? kMxNKB : 2;
     __shared__ bf16 As[16 * AST];
 
     for (int rc = r_begin; rc < r_end; rc += 16) {
@@ -209,15 +237,33 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(LayerArgs a) {
         // ---- phase 1: H[16 x MS] = Z[rows] . W1[e][j0 : j0+MS]^T, reduce over l
         const int my_slot = rc + min(lr, nr - 1);
         const bf16* zp = Z + (size_t)(a.perm[my_slot] / a.K) * l + k16;
-        const WT* bp[NBW];
+        size_t w1o[NBW];   // element offset of the lane's W1 row, at its k16
 #pragma unroll
-        for (int b = 0; b < NBW; ++b) bp[b] = W1e + (size_t)(j0 + (wave + 4 * b) * 16 + lr) * l + k16;
+        for (int b = 0; b < NBW; ++b) w1o[b] = ((size_t)e * m + j0 + (wave + 4 * b) * 16 + lr) * l + k16;
         f32x4 acc[NBW];
 #pragma unroll
         for (int b = 0; b < NBW; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
         for (int k0 = 0; k0 < l; k0 += 64 * NKB) {
             uint4 zv[NKB][2];
             WB wv[NKB][NBW];
+            // VS: the row's 2 NKB scale bytes of these 64 NKB k, as 32-bit words
+            constexpr int NW = (2 * NKB + 3) / 4;
+            [[maybe_unused]] uint32_t sv[NBW][NW];
+            if constexpr (VS) {
+#pragma unroll
+                for (int b = 0; b < NBW; ++b) {
+                    const uint8_t* sp = a.w1x + (w1o[b] - k16 + k0) / 32;
+                    if constexpr (NW == 1) {
+                        sv[b][0] = ldg4(sp);
+                    } else if constexpr (NW == 2) {
+                        const uint2 v = ldg8(sp);
+                        sv[b][0] = v.x, sv[b][1] = v.y;
+                    } else {
+                        const uint4 v = ldg16(sp);
+                        sv[b][0] = v.x, sv[b][1] = v.y, sv[b][2] = v.z, sv[b][3] = v.w;
+                    }
+                }
+            }
 #pragma unroll
             for (int p = 0; p < NKB; ++p) {
                 const int kb = k0 + 64 * p;
@@ -225,7 +271,12 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(LayerArgs a) {
                 zv[p][0] = ok ? ldg16(zp + kb) : kZero16;
                 zv[p][1] = ok ? ldg16(zp + kb + 8) : kZero16;
 #pragma unroll
-                for (int b = 0; b < NBW; ++b) wv[p][b] = ok ? WB::load(bp[b] + kb) : WB::zero();
+                for (int b = 0; b < NBW; ++b) {
+                    if constexpr (VS)   // block p, lane group g: scale byte 2p + g / 2
+                        wv[p][b] = WB::load(a.W1, w1o[b] + kb, sv[b][p >> 1] >> (8 * (2 * (p & 1) + (lane >> 5))));
+                    else
+                        wv[p][b] = ok ? WB::load(a.W1, a.w1x, w1o[b] + kb) : WB::zero();
+                }
             }
 #pragma unroll
             for (int p = 0; p < NKB; ++p)
@@ -235,7 +286,7 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(LayerArgs a) {
                     for (int b = 0; b < NBW; ++b)
                         acc[b] = mfma16(as_bf16x8(zv[p][h]), wv[p][b].frag(h), acc[b]);
         }
-        if constexpr (Q) {
+        if constexpr (F == 1) {
             // lane's column j0 + (wave + 4b) * 16 + lr: one W1 row scale
 #pragma unroll
             for (int b = 0; b < NBW; ++b) acc[b] *= a.w1s[(size_t)e * m + j0 + (wave + 4 * b) * 16 + lr];
@@ -256,9 +307,9 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(LayerArgs a) {
         // stores waits for them to complete.
         constexpr int KB = MS / 64;        // 64-wide k blocks of the slice
         constexpr int NU = 4;              // blocks per pass
-        // passes per batch of stores (FP8: 2, which keeps the decode
-        // registers within two waves per SIMD)
-        constexpr int NP = Q ? 2 : 4;
+        // passes per batch of stores (fewer for FP8 and MXFP4, whose decode
+        // registers would otherwise cut the waves per SIMD: 2 and 4 of them)
+        constexpr int NP = F == 0 ? 4 : (F == 1 ? 2 : 1);
         bf16x8 af[KB][2];
 #pragma unroll
         for (int q = 0; q < KB; ++q)
@@ -277,10 +328,18 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(LayerArgs a) {
                 for (int u = 0; u < NU; ++u) {
                     const int ib = ib0 + 4 * (NU * it + u);
                     const bool ok = ib < nblk;
-                    const WT* p = W2e + (size_t)(ib * 16 + lr) * m + j0 + k16;
+                    const size_t w2o = ((size_t)e * l + ib * 16 + lr) * m + j0 + k16;
+                    if constexpr (VS) {
+                        // the row's 4 scale bytes of the slice; block q, lane group g: byte 2q + g / 2
+                        const uint32_t sb = ok ? ldg4(a.w2x + (w2o - k16) / 32) : 0x7f7f7f7fu;
 #pragma unroll
-                    for (int q = 0; q < KB; ++q) wv[u][q] = ok ? WB::load(p + 64 * q) : WB::zero();
-                    if constexpr (Q) {
+                        for (int q = 0; q < KB; ++q)
+                            wv[u][q] = ok ? WB::load(a.W2, w2o + 64 * q, sb >> (8 * (2 * q + (lane >> 5)))) : WB::zero();
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < KB; ++q) wv[u][q] = ok ? WB::load(a.W2, a.w2x, w2o + 64 * q) : WB::zero();
+                    }
+                    if constexpr (F == 1) {
                         // the lane's 4 output rows ib*16 + 4 (lane/16) .. +3 of W2
                         sc[u] = ok ? *reinterpret_cast<const f32x4*>(a.w2s + (size_t)e * l + ib * 16 + 4 * (lane >> 4))
                                    : f32x4{0.f, 0.f, 0.f, 0.f};
@@ -293,7 +352,7 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(LayerArgs a) {
                     for (int q = 0; q < KB; ++q)
 #pragma unroll
                         for (int h = 0; h < 2; ++h) y = mfma16(wv[u][q].frag(h), af[q][h], y);
-                    if constexpr (Q) y *= sc[u];
+                    if constexpr (F == 1) y *= sc[u];
                     yb[it][u] = y;
                 }
             }

@@ -27,6 +27,9 @@ operands of every product):
   W_s1     [m_s, d], W_s2 [d, m_s]   shared expert (the *_shared workloads)
   FP8 experts (the *_fp8 workloads): W1, W2 as uint8 E4M3 codes in the same
   layout, W1_scale [N, m] and W2_scale [N, l] float32 row scales
+  MXFP4 experts (the *_mxfp4 workloads): W1 [N, m, l/2], W2 [N, l, m/2]
+  uint8 (two E2M1 codes per byte, even element in the low nibble),
+  W1_scale [N, m, l/32] and W2_scale [N, l, m/32] uint8 E8M0 block scales
   zero-computation experts (the *_zc workloads): W_router (and bias) get
   n_zero + n_copy + n_const more rows; zc_const [n_const, l]
 
@@ -43,7 +46,11 @@ except the bias is then rounded to bfloat16 (round-to-nearest-even).
 FP8 experts stand for a checkpoint stored that way: each expert's float32
 draw (the same draw as above) is cut into rows, each row gets the scale
 max|row| / 448 (1 for an all-zero row) and its codes are the row divided by
-that scale, rounded to E4M3 by torch's float8_e4m3fn conversion.
+that scale, rounded to E4M3 by torch's float8_e4m3fn conversion.  MXFP4
+experts likewise: each block of 32 elements of a row gets the shared
+exponent floor(log2 max|block|) - 2 (so the block's largest element lands
+in [4, 8) and E2M1's largest value, 6, is reached), and each element is
+rounded to the nearest E2M1 value (ties down, saturating at 6).
 x ~ N(0, 1) throughout, so routing is near uniform except where the fixed
 logit bias ~ N(0, 1) skews the expert loads.
 """
@@ -69,7 +76,8 @@ class Workload:
     standard: bool = False  # no projections: l == d, z = x, out = x + s
     bias: bool = False      # fixed per-expert logit bias ~ N(0, 1)
     m_shared: int = 0       # shared expert width (0: none)
-    experts: str = "dense"  # routed expert weights: "dense" (the layer's dtype) or "fp8" (E4M3 + row scales)
+    experts: str = "dense"  # routed expert weights: "dense" (the layer's dtype), "fp8" (E4M3 + row scales)
+    #                         or "mxfp4" (E2M1 + E8M0 block scales)
     n_zero: int = 0         # zero-computation experts (ids N ...): zero,
     n_copy: int = 0         # copy
     n_const: int = 0        # and constant experts
@@ -113,6 +121,11 @@ WORKLOADS: Dict[str, Workload] = {
                            experts="fp8"),
     "prefill_fp8": Workload("prefill_fp8", T=16384, d=4096, l=1024, N=512, K=22, m=768, dtype="bf16",
                             experts="fp8"),
+    # The decode and prefill layers with MXFP4 routed-expert weights.
+    "decode_mxfp4": Workload("decode_mxfp4", T=32, d=4096, l=1024, N=512, K=22, m=768, dtype="bf16",
+                             experts="mxfp4"),
+    "prefill_mxfp4": Workload("prefill_mxfp4", T=16384, d=4096, l=1024, N=512, K=22, m=768, dtype="bf16",
+                              experts="mxfp4"),
     # The decode and prefill layers with 64 zero-computation experts besides
     # the 512 FFN experts (32 zero, 16 copy, 16 constant): about 11 % of the
     # top-22 picks skip the FFN (the pages report LongCat's average activated
@@ -125,6 +138,32 @@ WORKLOADS: Dict[str, Workload] = {
 
 
 E4M3_MAX = 448.0
+
+
+# E2M1 magnitudes by code (OCP Microscaling spec) and the rounding
+# boundaries between neighbours
+_E2M1 = torch.tensor([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+_E2M1_MID = (_E2M1[1:] + _E2M1[:-1]) / 2
+
+
+def quantize_mxfp4(w: torch.Tensor):
+    """float32 [rows, cols] -> (uint8 codes [rows, cols/2], uint8 E8M0 scales [rows, cols/32])."""
+    rows, cols = w.shape
+    b = w.reshape(rows, cols // 32, 32)
+    amax = b.abs().amax(dim=-1)
+    ex = (torch.floor(torch.log2(amax.clamp_min(2.0 ** -120))) - 2).clamp(-126, 127)
+    q = b / torch.exp2(ex).unsqueeze(-1)
+    idx = torch.bucketize(q.abs(), _E2M1_MID)
+    code = (idx | ((q < 0).to(idx.dtype) << 3)).reshape(rows, cols).to(torch.uint8)
+    packed = code[:, 0::2] | (code[:, 1::2] << 4)
+    return packed.contiguous(), (ex + 127).to(torch.uint8).contiguous()
+
+
+def decode_mxfp4(codes: torch.Tensor, scales: torch.Tensor) -> torch.Tensor:
+    """uint8 codes [..., cols/2], scales [..., cols/32] -> float32 [..., cols]."""
+    nib = torch.stack([codes & 15, codes >> 4], dim=-1).reshape(*codes.shape[:-1], 2 * codes.shape[-1]).long()
+    val = _E2M1[nib & 7] * torch.where((nib & 8) != 0, -1.0, 1.0)
+    return val * torch.exp2(scales.float() - 127).repeat_interleave(32, dim=-1)
 
 
 def quantize_rows_e4m3(w: torch.Tensor):
@@ -161,20 +200,26 @@ def make_inputs(w: Workload, seed: int = 0, *, x_only_seed: Optional[int] = None
     else:
         out["W_down"] = _draw(gen, (w.l, w.d), 1.0 / math.sqrt(w.d)).to(dt)
     out["W_router"] = _draw(gen, (w.N, w.d), 1.0 / math.sqrt(w.d)).to(dt)
-    fp8 = w.experts == "fp8"
-    if w.experts not in ("dense", "fp8") or (fp8 and w.dtype != "bf16"):
+    fp8, mx = w.experts == "fp8", w.experts == "mxfp4"
+    if w.experts not in ("dense", "fp8", "mxfp4") or ((fp8 or mx) and w.dtype != "bf16"):
         raise ValueError(f"experts={w.experts!r} with dtype={w.dtype!r}")
     for name, rows, cols in (("W1", w.m, w.l), ("W2", w.l, w.m)):
-        W = torch.empty((w.N, rows, cols), dtype=torch.uint8 if fp8 else dt)
-        S = torch.empty((w.N, rows), dtype=torch.float32) if fp8 else None
+        if mx:
+            W = torch.empty((w.N, rows, cols // 2), dtype=torch.uint8)
+            S = torch.empty((w.N, rows, cols // 32), dtype=torch.uint8)
+        else:
+            W = torch.empty((w.N, rows, cols), dtype=torch.uint8 if fp8 else dt)
+            S = torch.empty((w.N, rows), dtype=torch.float32) if fp8 else None
         for e in range(w.N):
             we = _draw(gen, (rows, cols), 1.0 / math.sqrt(cols))
-            if fp8:
+            if mx:
+                W[e], S[e] = quantize_mxfp4(we)
+            elif fp8:
                 W[e], S[e] = quantize_rows_e4m3(we)
             else:
                 W[e] = we.to(dt)
         out[name] = W
-        if fp8:
+        if S is not None:
             out[name + "_scale"] = S
     if w.standard:
         out["W_up"] = None

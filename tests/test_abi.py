@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def dims_of(w, path=B.LMOE_PATH_AUTO):
-    fmt = B.LMOE_EXPERTS_FP8_E4M3 if w.experts == "fp8" else B.LMOE_EXPERTS_DENSE
+    fmt = {"dense": B.LMOE_EXPERTS_DENSE, "fp8": B.LMOE_EXPERTS_FP8_E4M3, "mxfp4": B.LMOE_EXPERTS_MXFP4}[w.experts]
     return B.make_dims(w.T, w.d, w.l, w.N, w.m, w.dtype, path, w.m_shared, fmt, w.n_zero, w.n_copy, w.n_const)
 
 
@@ -182,11 +182,27 @@ def test_fp8_expert_argument_checks(lib):
     f32 = dims_of(WORKLOADS["tiny_f32"].replace(experts="fp8"))
     assert call_ex(f32, 4) == B.LMOE_EUNSUPPORTED                         # FP8 experts need bf16
     bad = dims_of(w)
-    bad.expert_format = 2
+    bad.expert_format = 3
     assert B.latentmoe_workspace_bytes(bad, w.K) == 0
     assert call_ex(bad, w.K) == B.LMOE_EINVAL
     assert B.lib().latentmoe_forward_ex(None, w.K, ctypes.byref(d)) == B.LMOE_EINVAL
     assert call_ex(d, w.K, workspace_bytes=100) == B.LMOE_EWORKSPACE
+
+
+def test_mxfp4_expert_argument_checks(lib):
+    w = WORKLOADS["decode_mxfp4"]
+    d = dims_of(w)
+    assert d.expert_format == B.LMOE_EXPERTS_MXFP4
+    assert B.latentmoe_workspace_bytes(d, w.K) == B.latentmoe_workspace_bytes(dims_of(WORKLOADS["decode"]), w.K)
+    assert call_ex(d, w.K, W1_scale=None, W2_scale=None) == B.LMOE_EINVAL   # scales required
+    assert call_ex(d, w.K, W2_scale=None) == B.LMOE_EINVAL
+    # byte scales need no alignment (validation passes them, then the workspace check fails)
+    assert call_ex(d, w.K, W1_scale=FAKE + (10 << 30) + 3, workspace_bytes=64) == B.LMOE_EWORKSPACE
+    f32 = dims_of(WORKLOADS["tiny_f32"].replace(experts="mxfp4"))
+    assert call_ex(f32, 4) == B.LMOE_EUNSUPPORTED
+    big = dims_of(w.replace(m=65536, l=65536))
+    assert B.latentmoe_workspace_bytes(big, w.K) == 0                     # more than 2^31 code bytes
+    assert "MXFP4" in B.latentmoe_last_error()
 
 
 def test_zero_computation_argument_checks(lib):

@@ -214,6 +214,72 @@ def test_fp8_layer_is_the_bf16_layer_on_decoded_weights(path):
     assert torch.equal(a, b)
 
 
+# --- MXFP4 routed-expert weights (E2M1 codes, E8M0 scales per 32) -------------
+
+@pytest.mark.parametrize("path", [B.LMOE_PATH_AUTO, TL])
+def test_decode_mxfp4(path):
+    w = WORKLOADS["decode_mxfp4"]
+    P.compare(w, P.gen(w, 0), w.K, path=path, tag=f"decode_mxfp4/path{path}")
+
+
+def test_prefill_mxfp4_sampled():
+    w = WORKLOADS["prefill_mxfp4"]
+    P.compare(w, P.gen(w, 0), w.K, sample=sample_tokens(w.T, 96))
+
+
+@pytest.mark.parametrize("w", [x.replace(name=x.name.replace("fp8", "mxfp4"), experts="mxfp4") for x in FP8_SHAPES],
+                         ids=lambda w: w.name)
+@pytest.mark.parametrize("path", [B.LMOE_PATH_AUTO, S, TL])
+def test_mxfp4_shapes(w, path):
+    P.compare(w, make_inputs(w, 18), w.K, path=path, tag=f"{w.name}/path{path}")
+
+
+def every_byte_mxfp4(w: Workload, seed: int):
+    """MXFP4 inputs whose code bytes run through all 256 values, with block
+    scales 2^-11 .. 2^-4 that differ from block to block."""
+    inp = make_inputs(w, seed)
+    g = torch.Generator().manual_seed(seed + 1)
+    for name in ("W1", "W2"):
+        n = inp[name].numel()
+        perm = torch.randperm(256, generator=g).to(torch.uint8)
+        inp[name] = perm.repeat(n // 256 + 1)[:n].reshape(inp[name].shape).contiguous()
+        sc = inp[name + "_scale"]
+        inp[name + "_scale"] = torch.randint(116, 124, sc.shape, generator=g).to(torch.uint8)
+    return inp
+
+
+# l = 128: scale bytes loaded one per block; l = 256, m = 256: the streaming
+# FFN's vector scale loads
+MX_POW2 = [Workload("mxfp4_l128", T=120, d=256, l=128, N=16, K=4, m=128, dtype="bf16", experts="mxfp4"),
+           Workload("mxfp4_l256", T=60, d=256, l=256, N=16, K=4, m=256, dtype="bf16", experts="mxfp4")]
+
+
+@pytest.mark.parametrize("w", MX_POW2, ids=lambda w: w.name)
+@pytest.mark.parametrize("path", [S, TL])
+def test_mxfp4_every_byte(w, path):
+    P.compare(w, every_byte_mxfp4(w, 19), w.K, path=path, tag=f"{w.name}_every_byte/path{path}")
+
+
+@pytest.mark.parametrize("w", MX_POW2, ids=lambda w: w.name)
+@pytest.mark.parametrize("path", [S, TL])
+def test_mxfp4_layer_is_the_bf16_layer_on_decoded_weights(w, path):
+    """Every E2M1 value times a power-of-two block scale is a bfloat16 value,
+    so the MXFP4 layer equals, bit for bit, the bf16 layer on the decoded
+    weights (the formats share the MFMA grouping of every dot product)."""
+    from sparse_moe_layer_gemm_amd.inputs import decode_mxfp4
+
+    inp = every_byte_mxfp4(w, 20)
+    dense = dict(inp)
+    for name in ("W1", "W2"):
+        dec = decode_mxfp4(inp[name], dense.pop(name + "_scale"))
+        dense[name] = dec.to(torch.bfloat16).contiguous()
+        assert torch.equal(dense[name].float(), dec)
+    a = B.forward(P.to_device(inp), w.K, path=path)
+    b = B.forward(P.to_device(dense), w.K, path=path)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
 # --- zero-computation experts (zero, copy, constant) --------------------------
 
 def zc_forward(w, inp, path, **kw):
