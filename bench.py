@@ -223,13 +223,21 @@ def measure(w, sets, cpu_seconds: float) -> dict:
                 "achieved": ffn_flops / (ffn_us * 1e-6) / 1e12, "peak": FP32_VECTOR_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "traffic": None}
     else:
+        # FP8 / MXFP4 weights are decoded to bf16 on the way into LDS: the
+        # products run on the bf16 MFMAs, so the bf16 peak is the compute
+        # bound.  The FFN's bound is the one its arithmetic intensity (flops
+        # over the active experts' weight bytes, read once) puts it under.
         ffn_flops = 4.0 * R * w.l * w.m
-        # FP8 weights are decoded to bf16 on the way into LDS: the products
-        # run on the bf16 MFMAs, so the bf16 peak is the bound
+        ffn_bytes = expert_bytes(w, A)
         q = {"dense": "", "fp8": "Q", "mxfp4": "X"}[w.experts]
-        roof = {"kernel": f"gemm2_kernel<Ffn1{q}>+<Ffn2{q}>", "bound": "mfma",
-                "achieved": ffn_flops / (ffn_us * 1e-6) / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "traffic": None}
+        kern = f"gemm2_kernel<Ffn1{q}>+<Ffn2{q}>"
+        if ffn_flops / ffn_bytes >= MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+            roof = {"kernel": kern, "bound": "mfma", "achieved": ffn_flops / (ffn_us * 1e-6) / 1e12,
+                    "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "traffic": None}
+        else:
+            roof = {"kernel": kern, "bound": "hbm", "achieved": ffn_bytes / (ffn_us * 1e-6) / 1e9,
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": None}
+        roof["arithmetic_intensity"] = ffn_flops / ffn_bytes
     roof["traffic"] = measured_traffic(w, roof["kernel"])
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["kernel_us"] = ffn_us
@@ -269,13 +277,16 @@ def measure(w, sets, cpu_seconds: float) -> dict:
 
 
 def measured_traffic(w, kernel: str):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary (FETCH_SIZE + WRITE_SIZE, each scaled by the same counter on a
-    copy of known size), or None when there is none for this workload or the
-    kernel's sources changed since the counters were taken."""
+    """HBM bytes per launch of `kernel` (the FFN: one streaming kernel, or the
+    two tiled GEMMs together) from the committed rocprofv3 counter summary
+    profiles/<kernel>_<workload>_traffic.json (FETCH_SIZE + WRITE_SIZE, each
+    scaled by the same counter on a copy of known size), or None when there
+    is none for this workload or the kernel's sources changed since the
+    counters were taken."""
     import hashlib
 
-    path = os.path.join(ROOT, "profiles", "ffn_stream_decode_traffic.json")
+    tag = "ffn_stream" if kernel.startswith("ffn_stream") else "gemm2_ffn"
+    path = os.path.join(ROOT, "profiles", f"{tag}_{w.name}_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))

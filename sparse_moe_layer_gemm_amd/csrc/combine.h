@@ -80,12 +80,20 @@ __global__ __launch_bounds__(256) void combine_kernel(LayerArgs a, int nsplit, i
                 part[1] = __uint_as_float(raw.y);
                 part[2] = __uint_as_float(raw.z);
                 part[3] = __uint_as_float(raw.w);
-                for (int sp = 1; sp < nsplit; ++sp) {
-                    const uint4 q = ldg16(yp + sp * plane);
-                    part[0] += __uint_as_float(q.x);
-                    part[1] += __uint_as_float(q.y);
-                    part[2] += __uint_as_float(q.z);
-                    part[3] += __uint_as_float(q.w);
+                // the other planes, loaded 8 at a time before they are added
+                // (in plane order)
+                for (int sp0 = 1; sp0 < nsplit; sp0 += 8) {
+                    uint4 q[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) q[i] = sp0 + i < nsplit ? ldg16(yp + (sp0 + i) * plane) : kZero16;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        if (sp0 + i < nsplit) {
+                            part[0] += __uint_as_float(q[i].x);
+                            part[1] += __uint_as_float(q[i].y);
+                            part[2] += __uint_as_float(q[i].z);
+                            part[3] += __uint_as_float(q[i].w);
+                        }
                 }
             }
             const float gk = gated ? gt[k] : 1.0f;

@@ -66,7 +66,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 // The skinny projection's reduction is split into enough k-ranges that the
 // (16-column group, k-range) workgroups cover the CUs; its partial tiles
 // are part[split][T][stride], stride = columns rounded up to 4 floats.
-constexpr int kMaxProjSplit = 16;
+constexpr int kMaxProjSplit = kMaxSplit;   // the top-K kernel adds at most this many partials
 int proj_split(int ncols, int T) {
     return std::max(1, std::min(kMaxProjSplit, 512 / (cdiv(ncols, 16) * cdiv(T, 64))));
 }
@@ -347,7 +347,9 @@ void launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* events
     const unsigned mt = (unsigned)p.max_tiles;
     if constexpr (sizeof(E) == 2) {
         if (p.path == LMOE_PATH_STREAM) {
-            const dim3 g(p.nsplit, a.n_ffn);
+            // (MXFP4 pairs slices across the grid in chunks of 16 workgroups:
+            // a multiple of 8 experts keeps every chunk whole)
+            const dim3 g(p.nsplit, p.wfmt == 2 ? (unsigned)(cdiv(a.n_ffn, 8) * 8) : (unsigned)a.n_ffn);
             auto stream = [&](auto fmt) {
                 constexpr int F = decltype(fmt)::value;
                 p.ms == 128 ? ffn_stream_kernel<128, F><<<g, b256, 0, st>>>(a)

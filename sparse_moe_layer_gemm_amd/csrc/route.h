@@ -44,8 +44,9 @@ __device__ __forceinline__ int popc64(unsigned long long m) { return __popcll(m)
 // LayerArgs::logits (bias included) and z is written.
 struct PartIn {
     const float* part;
-    int nsplit, stride, lz;
+    int nsplit, stride, lz;   // nsplit <= kMaxSplit
 };
+constexpr int kMaxSplit = 16;
 
 // Top-K of token t by one wavefront, from its N logits at lg (global
 // memory or LDS).  s_key / s_idx / s_val: 64 entries of LDS private to the
@@ -63,7 +64,10 @@ __device__ inline void topk_token(const LayerArgs& a, int t, const float* lg, ui
         key[j] = e < a.N ? order_key(v[j]) : 0u;  // padding sorts below every real key
     }
     const int K = a.K;
-    // K-th largest key by bisection on its bits
+    // K-th largest key by bisection on its bits.  It stops early once
+    // exactly K keys reach the candidate: those are the K largest, and tau =
+    // cand selects them below (keys equal to tau are taken as ties).  With a
+    // tie at the K-th key no count equals K and all 32 bits are resolved.
     uint32_t tau = 0;
     for (int bit = 31; bit >= 0; --bit) {
         const uint32_t cand = tau | (1u << bit);
@@ -71,6 +75,7 @@ __device__ inline void topk_token(const LayerArgs& a, int t, const float* lg, ui
 #pragma unroll
         for (int j = 0; j < NPL; ++j) cnt += popc64(__ballot(key[j] >= cand));
         if (cnt >= K) tau = cand;
+        if (cnt == K) break;
     }
     int gt = 0;
 #pragma unroll
@@ -144,15 +149,28 @@ __global__ __launch_bounds__(256) void topk_part_kernel(LayerArgs a, PartIn pin)
     __shared__ float s_val[64];
     const size_t ps = (size_t)a.T * pin.stride;
     const float* pt = pin.part + (size_t)t * pin.stride;
+    // the partials of a value are all loaded before they are added (in split
+    // order), so their latencies overlap
     for (int e = threadIdx.x; e < a.N; e += 256) {
+        float v[kMaxSplit];
+#pragma unroll
+        for (int s = 0; s < kMaxSplit; ++s) v[s] = s < pin.nsplit ? pt[s * ps + pin.lz + e] : 0.0f;
         float acc = 0.0f;
-        for (int s = 0; s < pin.nsplit; ++s) acc += pt[s * ps + pin.lz + e];
+#pragma unroll
+        for (int s = 0; s < kMaxSplit; ++s)
+            if (s < pin.nsplit) acc += v[s];
         lg[e] = a.bias ? acc + a.bias[e] : acc;
     }
     bf16* zo = static_cast<bf16*>(a.z_w) + (size_t)t * a.l;
     for (int c = 4 * threadIdx.x; c < pin.lz; c += 1024) {
-        f32x4 zs = *reinterpret_cast<const f32x4*>(pt + c);
-        for (int s = 1; s < pin.nsplit; ++s) zs += *reinterpret_cast<const f32x4*>(pt + s * ps + c);
+        f32x4 v[kMaxSplit];
+#pragma unroll
+        for (int s = 0; s < kMaxSplit; ++s)
+            v[s] = s < pin.nsplit ? *reinterpret_cast<const f32x4*>(pt + s * ps + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 zs = v[0];
+#pragma unroll
+        for (int s = 1; s < kMaxSplit; ++s)
+            if (s < pin.nsplit) zs += v[s];
         const bf16 b[4] = {(bf16)zs[0], (bf16)zs[1], (bf16)zs[2], (bf16)zs[3]};
         *reinterpret_cast<uint2*>(zo + c) = *reinterpret_cast<const uint2*>(b);
     }

@@ -213,16 +213,34 @@ template <int MS, int F, bool VS = false>
 __global__ __launch_bounds__(256) void ffn_stream_kernel(LayerArgs a) {
     static_assert(!VS || (F == 2 && MS == 128), "vector scale loads: MXFP4 with 128-wide slices");
     using WB = W64<F>;
-    const int ai = blockIdx.y;
+    // Workgroup -> (slice, active expert).  MXFP4 with an even slice count:
+    // a 128-wide slice of a W2 row is 64 bytes, half a 128-byte line, so
+    // slices 2k and 2k+1 of an expert are placed 8 workgroups apart -- on
+    // the same XCD (workgroups go to the 8 XCDs in turn), whose L2 then
+    // fetches each line once.
+    int slice, ai;
+    if constexpr (F == 2) {
+        const int ns = gridDim.x;
+        if (ns % 2 == 0) {
+            const int L = blockIdx.y * ns + blockIdx.x;
+            const int q = (L / 16) * 8 + (L % 8);   // (expert, slice pair) index
+            ai = q / (ns / 2);
+            slice = 2 * (q % (ns / 2)) + (L % 16) / 8;
+        } else {
+            slice = blockIdx.x, ai = blockIdx.y;
+        }
+    } else {
+        slice = blockIdx.x, ai = blockIdx.y;
+    }
     if (ai >= *a.n_active) return;
     const int e = a.active[ai];
-    const int j0 = blockIdx.x * MS;
+    const int j0 = slice * MS;
     const int r_begin = a.offsets[e], r_end = a.offsets[e + 1];
     const int l = a.l, m = a.m;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int lr = lane & 15, k16 = 16 * (lane >> 4);
     const bf16* Z = static_cast<const bf16*>(a.z);
-    float* Yp = static_cast<float*>(a.ybuf) + (size_t)blockIdx.x * y_plane_elems(a);
+    float* Yp = static_cast<float*>(a.ybuf) + (size_t)slice * y_plane_elems(a);
 
     constexpr int NB = MS / 16;        // 16-column blocks of the slice
     constexpr int NBW = NB / 4;        // per wave
