@@ -89,7 +89,7 @@ struct RowCtx<ProjRouter<bf16>> {
     using ColPre = f32x4;
     __device__ static f32x4 col_load(const LayerArgs& a, int, int c0) {
         f32x4 b = {0.0f, 0.0f, 0.0f, 0.0f};
-        const int e0 = c0 - (a.standard ? 0 : a.l);
+        const int e0 = c0 - proj_lz(a) - a.m_s;
         if (a.bias && e0 >= 0)
             for (int i = 0; i < 4; ++i)
                 if (e0 + i < a.N) b[i] = a.bias[e0 + i];
@@ -99,11 +99,17 @@ struct RowCtx<ProjRouter<bf16>> {
     __device__ static NoPre load(const LayerArgs&, int, int, int) { return NoPre{}; }
     __device__ static void store(const LayerArgs& a, int, int r, int c0, f32x4 v, const NoPre&, const f32x4& b,
                                  float) {
-        const int lz = a.standard ? 0 : a.l;
+        const int lz = proj_lz(a), le = lz + a.m_s;
         if (c0 < lz) {
             store_cols(static_cast<bf16*>(a.z_w) + (size_t)r * a.l + c0, c0, lz, v);
+        } else if (c0 < le) {   // the shared expert's relu(h_s)^2
+            for (int i = 0; i < 4; ++i) {
+                const float t = v[i] > 0.0f ? v[i] : 0.0f;
+                v[i] = t * t;
+            }
+            store_cols(static_cast<bf16*>(a.a_s) + (size_t)r * a.m_s + (c0 - lz), c0 - lz, a.m_s, v);
         } else {
-            const int e0 = c0 - lz;
+            const int e0 = c0 - le;
             store_cols(a.logits + (size_t)r * a.N + e0, e0, a.N, v + b);
         }
     }
@@ -211,24 +217,6 @@ template <>
 struct RowCtx<Ffn2X> : RowCtx<Ffn2<bf16, bf16>> {};
 
 template <>
-struct RowCtx<Shared1<bf16>> {
-    static constexpr bool kRowVal = false;
-    __device__ static float row_value(const LayerArgs&, int, int) { return 0.0f; }
-    using ColPre = NoPre;
-    __device__ static NoPre col_load(const LayerArgs&, int, int) { return NoPre{}; }
-    using Pre = NoPre;
-    __device__ static NoPre load(const LayerArgs&, int, int, int) { return NoPre{}; }
-    __device__ static void store(const LayerArgs& a, int, int r, int c0, f32x4 v, const NoPre&, const NoPre&,
-                                 float) {
-        for (int i = 0; i < 4; ++i) {
-            const float t = v[i] > 0.0f ? v[i] : 0.0f;
-            v[i] = t * t;
-        }
-        store_cols(static_cast<bf16*>(a.a_s) + (size_t)r * a.m_s + c0, c0, a.m_s, v);
-    }
-};
-
-template <>
 struct RowCtx<Shared2<bf16>> {
     static constexpr bool kRowVal = false;
     __device__ static float row_value(const LayerArgs&, int, int) { return 0.0f; }
@@ -242,34 +230,10 @@ struct RowCtx<Shared2<bf16>> {
     }
 };
 
-// out = x + W_up s + y_s: the residual row and the shared expert's float32
-// output are loaded together before the stores.
-struct UpSharedPre {
-    uint2 x;
-    f32x4 ys;
-};
-
+// out = x + W_up s + W_s2 a_s: the epilogue of the up-projection (the
+// reduction covers both products).
 template <>
-struct RowCtx<UpShared<bf16>> {
-    static constexpr bool kRowVal = false;
-    __device__ static float row_value(const LayerArgs&, int, int) { return 0.0f; }
-    using ColPre = NoPre;
-    __device__ static NoPre col_load(const LayerArgs&, int, int) { return NoPre{}; }
-    using Pre = UpSharedPre;
-    __device__ static UpSharedPre load(const LayerArgs& a, int, int r, int c0) {
-        const size_t i = (size_t)r * a.d + c0;
-        return UpSharedPre{*reinterpret_cast<const uint2*>(static_cast<const bf16*>(a.x) + i),
-                           *reinterpret_cast<const f32x4*>(a.y_s + i)};
-    }
-    __device__ static void store(const LayerArgs& a, int, int r, int c0, f32x4 v, const UpSharedPre& p,
-                                 const NoPre&, float) {
-        v[0] += __uint_as_float(p.x.x << 16) + p.ys[0];
-        v[1] += __uint_as_float(p.x.x & 0xffff0000u) + p.ys[1];
-        v[2] += __uint_as_float(p.x.y << 16) + p.ys[2];
-        v[3] += __uint_as_float(p.x.y & 0xffff0000u) + p.ys[3];
-        store_cols(static_cast<bf16*>(a.out) + (size_t)r * a.d + c0, c0, a.d, v);
-    }
-};
+struct RowCtx<UpCat<bf16>> : RowCtx<Up<bf16>> {};
 
 template <class P, int BM, int BN, int NWM, int NWN>
 __global__ __launch_bounds__(64 * NWM * NWN) void gemm2_kernel(LayerArgs a, int nrow_tiles, int ncol_tiles) {
@@ -359,15 +323,42 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm2_kernel(LayerArgs a, int 
         }
     };
     set_rows(ct);
+    // Two-segment reductions: at k-step nk1 the cursor's rows switch to the
+    // second operand pair, offset by -k_split so that row + k0 addresses
+    // term k0 - k_split of it (k_split is a multiple of the k-tile).
+    constexpr bool kSeg = HasKSplit<P>::value;
+    [[maybe_unused]] Tile lt = ct;   // the tile the load cursor is on
+    [[maybe_unused]] int nk1 = nk;
+    if constexpr (kSeg) nk1 = P::k_split(a) / kG2K;
+    auto set_rows2 = [&](const Tile& t) {
+        if constexpr (kSeg) {
+            const int ks = P::k_split(a);
+#pragma unroll
+            for (int i = 0; i < S::LA; ++i) {
+                const int r = t.row0 + lrow + S::RSTEP * i;
+                ap[i] = P::a_row2(a, t.grp, r < t.row_end ? r : t.row0) + ch * 8 - ks;
+            }
+#pragma unroll
+            for (int i = 0; i < S::LB; ++i) {
+                const int c = t.col0 + lrow + S::RSTEP * i;
+                bp[i] = P::b_row2(a, t.grp, c < ncols ? c : t.col0) + ch * 8 - ks;
+            }
+        }
+    };
     // past the last tile the cursor stays on a valid k-step that is loaded
     // again and never used
     auto advance_load = [&]() {
-        if (++lkt < nk) return;
+        if (++lkt < nk) {
+            if constexpr (kSeg)
+                if (lkt == nk1) set_rows2(lt);
+            return;
+        }
         Tile nt;
         if (tile_at(lslot + nslot, nt)) {
             lslot += nslot;
             lkt = 0;
             set_rows(nt);
+            if constexpr (kSeg) lt = nt;
         } else {
             lkt = nk - 1;
         }

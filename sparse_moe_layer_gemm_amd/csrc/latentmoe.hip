@@ -207,10 +207,12 @@ Plan make_plan(const lmoe_dims* dm, int32_t K) {
     }
     p.s = take((size_t)d.T * d.l * p.es);
     // partial tiles of the split projection, for either mode (standard mode,
-    // W_down == NULL, is only known at the call: N instead of l + N columns)
+    // W_down == NULL, is only known at the call: m_s + Nr instead of
+    // l + m_s + Nr columns)
     size_t part_bytes = 0;
     if (p.skinny)
-        part_bytes = std::max(proj_part_floats(d.l + p.nr, d.T), proj_part_floats(p.nr, d.T)) * d.T * 4;
+        part_bytes = std::max(proj_part_floats(d.l + d.m_shared + p.nr, d.T),
+                              proj_part_floats(d.m_shared + p.nr, d.T)) * d.T * 4;
     p.part = take(part_bytes);
     p.a_s = take((size_t)d.T * d.m_shared * p.es);
     p.y_s = take(d.m_shared > 0 ? (size_t)d.T * d.d * 4 : 0);
@@ -275,7 +277,8 @@ void launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* events
         if (events && events[i]) hipEventRecord(static_cast<hipEvent_t>(events[i]), st);
     };
     const dim3 b256(256), b1024(1024);
-    const int ncols_pr = (a.standard ? 0 : a.l) + a.N;
+    // projection columns: [z | the shared expert's h_s | logits]
+    const int ncols_pr = (a.standard ? 0 : a.l) + a.m_s + a.N;
     PartIn pin{nullptr, 0, 0, 0};
     float* part = reinterpret_cast<float*>(a.part);
     // 1. projection + router logits
@@ -292,22 +295,12 @@ void launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* events
     } else {
         gemm_simt_kernel<ProjRouter<float>><<<dim3(cdiv(a.T, kSimtM), cdiv(ncols_pr, kSimtN)), b256, 0, st>>>(a);
     }
-    // the shared expert: a_s = relu(W_s1 x)^2, y_s = W_s2 a_s (float32),
-    // added to the output by the up-projection (latent) or the combine
-    if (a.m_s > 0) {
-        if constexpr (sizeof(E) == 2) {
-            if (p.skinny) {
-                skinny_kernel<Shared1<bf16>><<<dim3(cdiv(a.m_s, 16), cdiv(a.T, 64)), b1024, 0, st>>>(a);
-                skinny_kernel<Shared2<bf16>><<<dim3(cdiv(a.d, 16), cdiv(a.T, 64)), b1024, 0, st>>>(a);
-            } else {
-                launch_g2<Shared1<bf16>, G2Small>(a, cdiv(a.T, G2Small::BM), cdiv(a.m_s, G2Small::BN), st);
-                launch_g2<Shared2<bf16>, G2Small>(a, cdiv(a.T, G2Small::BM), cdiv(a.d, G2Small::BN), st);
-            }
-        } else {
-            gemm_simt_kernel<Shared1<float>><<<dim3(cdiv(a.T, kSimtM), cdiv(a.m_s, kSimtN)), b256, 0, st>>>(a);
-            gemm_simt_kernel<Shared2<float>><<<dim3(cdiv(a.T, kSimtM), cdiv(a.d, kSimtN)), b256, 0, st>>>(a);
-        }
-    }
+    // The shared expert's a_s = relu(W_s1 x)^2 comes out of the projection
+    // (its h_s columns).  Its second product: in the bf16 latent layer, part
+    // of the up-projection's reduction (UpCat); otherwise y_s = W_s2 a_s in
+    // float32, added by the up-projection (float32) or the combine
+    // (standard mode).
+    const bool shared_y = a.m_s > 0 && (sizeof(E) == 4 || a.standard);
     // 2. top-K gates
     mark(1);
     {
@@ -331,6 +324,16 @@ void launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* events
             launch_topk(std::integral_constant<int, 24>{});
         else
             launch_topk(std::integral_constant<int, 32>{});
+    }
+    if (shared_y) {
+        if constexpr (sizeof(E) == 2) {
+            if (p.skinny)
+                skinny_kernel<Shared2<bf16>><<<dim3(cdiv(a.d, 16), cdiv(a.T, 64)), b1024, 0, st>>>(a);
+            else
+                launch_g2<Shared2<bf16>, G2Small>(a, cdiv(a.T, G2Small::BM), cdiv(a.d, G2Small::BN), st);
+        } else {
+            gemm_simt_kernel<Shared2<float>><<<dim3(cdiv(a.T, kSimtM), cdiv(a.d, kSimtN)), b256, 0, st>>>(a);
+        }
     }
     // 3. dispatch
     mark(2);
@@ -408,13 +411,14 @@ void launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* events
             gemm_simt_kernel<Up<float>><<<dim3(cdiv(a.T, kSimtM), cdiv(a.d, kSimtN)), b256, 0, st>>>(a);
         }
     } else if (!a.standard) {
-        // with the shared expert's output added in the same epilogue (its
-        // wider per-row operands fit the 128 x 128 tile's registers)
+        // with the shared expert: its second product is the rest of the
+        // up-projection's reduction (bf16), or its float32 output is added
+        // in the epilogue (float32)
         if constexpr (sizeof(E) == 2) {
             if (p.skinny)
-                skinny_kernel<UpShared<bf16>><<<dim3(cdiv(a.d, 16), cdiv(a.T, 64)), b1024, 0, st>>>(a);
+                skinny_kernel<UpCat<bf16>><<<dim3(cdiv(a.d, 16), cdiv(a.T, 64)), b1024, 0, st>>>(a);
             else
-                launch_g2<UpShared<bf16>, G2Small>(a, cdiv(a.T, G2Small::BM), cdiv(a.d, G2Small::BN), st);
+                launch_g2<UpCat<bf16>, UpTile>(a, cdiv(a.T, UpTile::BM), cdiv(a.d, UpTile::BN), st);
         } else {
             gemm_simt_kernel<UpShared<float>><<<dim3(cdiv(a.T, kSimtM), cdiv(a.d, kSimtN)), b256, 0, st>>>(a);
         }
@@ -541,7 +545,9 @@ static int forward_impl(const void* x, const void* W_down, const void* W_router,
     a.s = ws + p.s;
     a.part = ws + p.part;
     a.a_s = d.m_shared > 0 ? ws + p.a_s : nullptr;
-    a.y_s = d.m_shared > 0 ? reinterpret_cast<float*>(ws + p.y_s) : nullptr;
+    // y_s (the shared expert's float32 output) only where it is kept apart:
+    // float32 layers and standard mode
+    a.y_s = (d.m_shared > 0 && (!p.bf16 || standard)) ? reinterpret_cast<float*>(ws + p.y_s) : nullptr;
     a.tile_rows = p.tile_rows;
     a.y_planes = p.nsplit;
     a.y_row_bytes = d.l * (p.path == LMOE_PATH_STREAM ? 4 : (int)p.es);

@@ -6,6 +6,9 @@
 // both operands are read along their contiguous reduction index.
 #pragma once
 
+#include <type_traits>
+#include <utility>
+
 #include "common.h"
 
 namespace lmoe {
@@ -65,8 +68,13 @@ struct LayerArgs {
 __device__ inline size_t y_plane_elems(const LayerArgs& a) { return ((size_t)a.T * a.K + 1) * a.l; }
 
 // ---------------------------------------------------------------------------
-// z = W_down x and logits = W_router x (+ bias), one product over the
-// concatenated columns [z | logits].
+// z = W_down x, the shared expert's a_s = relu(W_s1 x)^2 and logits =
+// W_router x (+ bias): one product of x over the concatenated columns
+// [z | h_s | logits] (z: l columns, none in standard mode; h_s: m_s
+// columns, none without a shared expert; both multiples of 64, so no group
+// of 4 columns straddles two parts).
+
+__device__ inline int proj_lz(const LayerArgs& a) { return a.standard ? 0 : a.l; }
 
 template <class E>
 struct ProjRouter {
@@ -79,22 +87,26 @@ struct ProjRouter {
     }
     // row tiles of this launch: the host's count
     __device__ static int row_tiles(const LayerArgs&, int host_count) { return host_count; }
-    __device__ static int ncols(const LayerArgs& a) { return (a.standard ? 0 : a.l) + a.N; }
+    __device__ static int ncols(const LayerArgs& a) { return proj_lz(a) + a.m_s + a.N; }
     __device__ static int kdim(const LayerArgs& a) { return a.d; }
     __device__ static const E* a_row(const LayerArgs& a, int, int r) {
         return static_cast<const E*>(a.x) + (size_t)r * a.d;
     }
     __device__ static const E* b_row(const LayerArgs& a, int, int c) {
-        const int lz = a.standard ? 0 : a.l;
-        return c < lz ? static_cast<const E*>(a.W_down) + (size_t)c * a.d
-                      : static_cast<const E*>(a.W_router) + (size_t)(c - lz) * a.d;
+        const int lz = proj_lz(a), le = lz + a.m_s;
+        return c < lz   ? static_cast<const E*>(a.W_down) + (size_t)c * a.d
+               : c < le ? static_cast<const E*>(a.W_s1) + (size_t)(c - lz) * a.d
+                        : static_cast<const E*>(a.W_router) + (size_t)(c - le) * a.d;
     }
     __device__ static void store(const LayerArgs& a, int, int r, int c, float v) {
-        const int lz = a.standard ? 0 : a.l;
+        const int lz = proj_lz(a), le = lz + a.m_s;
         if (c < lz) {
             static_cast<E*>(a.z_w)[(size_t)r * a.l + c] = from_f32<E>(v);
+        } else if (c < le) {
+            const float t = v > 0.0f ? v : 0.0f;
+            static_cast<E*>(a.a_s)[(size_t)r * a.m_s + (c - lz)] = from_f32<E>(t * t);
         } else {
-            const int e = c - lz;
+            const int e = c - le;
             a.logits[(size_t)r * a.N + e] = v + (a.bias ? a.bias[e] : 0.0f);
         }
     }
@@ -178,28 +190,6 @@ struct Up {
     }
 };
 
-// Shared expert, first product: a_s = relu(W_s1 x)^2 over all tokens.
-template <class E>
-struct Shared1 {
-    using BElem = E;   // element type of the B (weight) rows
-    __device__ static bool tile(const LayerArgs& a, int bx, int bm, int& grp, int& row0, int& row_end) {
-        return Up<E>::tile(a, bx, bm, grp, row0, row_end);
-    }
-    __device__ static int row_tiles(const LayerArgs&, int host_count) { return host_count; }
-    __device__ static int ncols(const LayerArgs& a) { return a.m_s; }
-    __device__ static int kdim(const LayerArgs& a) { return a.d; }
-    __device__ static const E* a_row(const LayerArgs& a, int, int r) {
-        return static_cast<const E*>(a.x) + (size_t)r * a.d;
-    }
-    __device__ static const E* b_row(const LayerArgs& a, int, int c) {
-        return static_cast<const E*>(a.W_s1) + (size_t)c * a.d;
-    }
-    __device__ static void store(const LayerArgs& a, int, int r, int c, float v) {
-        const float t = v > 0.0f ? v : 0.0f;
-        static_cast<E*>(a.a_s)[(size_t)r * a.m_s + c] = from_f32<E>(t * t);
-    }
-};
-
 // Shared expert, second product: y_s = W_s2 a_s, kept in float32 so that the
 // layer's output is still rounded once (in the up-projection or combine).
 template <class E>
@@ -220,7 +210,37 @@ struct Shared2 {
     __device__ static void store(const LayerArgs& a, int, int r, int c, float v) { a.y_s[(size_t)r * a.d + c] = v; }
 };
 
-// out = x + W_up s + y_s (latent mode with a shared expert), one rounding.
+// Problems whose reduction runs over two operand pairs (UpCat): k_split(a)
+// terms from a_row / b_row, then the rest from a_row2 / b_row2.
+template <class P, class = void>
+struct HasKSplit : std::false_type {};
+template <class P>
+struct HasKSplit<P, decltype((void)P::k_split(std::declval<const LayerArgs&>()))> : std::true_type {};
+template <class P>
+__device__ inline int k_first(const LayerArgs& a) {
+    if constexpr (HasKSplit<P>::value)
+        return P::k_split(a);
+    else
+        return P::kdim(a);
+}
+
+// out = x + W_up s + W_s2 a_s (latent mode with a shared expert): one
+// product whose reduction runs over l terms of [W_up | s], then m_s terms of
+// [W_s2 | a_s] (k_split = l), residual added and rounded once.
+template <class E>
+struct UpCat : Up<E> {
+    __device__ static int kdim(const LayerArgs& a) { return a.l + a.m_s; }
+    __device__ static int k_split(const LayerArgs& a) { return a.l; }
+    __device__ static const E* a_row2(const LayerArgs& a, int, int r) {
+        return static_cast<const E*>(a.a_s) + (size_t)r * a.m_s;
+    }
+    __device__ static const E* b_row2(const LayerArgs& a, int, int c) {
+        return static_cast<const E*>(a.W_s2) + (size_t)c * a.m_s;
+    }
+};
+
+// out = x + W_up s + y_s (latent mode with a shared expert, float32 path:
+// y_s computed beforehand), one rounding.
 template <class E>
 struct UpShared : Up<E> {
     __device__ static void store(const LayerArgs& a, int, int r, int c, float v) {

@@ -39,9 +39,9 @@ __device__ __forceinline__ uint32_t order_key(float v) {
 __device__ __forceinline__ int popc64(unsigned long long m) { return __popcll(m); }
 
 // Split-reduction input of the top-K kernel: nsplit fp32 partial tiles
-// part[s][T][stride] of [z | logits] (lz + N columns, rows padded to a
-// multiple of 4 floats).  nsplit = 0: the logits are already in
-// LayerArgs::logits (bias included) and z is written.
+// part[s][T][stride] of [z | h_s | logits] (lz + m_s + N columns, rows
+// padded to a multiple of 4 floats).  nsplit = 0: the logits are already in
+// LayerArgs::logits (bias included), and z and a_s are written.
 struct PartIn {
     const float* part;
     int nsplit, stride, lz;   // nsplit <= kMaxSplit
@@ -151,18 +151,22 @@ __global__ __launch_bounds__(256) void topk_part_kernel(LayerArgs a, PartIn pin)
     const float* pt = pin.part + (size_t)t * pin.stride;
     // the partials of a value are all loaded before they are added (in split
     // order), so their latencies overlap
+    const int le = pin.lz + a.m_s;   // first logit column
     for (int e = threadIdx.x; e < a.N; e += 256) {
         float v[kMaxSplit];
 #pragma unroll
-        for (int s = 0; s < kMaxSplit; ++s) v[s] = s < pin.nsplit ? pt[s * ps + pin.lz + e] : 0.0f;
+        for (int s = 0; s < kMaxSplit; ++s) v[s] = s < pin.nsplit ? pt[s * ps + le + e] : 0.0f;
         float acc = 0.0f;
 #pragma unroll
         for (int s = 0; s < kMaxSplit; ++s)
             if (s < pin.nsplit) acc += v[s];
         lg[e] = a.bias ? acc + a.bias[e] : acc;
     }
+    // z (columns [0, lz)) and the shared expert's relu(h_s)^2 (columns
+    // [lz, le)), rounded once to bf16
     bf16* zo = static_cast<bf16*>(a.z_w) + (size_t)t * a.l;
-    for (int c = 4 * threadIdx.x; c < pin.lz; c += 1024) {
+    bf16* so = a.m_s > 0 ? static_cast<bf16*>(a.a_s) + (size_t)t * a.m_s - pin.lz : nullptr;
+    for (int c = 4 * threadIdx.x; c < le; c += 1024) {
         f32x4 v[kMaxSplit];
 #pragma unroll
         for (int s = 0; s < kMaxSplit; ++s)
@@ -171,8 +175,15 @@ __global__ __launch_bounds__(256) void topk_part_kernel(LayerArgs a, PartIn pin)
 #pragma unroll
         for (int s = 1; s < kMaxSplit; ++s)
             if (s < pin.nsplit) zs += v[s];
+        if (c >= pin.lz) {   // (lz is a multiple of 64: no group of 4 straddles it)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float r = zs[i] > 0.0f ? zs[i] : 0.0f;
+                zs[i] = r * r;
+            }
+        }
         const bf16 b[4] = {(bf16)zs[0], (bf16)zs[1], (bf16)zs[2], (bf16)zs[3]};
-        *reinterpret_cast<uint2*>(zo + c) = *reinterpret_cast<const uint2*>(b);
+        *reinterpret_cast<uint2*>((c < pin.lz ? zo : so) + c) = *reinterpret_cast<const uint2*>(b);
     }
     __syncthreads();
     if (threadIdx.x < 64) topk_token<NPL>(a, t, lg, s_key, s_idx, s_val);

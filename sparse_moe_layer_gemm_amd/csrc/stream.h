@@ -34,11 +34,9 @@ template <class P>
 __global__ __launch_bounds__(1024) void skinny_kernel(LayerArgs a) {
     const int c0 = blockIdx.x * 16, r0 = blockIdx.y * 64;   // 16 columns x a group of 64 rows
     const int ncols = P::ncols(a), K = P::kdim(a);
+    const int K1 = k_first<P>(a);   // terms of the first operand pair (a multiple of 32)
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int nrb = min(4, cdiv(a.T - r0, 16));
-    const int ksteps = K / 32;
-    const int per = cdiv(ksteps, kSkinnyWaves);
-    const int ks0 = wave * per, ks1 = min(ksteps, ks0 + per);
     const int c = c0 + (lane & 15);
     const int koff = 8 * (lane >> 4);
     const bf16* bp = c < ncols ? P::b_row(a, 0, c) + koff : nullptr;
@@ -52,21 +50,40 @@ __global__ __launch_bounds__(1024) void skinny_kernel(LayerArgs a) {
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int ks = ks0; ks < ks1; ks += 4) {
-        uint4 bv[4], av[4][4];
+    // k-steps [kb, ke) of 32 terms from rows b / ar (offset so that row + k0
+    // addresses term k0)
+    auto run = [&](const bf16* b, const bf16* const* ar, int kb, int ke) {
+        for (int ks = kb; ks < ke; ks += 4) {
+            uint4 bv[4], av[4][4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int k0 = (ks + u) * 32;
-            const bool ok = ks + u < ks1;
-            bv[u] = (ok && bp) ? ldg16(bp + k0) : kZero16;
+            for (int u = 0; u < 4; ++u) {
+                const int k0 = (ks + u) * 32;
+                const bool ok = ks + u < ke;
+                bv[u] = (ok && b) ? ldg16(b + k0) : kZero16;
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb) av[u][rb] = (ok && ap[rb]) ? ldg16(ap[rb] + k0) : kZero16;
+                for (int rb = 0; rb < 4; ++rb) av[u][rb] = (ok && ar[rb]) ? ldg16(ar[rb] + k0) : kZero16;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int rb = 0; rb < 4; ++rb)
+                    if (rb < nrb) acc[rb] = mfma16(as_bf16x8(av[u][rb]), as_bf16x8(bv[u]), acc[rb]);
         }
+    };
+    // the waves split each operand pair's k-steps evenly (the first pair's
+    // split is the same as without a second pair)
+    const int k1s = K1 / 32, per1 = cdiv(k1s, kSkinnyWaves);
+    run(bp, ap, wave * per1, min(k1s, wave * per1 + per1));
+    if constexpr (HasKSplit<P>::value) {
+        const bf16* bp2 = bp ? P::b_row2(a, 0, c) + koff - K1 : nullptr;
+        const bf16* ap2[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb)
-                if (rb < nrb) acc[rb] = mfma16(as_bf16x8(av[u][rb]), as_bf16x8(bv[u]), acc[rb]);
+        for (int rb = 0; rb < 4; ++rb) {
+            const int r = r0 + rb * 16 + (lane & 15);
+            ap2[rb] = ap[rb] ? P::a_row2(a, 0, r) + koff - K1 : nullptr;
+        }
+        const int k2s = (K - K1) / 32, per2 = cdiv(k2s, kSkinnyWaves);
+        run(bp2, ap2, k1s + wave * per2, min(k1s + k2s, k1s + wave * per2 + per2));
     }
 
     __shared__ f32x4 red[kSkinnyWaves][4][64];
