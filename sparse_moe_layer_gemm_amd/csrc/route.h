@@ -343,12 +343,20 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(LayerArgs a, int nb
     int* off = cnt + a.N;
     int* tmp = off + a.N;
     int* wsum = tmp + a.N;
+    // each thread scans its expert's per-block counts, 8 blocks' counts
+    // loaded at a time so that their latencies overlap
     for (int e = threadIdx.x; e < a.N; e += blockDim.x) {
         int run = 0;
-        for (int b = 0; b < nblk; ++b) {
-            const int c = a.blk_counts[(size_t)b * a.N + e];
-            a.blk_offsets[(size_t)b * a.N + e] = run;
-            run += c;
+        for (int b0 = 0; b0 < nblk; b0 += 8) {
+            int c[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) c[i] = b0 + i < nblk ? a.blk_counts[(size_t)(b0 + i) * a.N + e] : 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (b0 + i < nblk) {
+                    a.blk_offsets[(size_t)(b0 + i) * a.N + e] = run;
+                    run += c[i];
+                }
         }
         cnt[e] = run;
     }
