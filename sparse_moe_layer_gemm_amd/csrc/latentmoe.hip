@@ -360,8 +360,8 @@ void launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* events
             };
             if (p.wfmt == 1)
                 stream(std::integral_constant<int, 1>{});
-            else if (p.wfmt == 2 && p.ms == 128 && a.l % (64 * kMxNKB) == 0 && a.m % 128 == 0)
-                ffn_stream_kernel<128, 2, true><<<g, b256, 0, st>>>(a);   // vector scale loads
+            else if (p.wfmt == 2 && p.ms == 128 && a.l % 256 == 0 && a.m % 128 == 0)
+                ffn_stream_mx_kernel<<<g, b256, 0, st>>>(a);   // 16-byte code loads
             else if (p.wfmt == 2)
                 stream(std::integral_constant<int, 2>{});
             else

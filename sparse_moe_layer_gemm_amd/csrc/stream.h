@@ -12,13 +12,15 @@
 //     reduction and add their partial tiles through LDS.
 //   skinny_part_kernel<P>: the same, with the reduction also split over
 //     workgroups (fp32 partial tiles added by the consumer).
-//   ffn_stream_kernel<MS>: the expert FFN.  Workgroup (s, a) takes active
-//     expert a and the m-slice [s*MS, (s+1)*MS): it computes
+//   ffn_stream_kernel<MS, F>: the expert FFN.  Workgroup (s, a) takes
+//     active expert a and the m-slice [s*MS, (s+1)*MS): it computes
 //     relu(W1[e][slice] z)^2 for up to 16 routed rows at a time, keeps it in
 //     LDS, and multiplies it by the matching column slice of W2[e], writing
 //     an fp32 partial expert output per slice.  Every weight byte of an
 //     active expert is read once per 16 rows; no atomics: the combine adds
-//     the slices in a fixed order.
+//     the slices in a fixed order.  F: bf16, FP8 or MXFP4 weights.
+//   ffn_stream_mx_kernel: the same for MXFP4 weights with 16-byte code
+//     loads (32 codes per lane), for the usual shapes.
 #pragma once
 
 #include <type_traits>
@@ -177,9 +179,6 @@ __global__ __launch_bounds__(256) void skinny_part_kernel(LayerArgs a, float* pa
 //   F = 2, MXFP4: one 8-byte load of 16 E2M1 codes and their block's E8M0
 //          scale byte (16 consecutive terms lie in one 32-element block),
 //          decoded and scaled to bf16 in registers.
-// MXFP4: 64-wide k blocks per batch of phase-1 loads
-constexpr int kMxNKB = 4;
-
 template <int F>
 struct W64;
 
@@ -213,42 +212,39 @@ struct W64<2> {
     __device__ __forceinline__ static W64 load(const void* W, const uint8_t* S, size_t off) {
         return W64{ldg8(static_cast<const uint8_t*>(W) + off / 2), e8m0_to_f32(ldg1(S + off / 32))};
     }
-    // the codes only, with a scale byte loaded beforehand
-    __device__ __forceinline__ static W64 load(const void* W, size_t off, uint32_t scale_byte) {
-        return W64{ldg8(static_cast<const uint8_t*>(W) + off / 2), e8m0_to_f32(scale_byte & 0xffu)};
-    }
     __device__ __forceinline__ static W64 zero() { return W64{uint2{0u, 0u}, 1.0f}; }
     __device__ __forceinline__ bf16x8 frag(int h) const { return as_bf16x8(fp4x8_to_bf16x8(h ? c.y : c.x, s)); }
 };
 
-// F: the expert weights' format (0 bf16, 1 FP8 E4M3 with one float32 scale
-// per weight row applied to that row's fp32 result, 2 MXFP4).  VS (MXFP4
-// with l % (64 kMxNKB) == 0, m % 128 == 0, MS == 128): the scale bytes of a
-// lane's row are loaded as one vector per batch (2 kMxNKB bytes in phase 1,
-// 4 in phase 2) instead of one byte per block.
-template <int MS, int F, bool VS = false>
-__global__ __launch_bounds__(256) void ffn_stream_kernel(LayerArgs a) {
-    static_assert(!VS || (F == 2 && MS == 128), "vector scale loads: MXFP4 with 128-wide slices");
-    using WB = W64<F>;
-    // Workgroup -> (slice, active expert).  MXFP4 with an even slice count:
-    // a 128-wide slice of a W2 row is 64 bytes, half a 128-byte line, so
-    // slices 2k and 2k+1 of an expert are placed 8 workgroups apart -- on
-    // the same XCD (workgroups go to the 8 XCDs in turn), whose L2 then
-    // fetches each line once.
-    int slice, ai;
-    if constexpr (F == 2) {
-        const int ns = gridDim.x;
-        if (ns % 2 == 0) {
-            const int L = blockIdx.y * ns + blockIdx.x;
-            const int q = (L / 16) * 8 + (L % 8);   // (expert, slice pair) index
-            ai = q / (ns / 2);
-            slice = 2 * (q % (ns / 2)) + (L % 16) / 8;
-        } else {
-            slice = blockIdx.x, ai = blockIdx.y;
-        }
+// Workgroup -> (slice, active expert) for MXFP4 experts.  With an even
+// slice count, slices 2k and 2k+1 of an expert are placed 8 workgroups
+// apart -- on the same XCD (workgroups go to the 8 XCDs in turn): a 128-wide
+// slice of an MXFP4 W2 row is 64 bytes, half a 128-byte line, and that
+// XCD's L2 then fetches each line once.  The grid's y extent is a multiple
+// of 8 (every chunk of 16 workgroups whole).
+__device__ inline void paired_slices(int& slice, int& ai) {
+    const int ns = gridDim.x;
+    if (ns % 2 == 0) {
+        const int L = blockIdx.y * ns + blockIdx.x;
+        const int q = (L / 16) * 8 + (L % 8);   // (expert, slice pair) index
+        ai = q / (ns / 2);
+        slice = 2 * (q % (ns / 2)) + (L % 16) / 8;
     } else {
         slice = blockIdx.x, ai = blockIdx.y;
     }
+}
+
+// F: the expert weights' format (0 bf16, 1 FP8 E4M3 with one float32 scale
+// per weight row applied to that row's fp32 result, 2 MXFP4 -- the shapes
+// ffn_stream_mx_kernel does not take).
+template <int MS, int F>
+__global__ __launch_bounds__(256) void ffn_stream_kernel(LayerArgs a) {
+    using WB = W64<F>;
+    int slice, ai;
+    if constexpr (F == 2)
+        paired_slices(slice, ai);
+    else
+        slice = blockIdx.x, ai = blockIdx.y;
     if (ai >= *a.n_active) return;
     const int e = a.active[ai];
     const int j0 = slice * MS;
@@ -264,7 +260,7 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(LayerArgs a) {
     constexpr int AST = MS + 8;        // LDS row stride (bf16), padded
     // 64-wide k blocks per batch of phase-1 loads (MXFP4 loads move a
     // quarter of the bf16 bytes per block: more blocks per batch)
-    constexpr int NKB = F == 2 ? kMxNKB : 2;
+    constexpr int NKB = F == 2 ? 4 : 2;
     __shared__ bf16 As[16 * AST];
 
     for (int rc = r_begin; rc < r_end; rc += 16) {
@@ -281,24 +277,6 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(LayerArgs a) {
         for (int k0 = 0; k0 < l; k0 += 64 * NKB) {
             uint4 zv[NKB][2];
             WB wv[NKB][NBW];
-            // VS: the row's 2 NKB scale bytes of these 64 NKB k, as 32-bit words
-            constexpr int NW = (2 * NKB + 3) / 4;
-            [[maybe_unused]] uint32_t sv[NBW][NW];
-            if constexpr (VS) {
-#pragma unroll
-                for (int b = 0; b < NBW; ++b) {
-                    const uint8_t* sp = a.w1x + (w1o[b] - k16 + k0) / 32;
-                    if constexpr (NW == 1) {
-                        sv[b][0] = ldg4(sp);
-                    } else if constexpr (NW == 2) {
-                        const uint2 v = ldg8(sp);
-                        sv[b][0] = v.x, sv[b][1] = v.y;
-                    } else {
-                        const uint4 v = ldg16(sp);
-                        sv[b][0] = v.x, sv[b][1] = v.y, sv[b][2] = v.z, sv[b][3] = v.w;
-                    }
-                }
-            }
 #pragma unroll
             for (int p = 0; p < NKB; ++p) {
                 const int kb = k0 + 64 * p;
@@ -306,12 +284,7 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(LayerArgs a) {
                 zv[p][0] = ok ? ldg16(zp + kb) : kZero16;
                 zv[p][1] = ok ? ldg16(zp + kb + 8) : kZero16;
 #pragma unroll
-                for (int b = 0; b < NBW; ++b) {
-                    if constexpr (VS)   // block p, lane group g: scale byte 2p + g / 2
-                        wv[p][b] = WB::load(a.W1, w1o[b] + kb, sv[b][p >> 1] >> (8 * (2 * (p & 1) + (lane >> 5))));
-                    else
-                        wv[p][b] = ok ? WB::load(a.W1, a.w1x, w1o[b] + kb) : WB::zero();
-                }
+                for (int b = 0; b < NBW; ++b) wv[p][b] = ok ? WB::load(a.W1, a.w1x, w1o[b] + kb) : WB::zero();
             }
 #pragma unroll
             for (int p = 0; p < NKB; ++p)
@@ -364,16 +337,8 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(LayerArgs a) {
                     const int ib = ib0 + 4 * (NU * it + u);
                     const bool ok = ib < nblk;
                     const size_t w2o = ((size_t)e * l + ib * 16 + lr) * m + j0 + k16;
-                    if constexpr (VS) {
-                        // the row's 4 scale bytes of the slice; block q, lane group g: byte 2q + g / 2
-                        const uint32_t sb = ok ? ldg4(a.w2x + (w2o - k16) / 32) : 0x7f7f7f7fu;
 #pragma unroll
-                        for (int q = 0; q < KB; ++q)
-                            wv[u][q] = ok ? WB::load(a.W2, w2o + 64 * q, sb >> (8 * (2 * q + (lane >> 5)))) : WB::zero();
-                    } else {
-#pragma unroll
-                        for (int q = 0; q < KB; ++q) wv[u][q] = ok ? WB::load(a.W2, a.w2x, w2o + 64 * q) : WB::zero();
-                    }
+                    for (int q = 0; q < KB; ++q) wv[u][q] = ok ? WB::load(a.W2, a.w2x, w2o + 64 * q) : WB::zero();
                     if constexpr (F == 1) {
                         // the lane's 4 output rows ib*16 + 4 (lane/16) .. +3 of W2
                         sc[u] = ok ? *reinterpret_cast<const f32x4*>(a.w2s + (size_t)e * l + ib * 16 + 4 * (lane >> 4))
@@ -401,6 +366,123 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(LayerArgs a) {
                             *reinterpret_cast<f32x4*>(&Yp[(size_t)(rc + lr) * l + ib * 16 + 4 * (lane >> 4)]) =
                                 yb[it][u];
                     }
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// MXFP4 experts, 16-byte code loads: lane group g = lane / 16 takes the 32
+// consecutive terms 32g .. 32g+31 of each 128-wide k block -- 16 code bytes,
+// all in one 32-element scale block -- and word q of them (terms 32g + 8q ..
+// +7) goes to MFMA q of the block.  Each load instruction then reads 64
+// contiguous bytes of each of 16 weight rows, with as many bytes per
+// instruction as the FP8 kernel.  (This groups the dot products' terms
+// differently from ffn_stream_kernel.)  Needs 128-wide m-slices,
+// l % 256 == 0 and m % 128 == 0; the scale bytes of a lane's row come as
+// one vector per batch (8 bytes in phase 1, 4 in phase 2).
+__global__ __launch_bounds__(256) void ffn_stream_mx_kernel(LayerArgs a) {
+    constexpr int MS = 128, NBW = 2, AST = MS + 8;
+    constexpr int NSB = 2;   // 128-wide k blocks per batch of phase-1 loads
+    int slice, ai;
+    paired_slices(slice, ai);
+    if (ai >= *a.n_active) return;
+    const int e = a.active[ai];
+    const int j0 = slice * MS;
+    const int r_begin = a.offsets[e], r_end = a.offsets[e + 1];
+    const int l = a.l, m = a.m;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int lr = lane & 15, g = lane >> 4;
+    const uint8_t* W1 = static_cast<const uint8_t*>(a.W1);
+    const uint8_t* W2 = static_cast<const uint8_t*>(a.W2);
+    const bf16* Z = static_cast<const bf16*>(a.z);
+    float* Yp = static_cast<float*>(a.ybuf) + (size_t)slice * y_plane_elems(a);
+    __shared__ bf16 As[16 * AST];
+    auto decode = [](uint32_t word, uint32_t scale_byte) {
+        return as_bf16x8(fp4x8_to_bf16x8(word, e8m0_to_f32(scale_byte & 0xffu)));
+    };
+
+    for (int rc = r_begin; rc < r_end; rc += 16) {
+        const int nr = min(16, r_end - rc);
+        // ---- phase 1: H[16 x MS] = Z[rows] . W1[e][j0 : j0+MS]^T, reduce over l
+        const int my_slot = rc + min(lr, nr - 1);
+        const bf16* zp = Z + (size_t)(a.perm[my_slot] / a.K) * l + 32 * g;
+        size_t w1e[NBW];   // element offset of the lane's W1 row
+#pragma unroll
+        for (int b = 0; b < NBW; ++b) w1e[b] = ((size_t)e * m + j0 + (wave + 4 * b) * 16 + lr) * l;
+        f32x4 acc[NBW];
+#pragma unroll
+        for (int b = 0; b < NBW; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int k0 = 0; k0 < l; k0 += 128 * NSB) {   // l % 256 == 0: every block is whole
+            uint2 sv[NBW];          // the row's 8 scale bytes of these 256 terms
+            uint4 cv[NSB][NBW];     // 32 codes per block and row
+            uint4 zv[NSB][4];       // the matching 32 terms of z
+#pragma unroll
+            for (int b = 0; b < NBW; ++b) sv[b] = ldg8(a.w1x + (w1e[b] + k0) / 32);
+#pragma unroll
+            for (int sb = 0; sb < NSB; ++sb) {
+                const int kb = k0 + 128 * sb;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) zv[sb][q] = ldg16(zp + kb + 8 * q);
+#pragma unroll
+                for (int b = 0; b < NBW; ++b) cv[sb][b] = ldg16(W1 + (w1e[b] + kb) / 2 + 16 * g);
+            }
+#pragma unroll
+            for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+                for (int b = 0; b < NBW; ++b) {
+                    // block sb, lane group g: scale byte 4 sb + g
+                    const uint32_t sc = (sb == 0 ? sv[b].x : sv[b].y) >> (8 * g);
+                    const uint32_t w[4] = {cv[sb][b].x, cv[sb][b].y, cv[sb][b].z, cv[sb][b].w};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) acc[b] = mfma16(as_bf16x8(zv[sb][q]), decode(w[q], sc), acc[b]);
+                }
+        }
+#pragma unroll
+        for (int b = 0; b < NBW; ++b)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float h = acc[b][r] > 0.0f ? acc[b][r] : 0.0f;
+                As[(4 * (lane >> 4) + r) * AST + (wave + 4 * b) * 16 + lr] = (bf16)(h * h);
+            }
+        __syncthreads();
+        // ---- phase 2: Y[16 x l] = A[16 x MS] . W2[e][:, j0 : j0+MS]^T, the
+        // weight fragment as the MFMA's first operand (lane l: output columns
+        // i0 + 4 (l / 16) .. +3 of row l % 16, one 16-byte store), one pass
+        // of NU blocks of 16 output columns per batch of stores
+        constexpr int NU = 4;
+        bf16x8 af[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) af[q] = *reinterpret_cast<const bf16x8*>(&As[lr * AST + 32 * g + 8 * q]);
+        const int nblk = l / 16;
+        for (int ib0 = wave; ib0 < nblk; ib0 += 4 * NU) {
+            uint4 cv[NU];
+            uint32_t sb[NU];
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+                const int ib = ib0 + 4 * u;
+                const bool ok = ib < nblk;
+                const size_t w2e = ((size_t)e * l + ib * 16 + lr) * m + j0;   // the row's slice
+                cv[u] = ok ? ldg16(W2 + w2e / 2 + 16 * g) : kZero16;
+                sb[u] = ok ? ldg4(a.w2x + w2e / 32) : 0x7f7f7f7fu;
+            }
+            f32x4 yb[NU];
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+                const uint32_t sc = sb[u] >> (8 * g);
+                const uint32_t w[4] = {cv[u].x, cv[u].y, cv[u].z, cv[u].w};
+                f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) y = mfma16(decode(w[q], sc), af[q], y);
+                yb[u] = y;
+            }
+            if (lr < nr) {
+#pragma unroll
+                for (int u = 0; u < NU; ++u) {
+                    const int ib = ib0 + 4 * u;
+                    if (ib < nblk)
+                        *reinterpret_cast<f32x4*>(&Yp[(size_t)(rc + lr) * l + ib * 16 + 4 * (lane >> 4)]) = yb[u];
+                }
             }
         }
         __syncthreads();

@@ -248,8 +248,9 @@ def every_byte_mxfp4(w: Workload, seed: int):
     return inp
 
 
-# l = 128: scale bytes loaded one per block; l = 256, m = 256: the streaming
-# FFN's vector scale loads
+# l = 128: the streaming FFN shared with bf16 and FP8 (8-byte code loads, a
+# scale byte per block); l = 256, m = 256: the MXFP4 streaming kernel with
+# 16-byte code loads
 MX_POW2 = [Workload("mxfp4_l128", T=120, d=256, l=128, N=16, K=4, m=128, dtype="bf16", experts="mxfp4"),
            Workload("mxfp4_l256", T=60, d=256, l=256, N=16, K=4, m=256, dtype="bf16", experts="mxfp4")]
 
@@ -264,8 +265,11 @@ def test_mxfp4_every_byte(w, path):
 @pytest.mark.parametrize("path", [S, TL])
 def test_mxfp4_layer_is_the_bf16_layer_on_decoded_weights(w, path):
     """Every E2M1 value times a power-of-two block scale is a bfloat16 value,
-    so the MXFP4 layer equals, bit for bit, the bf16 layer on the decoded
-    weights (the formats share the MFMA grouping of every dot product)."""
+    so where the MXFP4 kernels group the dot products' terms as the bf16
+    ones do (the tiled FFN, and the streaming FFN shared with bf16), the
+    MXFP4 layer equals the bf16 layer on the decoded weights bit for bit.
+    The MXFP4 streaming kernel with 16-byte code loads groups them its own
+    way: there the two agree to fp32 rounding (and both match the oracle)."""
     from sparse_moe_layer_gemm_amd.inputs import decode_mxfp4
 
     inp = every_byte_mxfp4(w, 20)
@@ -277,7 +281,12 @@ def test_mxfp4_layer_is_the_bf16_layer_on_decoded_weights(w, path):
     a = B.forward(P.to_device(inp), w.K, path=path)
     b = B.forward(P.to_device(dense), w.K, path=path)
     torch.cuda.synchronize()
-    assert torch.equal(a, b)
+    if path == S and w.l % 256 == 0:
+        moe = (b.float() - P.to_device(inp)["x"].float())
+        err = (a.float() - b.float()).abs().max().item()
+        assert err <= 1e-2 * moe.pow(2).mean().sqrt().item() + 2 ** -7 * b.float().abs().max().item(), err
+    else:
+        assert torch.equal(a, b)
 
 
 # --- zero-computation experts (zero, copy, constant) --------------------------
