@@ -215,7 +215,9 @@ def measure(w, sets, cpu_seconds: float) -> dict:
     # dominant kernel: the expert FFN
     if path == B.LMOE_PATH_STREAM:
         ffn_bytes = expert_bytes(w, A)
-        roof = {"kernel": "ffn_stream_kernel", "bound": "hbm", "achieved": ffn_bytes / (ffn_us * 1e-6) / 1e9,
+        # MXFP4 with 128-wide slices (m % 128 == 0), l % 256 == 0: its own kernel
+        mx16 = w.experts == "mxfp4" and w.m % 128 == 0 and w.l % 256 == 0
+        roof = {"kernel": "ffn_stream_mx_kernel" if mx16 else "ffn_stream_kernel", "bound": "hbm", "achieved": ffn_bytes / (ffn_us * 1e-6) / 1e9,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": None}
     elif w.dtype == "f32":
         ffn_flops = 4.0 * R * w.l * w.m
