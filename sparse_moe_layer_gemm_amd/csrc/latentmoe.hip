@@ -222,9 +222,14 @@ Plan make_plan(const lmoe_dims* dm, int32_t K) {
 
 size_t dispatch_lds_bytes(int N) { return (size_t)N * 32 + (size_t)N * 12 + 17 * 4; }
 
+// Once per device (kernel attributes belong to a device): the dispatch
+// kernels may use more dynamic LDS than the default limit.
 void init_once() {
-    static std::once_flag flag;
-    std::call_once(flag, [] {
+    constexpr int kMaxDevices = 64;
+    static std::once_flag flags[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
+    std::call_once(flags[dev], [] {
         const int bytes = (int)dispatch_lds_bytes(kMaxExperts);
         hipFuncSetAttribute((const void*)dispatch_one_block_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
         hipFuncSetAttribute((const void*)dispatch_count_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);

@@ -188,7 +188,21 @@ struct Up {
         const size_t i = (size_t)r * a.d + c;
         static_cast<E*>(a.out)[i] = from_f32<E>(to_f32(static_cast<const E*>(a.x)[i]) + v);
     }
+    // the same split in two, for kernels that load the residual early
+    __device__ static float residual(const LayerArgs& a, int r, int c) {
+        return to_f32(static_cast<const E*>(a.x)[(size_t)r * a.d + c]);
+    }
+    __device__ static void store_total(const LayerArgs& a, int r, int c, float t) {
+        static_cast<E*>(a.out)[(size_t)r * a.d + c] = from_f32<E>(t);
+    }
 };
+
+// Problems whose output adds a residual that a kernel may load early
+// (residual(a, r, c), then store_total(a, r, c, residual + v)).
+template <class P, class = void>
+struct HasResidual : std::false_type {};
+template <class P>
+struct HasResidual<P, decltype((void)P::residual(std::declval<const LayerArgs&>(), 0, 0))> : std::true_type {};
 
 // Shared expert, second product: y_s = W_s2 a_s, kept in float32 so that the
 // layer's output is still rounded once (in the up-projection or combine).

@@ -72,6 +72,18 @@ __global__ __launch_bounds__(1024) void skinny_kernel(LayerArgs a) {
                     if (rb < nrb) acc[rb] = mfma16(as_bf16x8(av[u][rb]), as_bf16x8(bv[u]), acc[rb]);
         }
     };
+    // the residual of this thread's outputs, loaded now so that its latency
+    // overlaps the weight stream (the first nrb waves store the results)
+    [[maybe_unused]] float res[4] = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (HasResidual<P>::value) {
+        if (threadIdx.x < nrb * 64) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = r0 + (threadIdx.x >> 6) * 16 + 4 * (lane >> 4) + r;
+                if (row < a.T && c < ncols) res[r] = P::residual(a, row, c);
+            }
+        }
+    }
     // the waves split each operand pair's k-steps evenly (the first pair's
     // split is the same as without a second pair)
     const int k1s = K1 / 32, per1 = cdiv(k1s, kSkinnyWaves);
@@ -100,7 +112,12 @@ __global__ __launch_bounds__(1024) void skinny_kernel(LayerArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = r0 + rb * 16 + 4 * (lane >> 4) + r;
-            if (row < a.T && c < ncols) P::store(a, 0, row, c, s[r]);
+            if (row < a.T && c < ncols) {
+                if constexpr (HasResidual<P>::value)
+                    P::store_total(a, row, c, res[r] + s[r]);
+                else
+                    P::store(a, 0, row, c, s[r]);
+            }
         }
     }
 }
