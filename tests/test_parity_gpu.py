@@ -437,6 +437,32 @@ def test_all_tokens_on_few_experts():
 # --- exact properties ----------------------------------------------------------
 
 @pytest.mark.parametrize("path", [S, TL])
+@pytest.mark.parametrize("N,K", [(16, 3), (200, 9), (512, 22), (640, 22), (1100, 16)])
+def test_exact_ties_take_the_lower_index(path, N, K):
+    """Small-integer x and router rows make every logit an exact integer in
+    fp32 and fp64 alike, with router rows duplicated in pairs on top, so
+    ties straddle the top-K boundary on most tokens: the ids, in rank order,
+    must be exactly the oracle's (larger logit first, then lower index), on
+    both top-K kernels and across the logits-per-lane tiers."""
+    w = Workload(f"ties_{N}_{K}", T=96, d=256, l=64, N=N, K=K, m=64, dtype="bf16")
+    inp = make_inputs(w, 22)
+    g = torch.Generator().manual_seed(23)
+    inp["x"] = torch.randint(-3, 4, inp["x"].shape, generator=g).to(torch.bfloat16)
+    wr = torch.randint(-2, 3, inp["W_router"].shape, generator=g).to(torch.bfloat16)
+    wr[1::2] = wr[0::2][: N // 2]
+    inp["W_router"] = wr.contiguous()
+    d = P.to_device(inp)
+    _, ids, gates, _ = B.forward(d, w.K, path=path, routing=True)
+    torch.cuda.synchronize()
+    ref = P.run_oracle(P.oracle_arrays(inp), w.K)
+    ids_g = ids.cpu().numpy()
+    assert np.array_equal(ids_g, ref["ids"]), (
+        f"{int((ids_g != ref['ids']).any(axis=1).sum())} tokens differ from the oracle's tie order")
+    assert np.abs(gates.cpu().numpy() - ref["gates"]).max() <= 1e-5
+
+
+
+@pytest.mark.parametrize("path", [S, TL])
 def test_zero_weights_give_x_exactly(path):
     w = Workload("zeros", T=77, d=256, l=128, N=16, K=4, m=128, dtype="bf16")
     inp = make_inputs(w, 7)
