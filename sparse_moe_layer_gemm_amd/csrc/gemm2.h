@@ -467,7 +467,8 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm2_kernel(LayerArgs a, int 
     // consecutive columns: each store instruction covers whole rows instead
     // of 16 bytes of 32 rows.  Each round is written by the waves that own
     // its rows.
-    constexpr int kEpiRows = (kStageU4 * 16 / (BN * 4)) < BM ? (kStageU4 * 16 / (BN * 4)) : BM;
+    constexpr int kEpiFit = kStageU4 * 16 / (BN * 4) / 32 * 32;   // fp32 rows one stage holds, in 32s
+    constexpr int kEpiRows = kEpiFit < BM ? kEpiFit : BM;
     constexpr int kUpr = BN / 4, kPasses = kEpiRows * kUpr / S::NT;
     static_assert(!RowCtx<P>::kRowVal || BM <= S::NT, "one thread per row for the row values");
     // per-tile operands, loaded when the compute cursor enters a tile

@@ -231,10 +231,10 @@ void init_once() {
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
     std::call_once(flags[dev], [] {
         const int bytes = (int)dispatch_lds_bytes(kMaxExperts);
-        hipFuncSetAttribute((const void*)dispatch_one_block_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-        hipFuncSetAttribute((const void*)dispatch_count_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-        hipFuncSetAttribute((const void*)dispatch_scan_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-        hipFuncSetAttribute((const void*)dispatch_scatter_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+        (void)hipFuncSetAttribute((const void*)dispatch_one_block_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+        (void)hipFuncSetAttribute((const void*)dispatch_count_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+        (void)hipFuncSetAttribute((const void*)dispatch_scan_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+        (void)hipFuncSetAttribute((const void*)dispatch_scatter_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
         (void)hipGetLastError();
     });
 }
@@ -279,7 +279,7 @@ void launch_combine(const LayerArgs& a, int nsplit, int gated, hipStream_t st) {
 template <class E, class YT>
 void launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* events) {
     auto mark = [&](int i) {
-        if (events && events[i]) hipEventRecord(static_cast<hipEvent_t>(events[i]), st);
+        if (events && events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(events[i]), st);
     };
     const dim3 b256(256), b1024(1024);
     // projection columns: [z | the shared expert's h_s | logits]
