@@ -80,6 +80,20 @@ __device__ __forceinline__ uint4 fp4x8_to_bf16x8(uint32_t v, float sc) {
 #endif
 }
 
+// Streaming (non-temporal) vector stores, for outputs that the kernel does
+// not read back.  A GEMM tile's stores are issued in a burst at its end, and
+// loads issued after them are counted behind them (one in-order vector
+// memory counter): non-temporal stores are acknowledged sooner, so the next
+// tile's operand loads wait less.
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void st_nt8(void* p, uint2 v) {
+    __builtin_nontemporal_store(u32x2{v.x, v.y}, static_cast<u32x2*>(p));
+}
+__device__ __forceinline__ void st_nt16(void* p, uint4 v) {
+    __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, static_cast<u32x4*>(p));
+}
+
 constexpr uint4 kZero16 = {0u, 0u, 0u, 0u};
 
 __host__ __device__ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }

@@ -52,14 +52,26 @@ struct G2Shape {
 __device__ __forceinline__ int g2_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 // 4 consecutive output columns of one row (c0 .. c0+3), epilogue per problem.
-template <class E>
+// kStream: streaming stores, for the expert FFN's intermediates (A and the
+// gate-scaled outputs: hundreds of MB at prefill, read once by the next
+// kernel).  They shorten the wait of the next tile's operand loads, which
+// are counted behind the stores; measured slower for the projections'
+// outputs, which the next kernel reads while they may still be cached.
+template <class E, bool kStream = false>
 __device__ __forceinline__ void store_cols(E* dst, int c0, int ncols, const f32x4& v) {
     if (c0 + 3 < ncols && (reinterpret_cast<uintptr_t>(dst) & (4 * sizeof(E) - 1)) == 0) {
         if constexpr (sizeof(E) == 2) {
             bf16 b[4] = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
-            *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(b);
+            if constexpr (kStream)
+                st_nt8(dst, *reinterpret_cast<const uint2*>(b));
+            else
+                *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(b);
         } else {
-            *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+            const uint4 u = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
+            if constexpr (kStream)
+                st_nt16(dst, u);
+            else
+                *reinterpret_cast<uint4*>(dst) = u;
         }
     } else {
         for (int i = 0; i < 4; ++i)
@@ -129,7 +141,7 @@ struct RowCtx<Ffn1<bf16>> {
             const float t = v[i] > 0.0f ? v[i] : 0.0f;
             v[i] = t * t;
         }
-        store_cols(static_cast<bf16*>(a.abuf) + (size_t)slot * a.m + c0, c0, a.m, v);
+        store_cols<bf16, true>(static_cast<bf16*>(a.abuf) + (size_t)slot * a.m + c0, c0, a.m, v);
     }
 };
 
@@ -143,7 +155,7 @@ struct RowCtx<Ffn2<bf16, bf16>> {
     __device__ static NoPre load(const LayerArgs&, int, int, int) { return NoPre{}; }
     __device__ static void store(const LayerArgs& a, int, int slot, int c0, f32x4 v, const NoPre&, const NoPre&,
                                  float g) {
-        store_cols(static_cast<bf16*>(a.ybuf) + (size_t)slot * a.l + c0, c0, a.l, v * g);
+        store_cols<bf16, true>(static_cast<bf16*>(a.ybuf) + (size_t)slot * a.l + c0, c0, a.l, v * g);
     }
 };
 
