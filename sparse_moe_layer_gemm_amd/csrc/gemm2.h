@@ -94,6 +94,12 @@ struct NoPre {};
 template <class P>
 struct RowCtx;
 
+// RowCtx<P>::kBf16Tile, false where a problem does not define it
+template <class R, class = void>
+struct Bf16Tile : std::false_type {};
+template <class R>
+struct Bf16Tile<R, std::void_t<decltype(R::kBf16Tile)>> : std::integral_constant<bool, R::kBf16Tile> {};
+
 template <>
 struct RowCtx<ProjRouter<bf16>> {
     static constexpr bool kRowVal = false;
@@ -127,9 +133,22 @@ struct RowCtx<ProjRouter<bf16>> {
     }
 };
 
+// The FFN problems' epilogues depend only on the element and its row (relu^2;
+// the slot's gate), so they run in registers and the tile goes through LDS
+// as bf16 (kBf16Tile): tile_op() is the epilogue, tile_row() the row's
+// destination.
 template <>
 struct RowCtx<Ffn1<bf16>> {
     static constexpr bool kRowVal = false;
+    static constexpr bool kBf16Tile = true;
+    __device__ static f32x4 tile_op(f32x4 v, float) {
+        for (int i = 0; i < 4; ++i) {
+            const float t = v[i] > 0.0f ? v[i] : 0.0f;
+            v[i] = t * t;
+        }
+        return v;
+    }
+    __device__ static bf16* tile_row(const LayerArgs& a, int slot) { return static_cast<bf16*>(a.abuf) + (size_t)slot * a.m; }
     __device__ static float row_value(const LayerArgs&, int, int) { return 0.0f; }
     using ColPre = NoPre;
     __device__ static NoPre col_load(const LayerArgs&, int, int) { return NoPre{}; }
@@ -148,6 +167,9 @@ struct RowCtx<Ffn1<bf16>> {
 template <>
 struct RowCtx<Ffn2<bf16, bf16>> {
     static constexpr bool kRowVal = true;   // the slot's gate
+    static constexpr bool kBf16Tile = true;
+    __device__ static f32x4 tile_op(f32x4 v, float g) { return v * g; }
+    __device__ static bf16* tile_row(const LayerArgs& a, int slot) { return static_cast<bf16*>(a.ybuf) + (size_t)slot * a.l; }
     __device__ static float row_value(const LayerArgs& a, int, int slot) { return a.gates[a.perm[slot]]; }
     using ColPre = NoPre;
     __device__ static NoPre col_load(const LayerArgs&, int, int) { return NoPre{}; }
@@ -496,7 +518,72 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm2_kernel(LayerArgs a, int 
     tile_loads();
     static_assert(kEpiRows % 32 == 0 && BM % kEpiRows == 0 && kUpr >= 16, "epilogue tiling");
     static_assert(kEpiRows * kUpr % S::NT == 0 && S::NT % kUpr == 0, "epilogue passes");
+    // bf16 tiles (kBf16Tile): the epilogue runs on the accumulators, and the
+    // rounded tile goes through LDS in rounds of kRowsB rows -- round h takes
+    // the 32-row blocks h*FM/R .. of every wave row, so all waves write in
+    // every round.  8-byte granule q (4 columns) of local row r is stored at
+    // q ^ (r & 31): the 32 rows of one write instruction (one granule each)
+    // hit 32 distinct bank pairs.  A 16-byte unit p (granules 2p, 2p+1) is
+    // then unit p ^ ((r & 31) >> 1), its halves swapped when r is odd; each
+    // thread stores whole units, consecutive threads on consecutive units.
+    constexpr int kRowsFit = kStageU4 * 16 / (BN * 2) / 32 * 32;   // bf16 rows one stage holds
+    constexpr int kRowsB = kRowsFit < BM ? kRowsFit : BM;
+    constexpr int kRounds = BM / kRowsB, kWRows = S::WM / kRounds;   // a wave's rows per round
+    constexpr int kUnits = BN / 8, kPassB = kRowsB * kUnits / S::NT;
+    static_assert(kRowsB % 32 == 0 && BM % kRowsB == 0 && S::FM % kRounds == 0, "bf16 epilogue rounds");
+    static_assert(S::NT % kUnits == 0 && kRowsB * kUnits % S::NT == 0, "bf16 epilogue passes");
+    auto epilogue_bf16 = [&](int st) {
+      if constexpr (Bf16Tile<RowCtx<P>>::value) {
+        int etid = tid;
+        asm volatile("" : "+v"(etid));
+        const int lane = etid & 63;
+        uint2* tg = reinterpret_cast<uint2*>(As(st));
+        if constexpr (RowCtx<P>::kRowVal) {
+            if (etid < BM) rowval[etid] = rv;
+            __syncthreads();
+        }
+        const int x = lane & 31;   // = local row & 31 of every row this lane writes
+#pragma unroll
+        for (int h = 0; h < kRounds; ++h) {
+            if (h > 0) __syncthreads();   // the previous round's reads are done
+#pragma unroll
+            for (int ii = 0; ii < S::FM / kRounds; ++ii) {
+                const int i = h * (S::FM / kRounds) + ii;
+                const int rl = wm * kWRows + ii * 32 + x;
+                const float g = RowCtx<P>::kRowVal ? rowval[wm * S::WM + i * 32 + x] : 0.0f;
+#pragma unroll
+                for (int j = 0; j < S::FN; ++j)
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const int q = (wn * S::WN + j * 32 + 8 * q4 + 4 * (lane >> 5)) >> 2;
+                        const f32x4 v = RowCtx<P>::tile_op(
+                            f32x4{acc[i][j][4 * q4], acc[i][j][4 * q4 + 1], acc[i][j][4 * q4 + 2], acc[i][j][4 * q4 + 3]}, g);
+                        const bf16 b[4] = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+                        tg[rl * (BN / 4) + (q ^ x)] = *reinterpret_cast<const uint2*>(b);
+                    }
+            }
+            __syncthreads();
+            const int p = etid % kUnits, c = ct.col0 + 8 * p;
+#pragma unroll
+            for (int it = 0; it < kPassB; ++it) {
+                const int rl = it * (S::NT / kUnits) + etid / kUnits;
+                const int row = ct.row0 + (rl / kWRows) * S::WM + h * kWRows + rl % kWRows;
+                if (row < ct.row_end && c < ncols) {
+                    const int y = rl & 31;
+                    uint4 w = reinterpret_cast<const uint4*>(tg)[rl * kUnits + (p ^ (y >> 1))];
+                    if (y & 1) w = uint4{w.z, w.w, w.x, w.y};
+                    st_nt16(RowCtx<P>::tile_row(a, row) + c, w);
+                }
+            }
+        }
+        __syncthreads();  // the stage is free for the k-step after next
+      }
+    };
     auto epilogue = [&](int st) {
+        if constexpr (Bf16Tile<RowCtx<P>>::value) {
+            epilogue_bf16(st);
+            return;
+        }
         // the epilogue's lane-dependent offsets are recomputed from an opaque
         // copy of the thread id, so they are not hoisted out of the tile loop
         // and kept live (in registers) across the k-steps
