@@ -99,6 +99,12 @@ template <class R, class = void>
 struct Bf16Tile : std::false_type {};
 template <class R>
 struct Bf16Tile<R, std::void_t<decltype(R::kBf16Tile)>> : std::integral_constant<bool, R::kBf16Tile> {};
+// RowCtx<P>::kColScale (a float per output column, applied first), false
+// where a problem does not define it
+template <class R, class = void>
+struct ColScale : std::false_type {};
+template <class R>
+struct ColScale<R, std::void_t<decltype(R::kColScale)>> : std::integral_constant<bool, R::kColScale> {};
 
 template <>
 struct RowCtx<ProjRouter<bf16>> {
@@ -201,46 +207,19 @@ struct RowCtx<Up<bf16>> {
     }
 };
 
-// FP8 experts: the four columns' row scales (columns of the product are
-// rows of the weight matrix), applied before the problem's own epilogue.
-template <class Q>
-struct QScales {
-    __device__ static f32x4 load(const LayerArgs& a, int e, int c0, int ncols) {
-        f32x4 s = {1.0f, 1.0f, 1.0f, 1.0f};
-        for (int i = 0; i < 4; ++i)
-            if (c0 + i < ncols) s[i] = Q::row_scale(a, e, c0 + i);
-        return s;
-    }
+// FP8 experts: the bf16 problems' epilogues after the column's scale (the
+// scale of that weight row), which each tile loads once per column
+// (kColScale) and passes through LDS.
+template <>
+struct RowCtx<Ffn1Q> : RowCtx<Ffn1<bf16>> {
+    static constexpr bool kColScale = true;
+    __device__ static float col_scale(const LayerArgs& a, int e, int c) { return Ffn1Q::row_scale(a, e, c); }
 };
 
 template <>
-struct RowCtx<Ffn1Q> {
-    static constexpr bool kRowVal = false;
-    __device__ static float row_value(const LayerArgs&, int, int) { return 0.0f; }
-    using ColPre = f32x4;
-    __device__ static f32x4 col_load(const LayerArgs& a, int e, int c0) { return QScales<Ffn1Q>::load(a, e, c0, a.m); }
-    using Pre = NoPre;
-    __device__ static NoPre load(const LayerArgs&, int, int, int) { return NoPre{}; }
-    __device__ static void store(const LayerArgs& a, int g, int slot, int c0, f32x4 v, const NoPre& p,
-                                 const f32x4& sc, float rv) {
-        RowCtx<Ffn1<bf16>>::store(a, g, slot, c0, v * sc, p, NoPre{}, rv);
-    }
-};
-
-template <>
-struct RowCtx<Ffn2Q> {
-    static constexpr bool kRowVal = true;   // the slot's gate
-    __device__ static float row_value(const LayerArgs& a, int e, int slot) {
-        return RowCtx<Ffn2<bf16, bf16>>::row_value(a, e, slot);
-    }
-    using ColPre = f32x4;
-    __device__ static f32x4 col_load(const LayerArgs& a, int e, int c0) { return QScales<Ffn2Q>::load(a, e, c0, a.l); }
-    using Pre = NoPre;
-    __device__ static NoPre load(const LayerArgs&, int, int, int) { return NoPre{}; }
-    __device__ static void store(const LayerArgs& a, int g, int slot, int c0, f32x4 v, const NoPre& p,
-                                 const f32x4& sc, float gate) {
-        RowCtx<Ffn2<bf16, bf16>>::store(a, g, slot, c0, v * sc, p, NoPre{}, gate);
-    }
+struct RowCtx<Ffn2Q> : RowCtx<Ffn2<bf16, bf16>> {
+    static constexpr bool kColScale = true;
+    __device__ static float col_scale(const LayerArgs& a, int e, int c) { return Ffn2Q::row_scale(a, e, c); }
 };
 
 // MXFP4 experts: the block scales are applied when the codes are decoded,
@@ -301,6 +280,8 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm2_kernel(LayerArgs a, int 
     constexpr int kStageU4 = (BM + BN) * 8;
     __shared__ uint4 smem[2 * kStageU4];
     __shared__ float rowval[RowCtx<P>::kRowVal ? BM : 1];
+    constexpr bool kColS = ColScale<RowCtx<P>>::value;
+    __shared__ float colval[kColS ? BN : 1];
     auto As = [&](int st) { return smem + st * kStageU4; };
     auto Bs = [&](int st) { return smem + st * kStageU4 + BM * 8; };
 
@@ -508,9 +489,14 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm2_kernel(LayerArgs a, int 
     // per-tile operands, loaded when the compute cursor enters a tile
     float rv = 0.0f;
     typename RowCtx<P>::ColPre colpre;
+    float cs = 1.0f;
+    static_assert(!kColS || (BN <= S::NT && Bf16Tile<RowCtx<P>>::value), "one thread per column for the scales");
     auto tile_loads = [&]() {
         if constexpr (RowCtx<P>::kRowVal) {
             if (tid < BM && ct.row0 + tid < ct.row_end) rv = RowCtx<P>::row_value(a, ct.grp, ct.row0 + tid);
+        }
+        if constexpr (kColS) {
+            if (tid < BN) cs = ct.col0 + tid < ncols ? RowCtx<P>::col_scale(a, ct.grp, ct.col0 + tid) : 1.0f;
         }
         const int c = ct.col0 + 4 * (tid % kUpr);
         if (c < ncols) colpre = RowCtx<P>::col_load(a, ct.grp, c);
@@ -540,8 +526,11 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm2_kernel(LayerArgs a, int 
         uint2* tg = reinterpret_cast<uint2*>(As(st));
         if constexpr (RowCtx<P>::kRowVal) {
             if (etid < BM) rowval[etid] = rv;
-            __syncthreads();
         }
+        if constexpr (kColS) {
+            if (etid < BN) colval[etid] = cs;
+        }
+        if constexpr (RowCtx<P>::kRowVal || kColS) __syncthreads();
         const int x = lane & 31;   // = local row & 31 of every row this lane writes
 #pragma unroll
         for (int h = 0; h < kRounds; ++h) {
@@ -556,8 +545,9 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm2_kernel(LayerArgs a, int 
 #pragma unroll
                     for (int q4 = 0; q4 < 4; ++q4) {
                         const int q = (wn * S::WN + j * 32 + 8 * q4 + 4 * (lane >> 5)) >> 2;
-                        const f32x4 v = RowCtx<P>::tile_op(
-                            f32x4{acc[i][j][4 * q4], acc[i][j][4 * q4 + 1], acc[i][j][4 * q4 + 2], acc[i][j][4 * q4 + 3]}, g);
+                        f32x4 v = {acc[i][j][4 * q4], acc[i][j][4 * q4 + 1], acc[i][j][4 * q4 + 2], acc[i][j][4 * q4 + 3]};
+                        if constexpr (kColS) v *= *reinterpret_cast<const f32x4*>(&colval[4 * q]);
+                        v = RowCtx<P>::tile_op(v, g);
                         const bf16 b[4] = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
                         tg[rl * (BN / 4) + (q ^ x)] = *reinterpret_cast<const uint2*>(b);
                     }
