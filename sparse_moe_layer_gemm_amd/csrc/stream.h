@@ -323,6 +323,27 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(LayerArgs a) {
                 const float h = acc[b][r] > 0.0f ? acc[b][r] : 0.0f;
                 As[(4 * (lane >> 4) + r) * AST + (wave + 4 * b) * 16 + lr] = (bf16)(h * h);
             }
+        // FP8: the first pass's W2 blocks do not depend on phase 1, so their
+        // loads are issued before the barrier and the phase change does not
+        // wait for them (for bf16 and MXFP4 weights the extra registers would
+        // cost a wave per SIMD; measured slower for bf16)
+        constexpr int KB = MS / 64;        // 64-wide k blocks of the slice
+        constexpr int NU = 4;              // blocks per pass
+        constexpr bool kPre = F == 1;
+        const int nblk = l / 16;
+        [[maybe_unused]] WB w0[NU][KB];
+        [[maybe_unused]] f32x4 sc0[NU];
+#pragma unroll
+        for (int u = 0; u < NU && kPre; ++u) {
+            const int ib = wave + 4 * u;
+            const bool ok = ib < nblk;
+            const size_t w2o = ((size_t)e * l + ib * 16 + lr) * m + j0 + k16;
+#pragma unroll
+            for (int q = 0; q < KB; ++q) w0[u][q] = ok ? WB::load(a.W2, a.w2x, w2o + 64 * q) : WB::zero();
+            if constexpr (F == 1)
+                sc0[u] = ok ? *reinterpret_cast<const f32x4*>(a.w2s + (size_t)e * l + ib * 16 + 4 * (lane >> 4))
+                            : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
         __syncthreads();
         // ---- phase 2: Y[16 x l] = A[16 x MS] . W2[e][:, j0 : j0+MS]^T.  The
         // weight fragment is the MFMA's first operand, so lane l holds output
@@ -330,8 +351,6 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(LayerArgs a) {
         // A pass loads NU blocks of 16 output columns; the results of NP
         // passes are stored together, since a load issued behind pending
         // stores waits for them to complete.
-        constexpr int KB = MS / 64;        // 64-wide k blocks of the slice
-        constexpr int NU = 4;              // blocks per pass
         // passes per batch of stores (fewer for FP8 and MXFP4, whose decode
         // registers would otherwise cut the waves per SIMD: 2 and 4 of them)
         constexpr int NP = F == 0 ? 4 : (F == 1 ? 2 : 1);
@@ -341,7 +360,6 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(LayerArgs a) {
 #pragma unroll
             for (int h = 0; h < 2; ++h)
                 af[q][h] = *reinterpret_cast<const bf16x8*>(&As[lr * AST + 64 * q + k16 + 8 * h]);
-        const int nblk = l / 16;
         // a wave takes blocks wave + 4 (NU it + u), NP passes it per batch
         for (int ib0 = wave; ib0 < nblk; ib0 += 4 * NU * NP) {
             f32x4 yb[NP][NU];
@@ -349,6 +367,14 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(LayerArgs a) {
             for (int it = 0; it < NP; ++it) {
                 WB wv[NU][KB];
                 f32x4 sc[NU];
+                if (kPre && it == 0 && ib0 == wave) {
+#pragma unroll
+                    for (int u = 0; u < NU; ++u) {
+#pragma unroll
+                        for (int q = 0; q < KB; ++q) wv[u][q] = w0[u][q];
+                        if constexpr (F == 1) sc[u] = sc0[u];
+                    }
+                } else
 #pragma unroll
                 for (int u = 0; u < NU; ++u) {
                     const int ib = ib0 + 4 * (NU * it + u);
