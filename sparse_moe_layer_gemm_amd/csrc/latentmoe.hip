@@ -14,6 +14,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <mutex>
@@ -77,6 +78,14 @@ size_t proj_part_floats(int ncols, int T) {  // per token row
 
 // mean rows per expert at or below which the streaming FFN is chosen
 constexpr int kStreamMaxMeanRows = 16;
+// The streaming FFN's m-slice: 128 (64 where m is not a multiple of 128),
+// or 256 for bf16 experts when the expected (active expert, slice)
+// workgroups under uniform routing number at least kWideSliceMinWgs (four
+// per CU) and the active experts average at most kWideSliceMaxRows rows.
+// Wider slices halve the fp32 partial planes (the FFN's stores, the
+// combine's reads) but also the workgroups that stream the weights.
+constexpr double kWideSliceMinWgs = 1024;
+constexpr double kWideSliceMaxRows = 8;
 
 struct Plan {
     int status = LMOE_OK;
@@ -172,6 +181,11 @@ Plan make_plan(const lmoe_dims* dm, int32_t K) {
         p.ffn_large = TK >= (long long)kFfnLargeMinMeanRows * d.N;
         p.tile_rows = p.ffn_large ? G2Large::BM : G2Small::BM;
         p.ms = (d.m % 128 == 0) ? 128 : 64;
+        if (p.wfmt == 0 && d.m % 256 == 0) {
+            const double ffn_slots = (double)TK * d.N / p.nr;   // routed rows of FFN experts
+            const double active = d.N * (1.0 - std::pow(1.0 - (double)K / p.nr, (double)d.T));
+            if (active * (d.m / 256) >= kWideSliceMinWgs && ffn_slots <= kWideSliceMaxRows * active) p.ms = 256;
+        }
         p.nsplit = p.path == LMOE_PATH_STREAM ? d.m / p.ms : 1;
         p.skinny = p.path == LMOE_PATH_STREAM && d.T <= kSkinnyMaxRows;
     }
@@ -360,8 +374,12 @@ void launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* events
             const dim3 g(p.nsplit, p.wfmt == 2 ? (unsigned)(cdiv(a.n_ffn, 8) * 8) : (unsigned)a.n_ffn);
             auto stream = [&](auto fmt) {
                 constexpr int F = decltype(fmt)::value;
-                p.ms == 128 ? ffn_stream_kernel<128, F><<<g, b256, 0, st>>>(a)
-                            : ffn_stream_kernel<64, F><<<g, b256, 0, st>>>(a);
+                if (F == 0 && p.ms == 256)
+                    ffn_stream_kernel<256, 0><<<g, b256, 0, st>>>(a);
+                else if (p.ms == 128)
+                    ffn_stream_kernel<128, F><<<g, b256, 0, st>>>(a);
+                else
+                    ffn_stream_kernel<64, F><<<g, b256, 0, st>>>(a);
             };
             if (p.wfmt == 1)
                 stream(std::integral_constant<int, 1>{});

@@ -13,7 +13,8 @@
 //   skinny_part_kernel<P>: the same, with the reduction also split over
 //     workgroups (fp32 partial tiles added by the consumer).
 //   ffn_stream_kernel<MS, F>: the expert FFN.  Workgroup (s, a) takes
-//     active expert a and the m-slice [s*MS, (s+1)*MS): it computes
+//     active expert a and the m-slice [s*MS, (s+1)*MS) (MS = 64, 128, or 256
+//     when there are enough workgroups to go round): it computes
 //     relu(W1[e][slice] z)^2 for up to 16 routed rows at a time, keeps it in
 //     LDS, and multiplies it by the matching column slice of W2[e], writing
 //     an fp32 partial expert output per slice.  Every weight byte of an
@@ -328,7 +329,7 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(LayerArgs a) {
         // wait for them (for bf16 and MXFP4 weights the extra registers would
         // cost a wave per SIMD; measured slower for bf16)
         constexpr int KB = MS / 64;        // 64-wide k blocks of the slice
-        constexpr int NU = 4;              // blocks per pass
+        constexpr int NU = MS == 256 ? 2 : 4;   // blocks per pass (fewer for the wider slice's k blocks)
         constexpr bool kPre = F == 1;
         const int nblk = l / 16;
         [[maybe_unused]] WB w0[NU][KB];
