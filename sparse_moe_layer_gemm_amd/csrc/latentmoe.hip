@@ -79,7 +79,7 @@ size_t proj_part_floats(int ncols, int T) {  // per token row
 // mean rows per expert at or below which the streaming FFN is chosen
 constexpr int kStreamMaxMeanRows = 16;
 // The streaming FFN's m-slice: 128 (64 where m is not a multiple of 128),
-// or 256 for bf16 experts when the expected (active expert, slice)
+// or 256 for bf16 and FP8 experts when the expected (active expert, slice)
 // workgroups under uniform routing number at least kWideSliceMinWgs (four
 // per CU) and the active experts average at most kWideSliceMaxRows rows.
 // Wider slices halve the fp32 partial planes (the FFN's stores, the
@@ -181,7 +181,7 @@ Plan make_plan(const lmoe_dims* dm, int32_t K) {
         p.ffn_large = TK >= (long long)kFfnLargeMinMeanRows * d.N;
         p.tile_rows = p.ffn_large ? G2Large::BM : G2Small::BM;
         p.ms = (d.m % 128 == 0) ? 128 : 64;
-        if (p.wfmt == 0 && d.m % 256 == 0) {
+        if (p.wfmt <= 1 && d.m % 256 == 0) {
             const double ffn_slots = (double)TK * d.N / p.nr;   // routed rows of FFN experts
             const double active = d.N * (1.0 - std::pow(1.0 - (double)K / p.nr, (double)d.T));
             if (active * (d.m / 256) >= kWideSliceMinWgs && ffn_slots <= kWideSliceMaxRows * active) p.ms = 256;
@@ -374,8 +374,8 @@ void launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* events
             const dim3 g(p.nsplit, p.wfmt == 2 ? (unsigned)(cdiv(a.n_ffn, 8) * 8) : (unsigned)a.n_ffn);
             auto stream = [&](auto fmt) {
                 constexpr int F = decltype(fmt)::value;
-                if (F == 0 && p.ms == 256)
-                    ffn_stream_kernel<256, 0><<<g, b256, 0, st>>>(a);
+                if (F <= 1 && p.ms == 256)
+                    ffn_stream_kernel<256, F <= 1 ? F : 0><<<g, b256, 0, st>>>(a);
                 else if (p.ms == 128)
                     ffn_stream_kernel<128, F><<<g, b256, 0, st>>>(a);
                 else

@@ -164,12 +164,10 @@ def test_fp8_expert_argument_checks(lib):
     w = WORKLOADS["decode_fp8"]
     d = dims_of(w)
     assert d.expert_format == B.LMOE_EXPERTS_FP8_E4M3
-    # the FP8 weights change no workspace region where both layers take the
-    # same m-slices (T = 16: 128 wide); at T = 32 the bf16 layer's 256-wide
-    # slices need half the partial planes
-    d16, b16 = dims_of(w.replace(T=16)), dims_of(WORKLOADS["decode"].replace(T=16))
-    assert B.latentmoe_workspace_bytes(d16, w.K) == B.latentmoe_workspace_bytes(b16, w.K)
-    assert B.latentmoe_workspace_bytes(d, w.K) > B.latentmoe_workspace_bytes(dims_of(WORKLOADS["decode"]), w.K)
+    # the FP8 weights change no workspace region (the same m-slices as bf16)
+    for T in (16, 32):
+        assert B.latentmoe_workspace_bytes(dims_of(w.replace(T=T)), w.K) == \
+            B.latentmoe_workspace_bytes(dims_of(WORKLOADS["decode"].replace(T=T)), w.K)
     P = ctypes.c_void_p
     rc = B.lib().latentmoe_forward(P(FAKE), P(FAKE + (1 << 30)), P(FAKE + (2 << 30)), P(FAKE + (3 << 30)),
                                    P(FAKE + (4 << 30)), P(FAKE + (5 << 30)), w.K, P(FAKE + (6 << 30)),
@@ -197,8 +195,12 @@ def test_mxfp4_expert_argument_checks(lib):
     w = WORKLOADS["decode_mxfp4"]
     d = dims_of(w)
     assert d.expert_format == B.LMOE_EXPERTS_MXFP4
-    # same workspace as the FP8 layer (both take 128-wide slices)
-    assert B.latentmoe_workspace_bytes(d, w.K) == B.latentmoe_workspace_bytes(dims_of(WORKLOADS["decode_fp8"]), w.K)
+    # the MXFP4 weights change no workspace region where the bf16 layer takes
+    # the same 128-wide m-slices (T = 16); at T = 32 the bf16 layer's 256-wide
+    # slices need half the partial planes
+    assert B.latentmoe_workspace_bytes(dims_of(w.replace(T=16)), w.K) == \
+        B.latentmoe_workspace_bytes(dims_of(WORKLOADS["decode"].replace(T=16)), w.K)
+    assert B.latentmoe_workspace_bytes(d, w.K) > B.latentmoe_workspace_bytes(dims_of(WORKLOADS["decode"]), w.K)
     assert call_ex(d, w.K, W1_scale=None, W2_scale=None) == B.LMOE_EINVAL   # scales required
     assert call_ex(d, w.K, W2_scale=None) == B.LMOE_EINVAL
     # byte scales need no alignment (validation passes them, then the workspace check fails)
