@@ -79,7 +79,8 @@ size_t proj_part_floats(int ncols, int T) {  // per token row
 // mean rows per expert at or below which the streaming FFN is chosen
 constexpr int kStreamMaxMeanRows = 16;
 // The streaming FFN's m-slice: 128 (64 where m is not a multiple of 128),
-// or 256 for bf16 and FP8 experts when the expected (active expert, slice)
+// or 256 (bf16, FP8, and MXFP4 experts with l % 256 == 0, which take
+// ffn_stream_mx_kernel) when the expected (active expert, slice)
 // workgroups under uniform routing number at least kWideSliceMinWgs (four
 // per CU) and the active experts average at most kWideSliceMaxRows rows.
 // Wider slices halve the fp32 partial planes (the FFN's stores, the
@@ -181,7 +182,7 @@ Plan make_plan(const lmoe_dims* dm, int32_t K) {
         p.ffn_large = TK >= (long long)kFfnLargeMinMeanRows * d.N;
         p.tile_rows = p.ffn_large ? G2Large::BM : G2Small::BM;
         p.ms = (d.m % 128 == 0) ? 128 : 64;
-        if (p.wfmt <= 1 && d.m % 256 == 0) {
+        if ((p.wfmt <= 1 || d.l % 256 == 0) && d.m % 256 == 0) {
             const double ffn_slots = (double)TK * d.N / p.nr;   // routed rows of FFN experts
             const double active = d.N * (1.0 - std::pow(1.0 - (double)K / p.nr, (double)d.T));
             if (active * (d.m / 256) >= kWideSliceMinWgs && ffn_slots <= kWideSliceMaxRows * active) p.ms = 256;
@@ -383,8 +384,10 @@ void launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* events
             };
             if (p.wfmt == 1)
                 stream(std::integral_constant<int, 1>{});
+            else if (p.wfmt == 2 && p.ms == 256 && a.l % 256 == 0)
+                ffn_stream_mx_kernel<256><<<g, b256, 0, st>>>(a);   // 16-byte code loads
             else if (p.wfmt == 2 && p.ms == 128 && a.l % 256 == 0 && a.m % 128 == 0)
-                ffn_stream_mx_kernel<<<g, b256, 0, st>>>(a);   // 16-byte code loads
+                ffn_stream_mx_kernel<128><<<g, b256, 0, st>>>(a);
             else if (p.wfmt == 2)
                 stream(std::integral_constant<int, 2>{});
             else

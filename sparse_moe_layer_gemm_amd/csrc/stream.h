@@ -20,8 +20,8 @@
 //     an fp32 partial expert output per slice.  Every weight byte of an
 //     active expert is read once per 16 rows; no atomics: the combine adds
 //     the slices in a fixed order.  F: bf16, FP8 or MXFP4 weights.
-//   ffn_stream_mx_kernel: the same for MXFP4 weights with 16-byte code
-//     loads (32 codes per lane), for the usual shapes.
+//   ffn_stream_mx_kernel<MS>: the same for MXFP4 weights with 16-byte code
+//     loads (32 codes per lane), for the usual shapes; MS = 128 or 256.
 #pragma once
 
 #include <type_traits>
@@ -422,11 +422,16 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(LayerArgs a) {
 // +7) goes to MFMA q of the block.  Each load instruction then reads 64
 // contiguous bytes of each of 16 weight rows, with as many bytes per
 // instruction as the FP8 kernel.  (This groups the dot products' terms
-// differently from ffn_stream_kernel.)  Needs 128-wide m-slices,
-// l % 256 == 0 and m % 128 == 0; the scale bytes of a lane's row come as
-// one vector per batch (8 bytes in phase 1, 4 in phase 2).
+// differently from ffn_stream_kernel.)  Needs l % 256 == 0 and m % MS == 0;
+// in phase 2 a W2 row's slice is MS / 128 such blocks.  The scale bytes of a
+// lane's row come as one vector per batch (8 bytes in phase 1, MS / 32 in
+// phase 2).  With MS = 256 a W2 row's slice is a whole 128-byte line, so no
+// slice pairing across XCDs is needed (paired_slices() keeps the plain
+// order for the odd slice count of m = 768, and pairs otherwise).
+template <int MS>
 __global__ __launch_bounds__(256) void ffn_stream_mx_kernel(LayerArgs a) {
-    constexpr int MS = 128, NBW = 2, AST = MS + 8;
+    constexpr int NBW = MS / 64, AST = MS + 8;
+    constexpr int KC = MS / 128;   // 128-term chunks of a W2 row's slice
     constexpr int NSB = 2;   // 128-wide k blocks per batch of phase-1 loads
     int slice, ai;
     paired_slices(slice, ai);
@@ -495,29 +500,39 @@ __global__ __launch_bounds__(256) void ffn_stream_mx_kernel(LayerArgs a) {
         // i0 + 4 (l / 16) .. +3 of row l % 16, one 16-byte store), one pass
         // of NU blocks of 16 output columns per batch of stores
         constexpr int NU = 4;
-        bf16x8 af[4];
+        bf16x8 af[KC][4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) af[q] = *reinterpret_cast<const bf16x8*>(&As[lr * AST + 32 * g + 8 * q]);
+        for (int c = 0; c < KC; ++c)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                af[c][q] = *reinterpret_cast<const bf16x8*>(&As[lr * AST + 128 * c + 32 * g + 8 * q]);
         const int nblk = l / 16;
         for (int ib0 = wave; ib0 < nblk; ib0 += 4 * NU) {
-            uint4 cv[NU];
-            uint32_t sb[NU];
+            uint4 cv[NU][KC];
+            uint2 sb[NU];   // the row slice's scale bytes (4 per 128-term chunk)
 #pragma unroll
             for (int u = 0; u < NU; ++u) {
                 const int ib = ib0 + 4 * u;
                 const bool ok = ib < nblk;
                 const size_t w2e = ((size_t)e * l + ib * 16 + lr) * m + j0;   // the row's slice
-                cv[u] = ok ? ldg16(W2 + w2e / 2 + 16 * g) : kZero16;
-                sb[u] = ok ? ldg4(a.w2x + w2e / 32) : 0x7f7f7f7fu;
+#pragma unroll
+                for (int c = 0; c < KC; ++c) cv[u][c] = ok ? ldg16(W2 + (w2e + 128 * c) / 2 + 16 * g) : kZero16;
+                if constexpr (KC == 1)
+                    sb[u] = uint2{ok ? ldg4(a.w2x + w2e / 32) : 0x7f7f7f7fu, 0u};
+                else
+                    sb[u] = ok ? ldg8(a.w2x + w2e / 32) : uint2{0x7f7f7f7fu, 0x7f7f7f7fu};
             }
             f32x4 yb[NU];
 #pragma unroll
             for (int u = 0; u < NU; ++u) {
-                const uint32_t sc = sb[u] >> (8 * g);
-                const uint32_t w[4] = {cv[u].x, cv[u].y, cv[u].z, cv[u].w};
                 f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int q = 0; q < 4; ++q) y = mfma16(decode(w[q], sc), af[q], y);
+                for (int c = 0; c < KC; ++c) {
+                    const uint32_t sc = (c == 0 ? sb[u].x : sb[u].y) >> (8 * g);
+                    const uint32_t w[4] = {cv[u][c].x, cv[u][c].y, cv[u][c].z, cv[u][c].w};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) y = mfma16(decode(w[q], sc), af[c][q], y);
+                }
                 yb[u] = y;
             }
             if (lr < nr) {

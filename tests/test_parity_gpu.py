@@ -104,6 +104,22 @@ def test_standard_decode_batch_sweep(T):
     P.compare(w, make_inputs(w, 8), w.K, tag=f"standard_decode_T{T}")
 
 
+# FP8 and MXFP4 experts across the batch sizes where the decode FFN's m-slice
+# changes: 128 wide at T = 16, 256 wide at T = 64 and 128 (one draw per
+# format, x = its first T rows)
+@pytest.fixture(scope="module", params=["fp8", "mxfp4"])
+def sweep_low_precision(request):
+    w = WORKLOADS[f"decode_{request.param}"].replace(T=128)
+    return w, make_inputs(w, 9)
+
+
+@pytest.mark.parametrize("T", [16, 64, 128])
+def test_low_precision_decode_batch_sweep(sweep_low_precision, T):
+    w0, inp = sweep_low_precision
+    w = w0.replace(name=f"{w0.name}_T{T}", T=T)
+    P.compare(w, {**inp, "x": inp["x"][:T]}, w.K, tag=f"{w0.name}_T{T}")
+
+
 # --- the shared expert at full d ---------------------------------------------
 
 @pytest.mark.parametrize("path", [B.LMOE_PATH_AUTO, TL])
