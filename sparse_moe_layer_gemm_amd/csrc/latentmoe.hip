@@ -84,9 +84,13 @@ constexpr int kStreamMaxMeanRows = 16;
 // workgroups under uniform routing number at least kWideSliceMinWgs (four
 // per CU) and the active experts average at most kWideSliceMaxRows rows.
 // Wider slices halve the fp32 partial planes (the FFN's stores, the
-// combine's reads) but also the workgroups that stream the weights.
+// combine's reads) but also the workgroups that stream the weights.  With
+// bf16 experts and fewer than kNarrowSliceMaxWgs such workgroups at 128
+// (a few tokens on few, large experts) the slice is 64 wide: twice the
+// workgroups, each streaming half as much.
 constexpr double kWideSliceMinWgs = 1024;
 constexpr double kWideSliceMaxRows = 8;
+constexpr double kNarrowSliceMaxWgs = 128;
 
 struct Plan {
     int status = LMOE_OK;
@@ -182,11 +186,13 @@ Plan make_plan(const lmoe_dims* dm, int32_t K) {
         p.ffn_large = TK >= (long long)kFfnLargeMinMeanRows * d.N;
         p.tile_rows = p.ffn_large ? G2Large::BM : G2Small::BM;
         p.ms = (d.m % 128 == 0) ? 128 : 64;
-        if ((p.wfmt <= 1 || d.l % 256 == 0) && d.m % 256 == 0) {
-            const double ffn_slots = (double)TK * d.N / p.nr;   // routed rows of FFN experts
-            const double active = d.N * (1.0 - std::pow(1.0 - (double)K / p.nr, (double)d.T));
-            if (active * (d.m / 256) >= kWideSliceMinWgs && ffn_slots <= kWideSliceMaxRows * active) p.ms = 256;
-        }
+        const double ffn_slots = (double)TK * d.N / p.nr;   // routed rows of FFN experts
+        const double active = d.N * (1.0 - std::pow(1.0 - (double)K / p.nr, (double)d.T));   // expected
+        if ((p.wfmt <= 1 || d.l % 256 == 0) && d.m % 256 == 0 && active * (d.m / 256) >= kWideSliceMinWgs &&
+            ffn_slots <= kWideSliceMaxRows * active)
+            p.ms = 256;
+        else if (p.wfmt == 0 && p.ms == 128 && active * (d.m / 128) < kNarrowSliceMaxWgs)
+            p.ms = 64;
         p.nsplit = p.path == LMOE_PATH_STREAM ? d.m / p.ms : 1;
         p.skinny = p.path == LMOE_PATH_STREAM && d.T <= kSkinnyMaxRows;
     }
