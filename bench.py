@@ -210,6 +210,7 @@ def measure(w, sets, cpu_seconds: float) -> dict:
         for si, name in enumerate(B.STAGES):
             stages[name] = float(np.mean([hip.elapsed_ms(ev[si], ev[si + 1]) for ev in ev_all])) * 1e3
     copy_gbs = copy_bandwidth(torch, dev)
+    mm_tflops = matmul_rate(torch, dev) if w.dtype == "bf16" else None
     lay_bytes, lay_flops = algorithmic(w, A, R)
 
     # dominant kernel: the expert FFN
@@ -244,6 +245,7 @@ def measure(w, sets, cpu_seconds: float) -> dict:
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["kernel_us"] = ffn_us
     roof["copy_GBps_measured"] = copy_gbs
+    roof["matmul_TFLOPs_measured"] = mm_tflops
     flop_peak = FP32_VECTOR_PEAK_TFLOPS if w.dtype == "f32" else MFMA_BF16_PEAK_TFLOPS
     layer_frac = max(lay_bytes / (HBM_PEAK_GBS * 1e9), lay_flops / (flop_peak * 1e12)) / (ms * 1e-3)
 
@@ -296,6 +298,24 @@ def measured_traffic(w, kernel: str):
         return None
     h = hashlib.sha256(b"".join(open(os.path.join(ROOT, p), "rb").read() for p in rec["sources"])).hexdigest()
     return rec["traffic_bytes_per_launch"] if h == rec["sources_sha256"] else None
+
+
+def matmul_rate(torch, dev, n: int = 8192, reps: int = 10) -> float:
+    """In-run MFMA reference: a large bf16 library GEMM (torch.matmul, n^3),
+    flops / s in TFLOP/s.  A yardstick for the tiled kernels, not part of the
+    layer."""
+    a = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    b = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    c = torch.matmul(a, b)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        c = torch.matmul(a, b)
+    t1.record()
+    torch.cuda.synchronize()
+    rate = 2.0 * n ** 3 * reps / (t0.elapsed_time(t1) * 1e-3) / 1e12
+    del a, b, c
+    return rate
 
 
 def copy_bandwidth(torch, dev, nbytes: int = 1 << 30, reps: int = 10) -> float:
