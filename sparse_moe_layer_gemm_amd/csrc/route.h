@@ -101,16 +101,20 @@ __device__ inline void topk_token(const LayerArgs& a, int t, const float* lg, ui
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // winner `lane` ranks itself against the others, whose keys and indices
+    // it reads from their lanes (v_readlane: no LDS round trip per winner)
     float my_v = -INFINITY;
+    uint32_t mk = 0u;
     int my_rank = 0, my_idx = 0;
     if (lane < K) {
-        const uint32_t mk = s_key[lane];
+        mk = s_key[lane];
         my_idx = s_idx[lane];
         my_v = s_val[lane];
-        for (int q = 0; q < K; ++q) {
-            const uint32_t qk = s_key[q];
-            my_rank += (qk > mk || (qk == mk && s_idx[q] < my_idx)) ? 1 : 0;
-        }
+    }
+    for (int q = 0; q < K; ++q) {
+        const uint32_t qk = __builtin_amdgcn_readlane(mk, q);
+        const int qi = __builtin_amdgcn_readlane(my_idx, q);
+        my_rank += (qk > mk || (qk == mk && qi < my_idx)) ? 1 : 0;
     }
     float mx = my_v;
 #pragma unroll
