@@ -153,28 +153,40 @@ __global__ __launch_bounds__(256) void topk_part_kernel(LayerArgs a, PartIn pin)
     __shared__ float s_val[64];
     const size_t ps = (size_t)a.T * pin.stride;
     const float* pt = pin.part + (size_t)t * pin.stride;
-    // the partials of a value are all loaded before they are added (in split
-    // order), so their latencies overlap
     const int le = pin.lz + a.m_s;   // first logit column
-    for (int e = threadIdx.x; e < a.N; e += 256) {
-        float v[kMaxSplit];
+    // The partials of a value are all loaded before they are added (in split
+    // order), so their latencies overlap; the first group of 4 z columns and
+    // the first two logits of each thread are loaded together, so the usual
+    // sizes (le <= 1024, N <= 512) take one round trip to memory.  The loads
+    // are unconditional (indices past the end and splits past nsplit are
+    // clamped to valid ones, and their values not used): conditional loads
+    // compile to branches that each wait for the loads before them.
+    const int s_last = pin.nsplit - 1;
+    auto load_lg = [&](int e, float* v, float& b) {
+        const int ec = min(e, a.N - 1);
 #pragma unroll
-        for (int s = 0; s < kMaxSplit; ++s) v[s] = s < pin.nsplit ? pt[s * ps + le + e] : 0.0f;
+        for (int s = 0; s < kMaxSplit; ++s) v[s] = pt[min(s, s_last) * ps + le + ec];
+        b = a.bias ? a.bias[ec] : 0.0f;
+    };
+    auto add_lg = [&](int e, const float* v, float b) {
+        if (e >= a.N) return;
         float acc = 0.0f;
 #pragma unroll
         for (int s = 0; s < kMaxSplit; ++s)
             if (s < pin.nsplit) acc += v[s];
-        lg[e] = a.bias ? acc + a.bias[e] : acc;
-    }
+        lg[e] = a.bias ? acc + b : acc;
+    };
     // z (columns [0, lz)) and the shared expert's relu(h_s)^2 (columns
     // [lz, le)), rounded once to bf16
     bf16* zo = static_cast<bf16*>(a.z_w) + (size_t)t * a.l;
     bf16* so = a.m_s > 0 ? static_cast<bf16*>(a.a_s) + (size_t)t * a.m_s - pin.lz : nullptr;
-    for (int c = 4 * threadIdx.x; c < le; c += 1024) {
-        f32x4 v[kMaxSplit];
+    auto load_z = [&](int c, f32x4* v) {
+        const int cc = min(c, le - 4);
 #pragma unroll
-        for (int s = 0; s < kMaxSplit; ++s)
-            v[s] = s < pin.nsplit ? *reinterpret_cast<const f32x4*>(pt + s * ps + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < kMaxSplit; ++s) v[s] = *reinterpret_cast<const f32x4*>(pt + min(s, s_last) * ps + cc);
+    };
+    auto add_z = [&](int c, const f32x4* v) {
+        if (c >= le) return;
         f32x4 zs = v[0];
 #pragma unroll
         for (int s = 1; s < kMaxSplit; ++s)
@@ -188,6 +200,27 @@ __global__ __launch_bounds__(256) void topk_part_kernel(LayerArgs a, PartIn pin)
         }
         const bf16 b[4] = {(bf16)zs[0], (bf16)zs[1], (bf16)zs[2], (bf16)zs[3]};
         *reinterpret_cast<uint2*>((c < pin.lz ? zo : so) + c) = *reinterpret_cast<const uint2*>(b);
+    };
+    {
+        f32x4 zv[kMaxSplit];
+        float v0[kMaxSplit], v1[kMaxSplit], b0, b1;
+        const int c = 4 * (int)threadIdx.x, e = (int)threadIdx.x;
+        load_z(c, zv);
+        load_lg(e, v0, b0);
+        load_lg(e + 256, v1, b1);
+        add_z(c, zv);
+        add_lg(e, v0, b0);
+        add_lg(e + 256, v1, b1);
+    }
+    for (int e = (int)threadIdx.x + 512; e < a.N; e += 256) {
+        float v[kMaxSplit], b;
+        load_lg(e, v, b);
+        add_lg(e, v, b);
+    }
+    for (int c = 4 * (int)threadIdx.x + 1024; c < le; c += 1024) {
+        f32x4 v[kMaxSplit];
+        load_z(c, v);
+        add_z(c, v);
     }
     __syncthreads();
     if (threadIdx.x < 64) topk_token<NPL>(a, t, lg, s_key, s_idx, s_val);
