@@ -10,8 +10,10 @@ expert weights to the next.
 
 Prints ONE JSON line.  `roofline` is for the dominant kernel (the expert FFN):
 its algorithmic bytes (weights of the experts that received rows, read once)
-or flops per launch over its mean duration measured with HIP events recorded
-on the launch stream around that kernel in every timed step.  `cpu_baseline`
+or flops per launch over its mean duration measured with HIP events on the
+launch stream in every timed step (on the streaming path the FFN kernel's
+own start and end, attached to its launch; around the two tiled GEMMs
+otherwise).  `cpu_baseline`
 times the fp64 CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -180,7 +182,9 @@ def measure(w, sets, cpu_seconds: float) -> dict:
         step(i)
     # Timed region: the whole forward, with HIP events recorded on the launch
     # stream only around the expert FFN (the dominant kernel).
-    ffn_end = 5  # both FFN kernels: stages 3 and 4
+    # the FFN: stage 3 on the streaming path (its events are then the
+    # kernel's own start and end), stages 3 and 4 (two kernels) otherwise
+    ffn_end = 4 if path == B.LMOE_PATH_STREAM else 5
     ev_ffn = None
     if not args.no_events:
         ev_ffn = []

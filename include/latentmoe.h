@@ -167,8 +167,11 @@ int latentmoe_forward_shared(const void* x, const void* W_down, const void* W_ro
  * 0 projection + router logits (and the shared expert's two products),
  * 1 top-K gates, 2 dispatch, 3 expert FFN first kernel (the whole FFN on the
  * streaming path), 4 expert FFN second kernel (empty on the streaming path),
- * 5 combine, 6 projection back to d (empty in standard mode).  The
- * computation is the same as the untimed call's.
+ * 5 combine, 6 projection back to d (empty in standard mode).  On the
+ * streaming path, when events 3 and 4 are both given and the stream is not
+ * being captured, they are the FFN kernel's own start and end (recorded
+ * with its launch by hipExtLaunchKernel) instead of event packets around
+ * it.  The computation is the same as the untimed call's.
  */
 #define LMOE_N_STAGE_EVENTS 8
 int latentmoe_forward_timed(const void* x, const void* W_down, const void* W_router,

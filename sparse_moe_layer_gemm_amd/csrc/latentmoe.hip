@@ -10,6 +10,7 @@
 //   5. gate-weighted combine                (+ residual in standard mode)
 //   6. out = x + W_up s                     (latent mode)
 // No host synchronisation and no allocation happen inside a forward.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -372,34 +373,50 @@ void launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* events
         dispatch_scatter_kernel<<<p.nblk, b1024, lds, st>>>(a);
     }
     // 4. expert FFN
-    mark(3);
     const unsigned mt = (unsigned)p.max_tiles;
     if constexpr (sizeof(E) == 2) {
         if (p.path == LMOE_PATH_STREAM) {
+            // The streaming FFN is one kernel; when both of its stage events
+            // are given (and the stream is not being captured) they are the
+            // kernel's own start and end, recorded with its launch, rather
+            // than separate event packets around it.
+            hipEvent_t ev0 = events ? static_cast<hipEvent_t>(events[3]) : nullptr;
+            hipEvent_t ev1 = events ? static_cast<hipEvent_t>(events[4]) : nullptr;
+            hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+            if (ev0 && ev1 && hipStreamIsCapturing(st, &cap) != hipSuccess) cap = hipStreamCaptureStatusActive;
+            const bool own = ev0 && ev1 && cap == hipStreamCaptureStatusNone;
+            if (!own) mark(3);
+            auto launch = [&](auto kernel, dim3 grid) {
+                if (own)
+                    hipExtLaunchKernelGGL(kernel, grid, b256, 0, st, ev0, ev1, 0, a);
+                else
+                    kernel<<<grid, b256, 0, st>>>(a);
+            };
             // (MXFP4 pairs slices across the grid in chunks of 16 workgroups:
             // a multiple of 8 experts keeps every chunk whole)
             const dim3 g(p.nsplit, p.wfmt == 2 ? (unsigned)(cdiv(a.n_ffn, 8) * 8) : (unsigned)a.n_ffn);
             auto stream = [&](auto fmt) {
                 constexpr int F = decltype(fmt)::value;
                 if (F <= 1 && p.ms == 256)
-                    ffn_stream_kernel<256, F <= 1 ? F : 0><<<g, b256, 0, st>>>(a);
+                    launch(ffn_stream_kernel<256, F <= 1 ? F : 0>, g);
                 else if (p.ms == 128)
-                    ffn_stream_kernel<128, F><<<g, b256, 0, st>>>(a);
+                    launch(ffn_stream_kernel<128, F>, g);
                 else
-                    ffn_stream_kernel<64, F><<<g, b256, 0, st>>>(a);
+                    launch(ffn_stream_kernel<64, F>, g);
             };
             if (p.wfmt == 1)
                 stream(std::integral_constant<int, 1>{});
             else if (p.wfmt == 2 && p.ms == 256 && a.l % 256 == 0)
-                ffn_stream_mx_kernel<256><<<g, b256, 0, st>>>(a);   // 16-byte code loads
+                launch(ffn_stream_mx_kernel<256>, g);   // 16-byte code loads
             else if (p.wfmt == 2 && p.ms == 128 && a.l % 256 == 0 && a.m % 128 == 0)
-                ffn_stream_mx_kernel<128><<<g, b256, 0, st>>>(a);
+                launch(ffn_stream_mx_kernel<128>, g);
             else if (p.wfmt == 2)
                 stream(std::integral_constant<int, 2>{});
             else
                 stream(std::integral_constant<int, 0>{});
-            mark(4);
+            if (!own) mark(4);
         } else {
+            mark(3);
             auto ffn = [&](auto f1, auto f2) {
                 using F1 = decltype(f1);
                 using F2 = decltype(f2);
@@ -421,6 +438,7 @@ void launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* events
                 ffn(Ffn1<bf16>{}, Ffn2<bf16, YT>{});
         }
     } else {
+        mark(3);
         gemm_simt_kernel<Ffn1<float>><<<dim3(mt, cdiv(a.m, kSimtN)), b256, 0, st>>>(a);
         mark(4);
         gemm_simt_kernel<Ffn2<float, float>><<<dim3(mt, cdiv(a.l, kSimtN)), b256, 0, st>>>(a);
