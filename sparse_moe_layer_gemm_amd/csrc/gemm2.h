@@ -7,8 +7,12 @@
 // 256 x 256); a wave owns (BM/NWM) x (BN/NWN) outputs as 32 x 32 blocks of
 // v_mfma_f32_32x32x16_bf16.  The weight fragment is the MFMA's first
 // operand, so a lane's 16 accumulators of a block are 4 groups of 4
-// consecutive output columns of one row: the epilogue reads per-row data
-// (gate, token, residual row) once per lane and stores 4 columns at a time.
+// consecutive output columns of one row.  After a tile's last k-step its
+// accumulators go through LDS so that the stores cover whole rows: as bf16
+// after the epilogue for the expert FFN's problems (their epilogue needs only
+// the element, its row's gate and its column's scale), as fp32 before it for
+// the others (whose epilogues read per-column bias or per-element residual
+// data in the store layout).
 //
 // Pipeline: global -> registers two k-tiles ahead, registers -> LDS one
 // k-tile ahead (two LDS buffers).  In MFMA groups 0 and 1 of a k-tile,
