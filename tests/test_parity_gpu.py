@@ -120,6 +120,20 @@ def test_low_precision_decode_batch_sweep(sweep_low_precision, T):
     P.compare(w, {**inp, "x": inp["x"][:T]}, w.K, tag=f"{w0.name}_T{T}")
 
 
+# 256-wide m-slices on shapes the named workloads do not reach: one slice per
+# expert (m = 256) in every weight format, and two slices of MXFP4 experts
+# (m = 512: the slice pairing across XCDs).  1280 experts, top-32 of 160
+# tokens: ~1257 active experts expected, ~4 rows each.
+WIDE = [Workload(f"wide_one_{e}", T=160, d=256, l=256, N=1280, K=32, m=256, dtype="bf16", experts=e)
+        for e in ("dense", "fp8", "mxfp4")]
+WIDE.append(Workload("wide_paired_mxfp4", T=160, d=256, l=256, N=1280, K=32, m=512, dtype="bf16", experts="mxfp4"))
+
+
+@pytest.mark.parametrize("w", WIDE, ids=lambda w: w.name)
+def test_wide_slice_shapes(w):
+    P.compare(w, make_inputs(w, 12), w.K, tag=w.name)
+
+
 # --- the shared expert at full d ---------------------------------------------
 
 @pytest.mark.parametrize("path", [B.LMOE_PATH_AUTO, TL])
