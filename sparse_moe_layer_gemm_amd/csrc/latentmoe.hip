@@ -61,7 +61,10 @@ using G2Small = G2Cfg<128, 128, 2, 2, 2>;   // 4 waves, 64 KB LDS
 // (the tile list, shared by both FFN GEMMs, is cut at that height); with few
 // rows per expert the 256-row tile would be mostly padding.
 constexpr int kFfnLargeMinMeanRows = 512;
-using ProjTile = G2Small;
+// The tiled projection takes the large tile when it still makes at least one
+// tile per CU (many rows and columns: the latent layer's [z | logits] at
+// prefill), else the small one (the standard layer's few router columns).
+constexpr long long kProjLargeMinTiles = 256;
 using UpTile = G2Large;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -317,7 +320,10 @@ void launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* events
                 <<<dim3(cdiv(ncols_pr, 16), split, cdiv(a.T, 64)), b256, 0, st>>>(a, part, split, stride);
             pin = PartIn{part, split, stride, a.standard ? 0 : a.l};
         } else {
-            launch_g2<ProjRouter<bf16>, ProjTile>(a, cdiv(a.T, ProjTile::BM), cdiv(ncols_pr, ProjTile::BN), st);
+            if ((long long)cdiv(a.T, G2Large::BM) * cdiv(ncols_pr, G2Large::BN) >= kProjLargeMinTiles)
+                launch_g2<ProjRouter<bf16>, G2Large>(a, cdiv(a.T, G2Large::BM), cdiv(ncols_pr, G2Large::BN), st);
+            else
+                launch_g2<ProjRouter<bf16>, G2Small>(a, cdiv(a.T, G2Small::BM), cdiv(ncols_pr, G2Small::BN), st);
         }
     } else {
         gemm_simt_kernel<ProjRouter<float>><<<dim3(cdiv(a.T, kSimtM), cdiv(ncols_pr, kSimtN)), b256, 0, st>>>(a);
