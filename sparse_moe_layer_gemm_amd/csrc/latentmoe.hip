@@ -302,7 +302,8 @@ void launch_combine(const LayerArgs& a, int nsplit, int gated, hipStream_t st) {
 }
 
 template <class E, class YT>
-void launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* events) {
+hipError_t launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* events) {
+    hipError_t ext_err = hipSuccess;   // the one launch whose status is returned, not left as the last error
     auto mark = [&](int i) {
         if (events && events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(events[i]), st);
     };
@@ -393,10 +394,14 @@ void launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* events
             const bool own = ev0 && ev1 && cap == hipStreamCaptureStatusNone;
             if (!own) mark(3);
             auto launch = [&](auto kernel, dim3 grid) {
-                if (own)
-                    hipExtLaunchKernelGGL(kernel, grid, b256, 0, st, ev0, ev1, 0, a);
-                else
+                if (own) {
+                    void* args[] = {&a};
+                    const hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, b256, args, 0,
+                                                            st, ev0, ev1, 0);
+                    if (e != hipSuccess) ext_err = e;
+                } else {
                     kernel<<<grid, b256, 0, st>>>(a);
+                }
             };
             // (MXFP4 pairs slices across the grid in chunks of 16 workgroups:
             // a multiple of 8 experts keeps every chunk whole)
@@ -480,6 +485,7 @@ void launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* events
         }
     }
     mark(7);
+    return ext_err;
 }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -610,11 +616,10 @@ static int forward_impl(const void* x, const void* W_down, const void* W_router,
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    if (p.bf16)
-        launch_all<bf16, bf16>(p, a, st, events);
-    else
-        launch_all<float, float>(p, a, st, events);
-    const hipError_t err = hipGetLastError();
+    const hipError_t launch_err =
+        p.bf16 ? launch_all<bf16, bf16>(p, a, st, events) : launch_all<float, float>(p, a, st, events);
+    const hipError_t last_err = hipGetLastError();
+    const hipError_t err = launch_err != hipSuccess ? launch_err : last_err;
     if (err != hipSuccess) return fail(LMOE_EHIP, "HIP launch failed: %s", hipGetErrorString(err));
     return LMOE_OK;
 }
