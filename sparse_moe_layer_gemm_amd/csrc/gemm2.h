@@ -103,6 +103,17 @@ template <class R, class = void>
 struct Bf16Tile : std::false_type {};
 template <class R>
 struct Bf16Tile<R, std::void_t<decltype(R::kBf16Tile)>> : std::integral_constant<bool, R::kBf16Tile> {};
+// RowCtx<P>::kElem (a per-element operand, elem_load(), added to the
+// accumulator before the epilogue) and kNtStores (streaming stores; true
+// where a problem does not say), for bf16 tiles
+template <class R, class = void>
+struct ElemOp : std::false_type {};
+template <class R>
+struct ElemOp<R, std::void_t<decltype(R::kElem)>> : std::integral_constant<bool, R::kElem> {};
+template <class R, class = void>
+struct NtStores : std::true_type {};
+template <class R>
+struct NtStores<R, std::void_t<decltype(R::kNtStores)>> : std::integral_constant<bool, R::kNtStores> {};
 // RowCtx<P>::kColScale (a float per output column, applied first), false
 // where a problem does not define it
 template <class R, class = void>
@@ -194,6 +205,15 @@ struct RowCtx<Ffn2<bf16, bf16>> {
 template <>
 struct RowCtx<Up<bf16>> {
     static constexpr bool kRowVal = false;
+    // bf16 tile: the residual (4 bf16 of x per granule) is loaded per lane in
+    // the accumulators' layout and added before the single rounding; plain
+    // stores (the output is the layer's, read by the caller)
+    static constexpr bool kBf16Tile = true, kElem = true, kNtStores = false;
+    __device__ static uint2 elem_load(const LayerArgs& a, int r, int c0) {
+        return *reinterpret_cast<const uint2*>(static_cast<const bf16*>(a.x) + (size_t)r * a.d + c0);
+    }
+    __device__ static f32x4 tile_op(f32x4 v, float) { return v; }
+    __device__ static bf16* tile_row(const LayerArgs& a, int r) { return static_cast<bf16*>(a.out) + (size_t)r * a.d; }
     __device__ static float row_value(const LayerArgs&, int, int) { return 0.0f; }
     using ColPre = NoPre;
     __device__ static NoPre col_load(const LayerArgs&, int, int) { return NoPre{}; }
@@ -539,6 +559,24 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm2_kernel(LayerArgs a, int 
 #pragma unroll
         for (int h = 0; h < kRounds; ++h) {
             if (h > 0) __syncthreads();   // the previous round's reads are done
+            // per-element operands of this round, all loaded before the first
+            // LDS write (rows past the tile's end and columns past ncols read
+            // valid ones; their results are not stored)
+            [[maybe_unused]] uint2 el[S::FM / kRounds][S::FN][4];
+            if constexpr (ElemOp<RowCtx<P>>::value) {
+#pragma unroll
+                for (int ii = 0; ii < S::FM / kRounds; ++ii) {
+                    const int i = h * (S::FM / kRounds) + ii;
+                    const int row = min(ct.row0 + wm * S::WM + i * 32 + x, ct.row_end - 1);
+#pragma unroll
+                    for (int j = 0; j < S::FN; ++j)
+#pragma unroll
+                        for (int q4 = 0; q4 < 4; ++q4) {
+                            const int col = min(ct.col0 + wn * S::WN + j * 32 + 8 * q4 + 4 * (lane >> 5), ncols - 4);
+                            el[ii][j][q4] = RowCtx<P>::elem_load(a, row, col);
+                        }
+                }
+            }
 #pragma unroll
             for (int ii = 0; ii < S::FM / kRounds; ++ii) {
                 const int i = h * (S::FM / kRounds) + ii;
@@ -551,6 +589,13 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm2_kernel(LayerArgs a, int 
                         const int q = (wn * S::WN + j * 32 + 8 * q4 + 4 * (lane >> 5)) >> 2;
                         f32x4 v = {acc[i][j][4 * q4], acc[i][j][4 * q4 + 1], acc[i][j][4 * q4 + 2], acc[i][j][4 * q4 + 3]};
                         if constexpr (kColS) v *= *reinterpret_cast<const f32x4*>(&colval[4 * q]);
+                        if constexpr (ElemOp<RowCtx<P>>::value) {
+                            const uint2 u = el[ii][j][q4];
+                            v[0] += __uint_as_float(u.x << 16);
+                            v[1] += __uint_as_float(u.x & 0xffff0000u);
+                            v[2] += __uint_as_float(u.y << 16);
+                            v[3] += __uint_as_float(u.y & 0xffff0000u);
+                        }
                         v = RowCtx<P>::tile_op(v, g);
                         const bf16 b[4] = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
                         tg[rl * (BN / 4) + (q ^ x)] = *reinterpret_cast<const uint2*>(b);
@@ -566,7 +611,10 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm2_kernel(LayerArgs a, int 
                     const int y = rl & 31;
                     uint4 w = reinterpret_cast<const uint4*>(tg)[rl * kUnits + (p ^ (y >> 1))];
                     if (y & 1) w = uint4{w.z, w.w, w.x, w.y};
-                    st_nt16(RowCtx<P>::tile_row(a, row) + c, w);
+                    if constexpr (NtStores<RowCtx<P>>::value)
+                        st_nt16(RowCtx<P>::tile_row(a, row) + c, w);
+                    else
+                        *reinterpret_cast<uint4*>(RowCtx<P>::tile_row(a, row) + c) = w;
                 }
             }
         }
