@@ -9,10 +9,11 @@
 // operand, so a lane's 16 accumulators of a block are 4 groups of 4
 // consecutive output columns of one row.  After a tile's last k-step its
 // accumulators go through LDS so that the stores cover whole rows: as bf16
-// after the epilogue for the expert FFN's problems (their epilogue needs only
-// the element, its row's gate and its column's scale), as fp32 before it for
-// the others (whose epilogues read per-column bias or per-element residual
-// data in the store layout).
+// after the epilogue for the expert FFN's problems and the up-projection
+// (their epilogues need only the element, its row's gate, its column's scale
+// or the residual element, which each lane loads in the accumulators'
+// layout), as fp32 before it for the projection (mixed bf16 / fp32 outputs
+// and a per-column bias, applied in the store layout).
 //
 // Pipeline: global -> registers two k-tiles ahead, registers -> LDS one
 // k-tile ahead (two LDS buffers).  In MFMA groups 0 and 1 of a k-tile,
