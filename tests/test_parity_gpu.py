@@ -134,6 +134,42 @@ def test_wide_slice_shapes(w):
     P.compare(w, make_inputs(w, 12), w.K, tag=w.name)
 
 
+# Seeded random shapes across the options (sizes, formats, shared expert,
+# zero-computation experts, bias, standard mode, both paths), drawn once
+# at import, to reach combinations the named cases do not.
+def _random_shapes(n, seed=2024):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        standard = rng.random() < 0.25
+        d = int(rng.choice([128, 192, 256, 384, 512]))
+        l = d if standard else int(rng.choice([x for x in (64, 128, 192, 256) if x <= d]))
+        m = int(rng.choice([64, 128, 192, 256, 320, 512]))
+        experts = str(rng.choice(["dense", "dense", "fp8", "mxfp4"]))
+        dtype = "bf16" if experts != "dense" or rng.random() < 0.8 else "f32"
+        N = int(rng.integers(4, 600))
+        nz = [int(x) for x in rng.integers(0, 3, size=3)] if rng.random() < 0.3 else [0, 0, 0]
+        K = int(rng.integers(1, min(32, N + sum(nz)) + 1))
+        T = int(rng.choice([1, 3, 17, 64, 129, 300, 777]))
+        m_s = int(rng.choice([0, 0, 64, 128]))
+        bias = bool(rng.random() < 0.3)
+        out.append(Workload(f"rand{i}", T=T, d=d, l=l, N=N, K=K, m=m, dtype=dtype, standard=standard,
+                            bias=bias, m_shared=m_s, experts=experts, n_zero=nz[0], n_copy=nz[1], n_const=nz[2]))
+    return out
+
+
+RANDOM_SHAPES = _random_shapes(12)
+
+
+@pytest.mark.parametrize("w", RANDOM_SHAPES, ids=lambda w: w.name)
+@pytest.mark.parametrize("path", [B.LMOE_PATH_AUTO, S, TL])
+def test_random_shapes(w, path):
+    if w.dtype == "f32" and path == S:
+        pytest.skip("the streaming FFN is bf16 only")
+    P.log(f"[rand] {w}")
+    P.compare(w, make_inputs(w, 13), w.K, path=path, tag=f"{w.name}/path{path}")
+
+
 # --- the shared expert at full d ---------------------------------------------
 
 @pytest.mark.parametrize("path", [B.LMOE_PATH_AUTO, TL])
