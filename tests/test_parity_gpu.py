@@ -153,12 +153,12 @@ def _random_shapes(n, seed=2024):
         T = int(rng.choice([1, 3, 17, 64, 129, 300, 777]))
         m_s = int(rng.choice([0, 0, 64, 128]))
         bias = bool(rng.random() < 0.3)
-        out.append(Workload(f"rand{i}", T=T, d=d, l=l, N=N, K=K, m=m, dtype=dtype, standard=standard,
+        out.append(Workload(f"rand{seed}_{i}", T=T, d=d, l=l, N=N, K=K, m=m, dtype=dtype, standard=standard,
                             bias=bias, m_shared=m_s, experts=experts, n_zero=nz[0], n_copy=nz[1], n_const=nz[2]))
     return out
 
 
-RANDOM_SHAPES = _random_shapes(12)
+RANDOM_SHAPES = _random_shapes(12) + _random_shapes(12, seed=7)
 
 
 @pytest.mark.parametrize("w", RANDOM_SHAPES, ids=lambda w: w.name)
