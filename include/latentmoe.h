@@ -51,9 +51,12 @@
  * W1 [N, m, l/2] and W2 [N, l, m/2] bytes hold two E2M1 codes each (sign,
  * 2 exponent bits with bias 1, 1 mantissa bit), the even element in the low
  * nibble; W1_scale [N, m, l/32] and W2_scale [N, l, m/32] bytes hold one
- * E8M0 scale (2^(b-127), b in 1 .. 254) per 32 consecutive elements along
- * the reduction index: weight = e2m1(code) * 2^(b-127).  The nibble order,
- * the blocks' direction and the scale range are readings.
+ * E8M0 scale (2^(b-127)) per 32 consecutive elements along the reduction
+ * index: weight = e2m1(code) * 2^(b-127).  Scale bytes 1 .. 254 are decoded
+ * exactly; byte 0 (2^-127) decodes to 0, which changes a product term by at
+ * most 6 * 2^-127 (below every nonzero float32 sum it joins); byte 255 (NaN
+ * in the format) is not supported and gives undefined results.  The nibble
+ * order, the blocks' direction and the scale range are readings.
  * Optional zero-computation experts (through latentmoe_forward_ex; after
  * MoE++, 10100.com article, section 3.2): dims.n_zero zero experts,
  * dims.n_copy copy experts and dims.n_const constant experts take the
@@ -134,7 +137,10 @@ size_t latentmoe_workspace_bytes(const lmoe_dims* dims, int32_t K);
  * (it changes both the selection and the gates).
  * topk_ids / topk_gates: NULL, or caller buffers that receive the selected
  * experts in rank order (largest logit first) and their gates.
- * out must not alias x or any weight.  dims->m_shared must be 0 (the shared
+ * The buffers the call writes -- out, topk_ids, topk_gates and the
+ * workspace -- must not overlap one another or any array it reads (x, the
+ * weights, their scales, zc_const, router_bias): LMOE_EINVAL otherwise, from
+ * the byte ranges the dims give.  dims->m_shared must be 0 (the shared
  * expert goes through latentmoe_forward_shared) and dims->expert_format
  * LMOE_EXPERTS_DENSE (FP8 experts go through latentmoe_forward_ex).
  */
@@ -186,8 +192,9 @@ int latentmoe_forward_timed(const void* x, const void* W_down, const void* W_rou
  * The general entry point: every option of the layer in one argument block.
  * Pointers as in latentmoe_forward; W_shared1 / W_shared2 with
  * dims->m_shared > 0 (else NULL); W1_scale / W2_scale with FP8 or MXFP4
- * experts (else NULL; FP8 float32 scales 16-byte aligned); zc_const [n_const, l] with dims->n_const > 0 (else NULL; 16-byte
- * aligned); events NULL or as in latentmoe_forward_timed.  The other
+ * experts (else NULL; FP8 float32 scales 16-byte aligned, MXFP4 scale
+ * bytes 8-byte aligned); zc_const [n_const, l] with dims->n_const > 0 (else
+ * NULL; 16-byte aligned); events NULL or as in latentmoe_forward_timed.  The other
  * forward entry points are this call with the options they do not name
  * turned off.
  */

@@ -494,6 +494,55 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     return pa < pb + nb && pb < pa + na;
 }
 
+// The buffers a forward writes (out, the routing buffers, the workspace) must
+// not overlap one another or any array it reads; a NULL pointer spans nothing.
+int check_aliasing(const Plan& p, const lmoe_dims& d, int K, bool standard, const void* x, const void* W_down,
+                   const void* W_router, const void* W1, const void* W2, const void* W_up, const void* W_s1,
+                   const void* W_s2, const void* w1s, const void* w2s, const void* zc_const, const float* bias,
+                   const void* out, const int32_t* ids, const float* gates, const void* workspace) {
+    struct Span {
+        const void* ptr;
+        size_t bytes;
+        const char* name;
+    };
+    const size_t es = p.es, T = d.T, dd = d.d, l = d.l, N = d.N, m = d.m, nr = p.nr, ms = d.m_shared;
+    // expert weight bytes per element: the layer's type, an FP8 code, half an MXFP4 byte
+    const double wb = p.wfmt == 0 ? (double)es : (p.wfmt == 1 ? 1.0 : 0.5);
+    const size_t wexp = (size_t)(wb * (double)(N * m * l));
+    const size_t s1b = p.wfmt == 1 ? N * m * 4 : N * m * (l / 32), s2b = p.wfmt == 1 ? N * l * 4 : N * l * (m / 32);
+    const Span in[] = {
+        {x, T * dd * es, "x"},
+        {standard ? nullptr : W_down, l * dd * es, "W_down"},
+        {W_router, nr * dd * es, "W_router"},
+        {W1, wexp, "W1"},
+        {W2, wexp, "W2"},
+        {standard ? nullptr : W_up, dd * l * es, "W_up"},
+        {W_s1, ms * dd * es, "W_shared1"},
+        {W_s2, dd * ms * es, "W_shared2"},
+        {p.wfmt ? w1s : nullptr, s1b, "W1_scale"},
+        {p.wfmt ? w2s : nullptr, s2b, "W2_scale"},
+        {zc_const, (size_t)d.n_const * l * es, "zc_const"},
+        {bias, nr * 4, "router_bias"},
+    };
+    const size_t tk = T * (size_t)K;
+    const Span wr[] = {
+        {out, T * dd * es, "out"},
+        {ids, tk * 4, "topk_ids"},
+        {gates, tk * 4, "topk_gates"},
+        {workspace, p.total, "the workspace"},
+    };
+    for (size_t i = 0; i < sizeof wr / sizeof wr[0]; ++i) {
+        if (!wr[i].ptr) continue;
+        for (const Span& r : in)
+            if (r.ptr && overlaps(wr[i].ptr, wr[i].bytes, r.ptr, r.bytes))
+                return fail(LMOE_EINVAL, "%s must not alias %s", wr[i].name, r.name);
+        for (size_t j = 0; j < i; ++j)
+            if (wr[j].ptr && overlaps(wr[i].ptr, wr[i].bytes, wr[j].ptr, wr[j].bytes))
+                return fail(LMOE_EINVAL, "%s must not alias %s", wr[i].name, wr[j].name);
+    }
+    return LMOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -545,12 +594,14 @@ static int forward_impl(const void* x, const void* W_down, const void* W_router,
         return fail(LMOE_EINVAL, "FP8 W1_scale and W2_scale must be 16-byte aligned");
     if ((d.n_const > 0) != (zc_const != nullptr))
         return fail(LMOE_EINVAL, "zc_const must be set when n_const > 0 and NULL otherwise (n_const=%d)", d.n_const);
+    if (p.wfmt == 2 && ((reinterpret_cast<uintptr_t>(w1s) & 7) != 0 || (reinterpret_cast<uintptr_t>(w2s) & 7) != 0))
+        return fail(LMOE_EINVAL, "MXFP4 W1_scale and W2_scale must be 8-byte aligned");
     if (!workspace) return fail(LMOE_EWORKSPACE, "workspace is NULL");
+    if (const int rc = check_aliasing(p, d, K, standard, x, W_down, W_router, W1, W2, W_up, W_s1, W_s2, w1s, w2s,
+                                      zc_const, router_bias, out, topk_ids, topk_gates, workspace))
+        return rc;
     if (workspace_bytes < p.total)
         return fail(LMOE_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, p.total);
-    const size_t xbytes = (size_t)d.T * d.d * p.es;
-    if (overlaps(out, xbytes, x, xbytes)) return fail(LMOE_EINVAL, "out must not alias x");
-    if (overlaps(out, xbytes, workspace, p.total)) return fail(LMOE_EINVAL, "out must not alias the workspace");
     if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
         return fail(LMOE_EINVAL, "workspace must be 256-byte aligned");
     const void* ptrs[] = {x, W_down, W_router, W1, W2, W_up, W_s1, W_s2, zc_const, out};

@@ -159,7 +159,8 @@ __global__ __launch_bounds__(256) void topk_part_kernel(LayerArgs a, PartIn pin)
     // the first two logits of each thread are loaded together, so the usual
     // sizes (le <= 1024, N <= 512) take one round trip to memory.  The loads
     // are unconditional (indices past the end and splits past nsplit are
-    // clamped to valid ones, and their values not used): conditional loads
+    // clamped to valid ones inside the partial rows, and their values not
+    // used): conditional loads
     // compile to branches that each wait for the loads before them.
     const int s_last = pin.nsplit - 1;
     auto load_lg = [&](int e, float* v, float& b) {
@@ -181,7 +182,9 @@ __global__ __launch_bounds__(256) void topk_part_kernel(LayerArgs a, PartIn pin)
     bf16* zo = static_cast<bf16*>(a.z_w) + (size_t)t * a.l;
     bf16* so = a.m_s > 0 ? static_cast<bf16*>(a.a_s) + (size_t)t * a.m_s - pin.lz : nullptr;
     auto load_z = [&](int c, f32x4* v) {
-        const int cc = min(c, le - 4);
+        // (with no z or h_s columns, le == 0, column 0 is a logit column:
+        // still inside the partial row, and add_z() skips the value)
+        const int cc = max(0, min(c, le - 4));
 #pragma unroll
         for (int s = 0; s < kMaxSplit; ++s) v[s] = *reinterpret_cast<const f32x4*>(pt + min(s, s_last) * ps + cc);
     };

@@ -97,7 +97,9 @@ def call(dims, K, **over):
                 workspace=FAKE + (7 << 30), workspace_bytes=B.latentmoe_workspace_bytes(dims, K) if K else 0)
     args.update(over)
     return B.latentmoe_forward(args["x"], args["W_down"], args["W_router"], args["W1"], args["W2"],
-                               args["W_up"], K, args["out"], dims, workspace=args["workspace"],
+                               args["W_up"], K, args["out"], dims, router_bias=args.get("bias"),
+                               topk_ids=args.get("ids"), topk_gates=args.get("gates"),
+                               workspace=args["workspace"],
                                workspace_bytes=args["workspace_bytes"], stream=0, check=False)
 
 
@@ -120,6 +122,36 @@ def test_forward_argument_checks(lib):
     assert call(d, w.K, W2=FAKE + (4 << 30) + 2) == B.LMOE_EINVAL
     ws = B.make_dims(w.T, w.d, w.l, w.N, w.m, "f32", B.LMOE_PATH_STREAM)
     assert call(ws, w.K) == B.LMOE_EUNSUPPORTED
+
+
+def test_written_buffers_alias_nothing(lib):
+    """out, the routing buffers and the workspace may overlap neither one
+    another nor any array the call reads (the header's promise)."""
+    w = WORKLOADS["decode"]
+    d = dims_of(w)
+    GB = 1 << 30
+    IDS, GATES = FAKE + (8 << 30), FAKE + (9 << 30)
+    assert call(d, w.K, ids=IDS, gates=GATES, workspace_bytes=64) == B.LMOE_EWORKSPACE   # valid otherwise
+    last_w1 = FAKE + 3 * GB + w.N * w.m * w.l * 2 - 16                   # W1's last 16 bytes
+    cases = [
+        (dict(out=FAKE + 3 * GB + 4096), "out must not alias W1"),
+        (dict(out=last_w1), "out must not alias W1"),
+        (dict(out=FAKE + 2 * GB), "out must not alias W_router"),
+        (dict(out=FAKE + 5 * GB + 256), "out must not alias W_up"),
+        (dict(out=FAKE + 1 * GB), "out must not alias W_down"),
+        (dict(bias=FAKE + (6 << 30) + 64), "out must not alias router_bias"),
+        (dict(ids=FAKE + (6 << 30), gates=GATES), "topk_ids must not alias out"),
+        (dict(ids=IDS, gates=IDS + 64), "topk_gates must not alias topk_ids"),
+        (dict(ids=FAKE + 4 * GB, gates=GATES), "topk_ids must not alias W2"),
+        (dict(ids=IDS, gates=FAKE), "topk_gates must not alias x"),
+        (dict(ids=IDS, gates=FAKE + (7 << 30) + 256), "the workspace must not alias topk_gates"),
+        (dict(workspace=FAKE + 4 * GB), "the workspace must not alias W2"),
+    ]
+    for over, msg in cases:
+        assert call(d, w.K, **over) == B.LMOE_EINVAL, over
+        assert msg in B.latentmoe_last_error(), (over, B.latentmoe_last_error())
+    # adjacent is fine: out right after W1's last byte (then the workspace size check fails)
+    assert call(d, w.K, out=last_w1 + 16, workspace_bytes=64) == B.LMOE_EWORKSPACE
 
 
 def call_shared(dims, K, **over):
@@ -201,8 +233,11 @@ def test_mxfp4_expert_argument_checks(lib):
             B.latentmoe_workspace_bytes(dims_of(WORKLOADS["decode"].replace(T=T)), w.K)
     assert call_ex(d, w.K, W1_scale=None, W2_scale=None) == B.LMOE_EINVAL   # scales required
     assert call_ex(d, w.K, W2_scale=None) == B.LMOE_EINVAL
-    # byte scales need no alignment (validation passes them, then the workspace check fails)
-    assert call_ex(d, w.K, W1_scale=FAKE + (10 << 30) + 3, workspace_bytes=64) == B.LMOE_EWORKSPACE
+    # the streaming kernel reads a row's scale bytes as 8-byte vectors
+    assert call_ex(d, w.K, W1_scale=FAKE + (10 << 30) + 3) == B.LMOE_EINVAL
+    assert call_ex(d, w.K, W2_scale=FAKE + (11 << 30) + 4) == B.LMOE_EINVAL
+    assert "8-byte" in B.latentmoe_last_error()
+    assert call_ex(d, w.K, W1_scale=FAKE + (10 << 30) + 8, workspace_bytes=64) == B.LMOE_EWORKSPACE
     f32 = dims_of(WORKLOADS["tiny_f32"].replace(experts="mxfp4"))
     assert call_ex(f32, 4) == B.LMOE_EUNSUPPORTED
     big = dims_of(w.replace(m=65536, l=65536))

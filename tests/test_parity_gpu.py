@@ -329,6 +329,24 @@ def test_mxfp4_every_byte(w, path):
 
 @pytest.mark.parametrize("w", MX_POW2, ids=lambda w: w.name)
 @pytest.mark.parametrize("path", [S, TL])
+def test_mxfp4_scale_byte_zero(w, path):
+    """E8M0 scale byte 0 (2^-127): the kernels decode such a block to 0, the
+    oracle to its exact value; each product term differs by at most
+    6 * 2^-127, far below anything the fp32 sums keep, so the two agree
+    within the usual bar.  A quarter of the blocks, and every block of
+    expert 0's W1, get byte 0."""
+    inp = make_inputs(w, 21)
+    g = torch.Generator().manual_seed(22)
+    for name in ("W1_scale", "W2_scale"):
+        sc = inp[name].clone()
+        sc[torch.rand(sc.shape, generator=g) < 0.25] = 0
+        inp[name] = sc.contiguous()
+    inp["W1_scale"][0] = 0
+    P.compare(w, inp, w.K, path=path, tag=f"{w.name}_scale_byte_zero/path{path}")
+
+
+@pytest.mark.parametrize("w", MX_POW2, ids=lambda w: w.name)
+@pytest.mark.parametrize("path", [S, TL])
 def test_mxfp4_layer_is_the_bf16_layer_on_decoded_weights(w, path):
     """Every E2M1 value times a power-of-two block scale is a bfloat16 value,
     so where the MXFP4 kernels group the dot products' terms as the bf16
