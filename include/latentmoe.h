@@ -222,6 +222,28 @@ typedef struct {
 
 int latentmoe_forward_ex(const lmoe_args* args, int32_t K, const lmoe_dims* dims);
 
+/*
+ * latentmoe_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  The workspace is a static
+ * device array of the library, LMOE_NOALLOC_SCRATCH_BYTES (64 MiB) per
+ * device, created when the library's code is loaded on a device and held
+ * until the process ends; the call allocates nothing.  Dims whose
+ * latentmoe_workspace_bytes() exceeds that size are rejected with
+ * LMOE_EUNSUPPORTED (at d = 4096, l = 1024, 512 experts, top-22 that is
+ * T > 128).  Every call on one device uses the same array and leaves the
+ * last call's routing data in it: calls that may overlap on one device --
+ * on two streams, or from two threads -- race and must be serialised by
+ * the caller.  Arguments, results, errors and the stream rules are those of
+ * latentmoe_forward; the first call on a device also looks up the array's
+ * address (hipGetSymbolAddress), whose failure returns LMOE_EHIP.
+ */
+#define LMOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+int latentmoe_forward_noalloc(const void* x, const void* W_down, const void* W_router,
+                              const void* W1, const void* W2, const void* W_up, int32_t K,
+                              void* out, const lmoe_dims* dims, const float* router_bias,
+                              int32_t* topk_ids, float* topk_gates, void* stream);
+
 /* Static text for a status code. */
 const char* latentmoe_status_string(int status);
 

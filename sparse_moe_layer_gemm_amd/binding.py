@@ -29,6 +29,7 @@ EXPORTED = (
     "latentmoe_forward_shared",
     "latentmoe_forward_timed",
     "latentmoe_forward_ex",
+    "latentmoe_forward_noalloc",
     "latentmoe_status_string",
     "latentmoe_last_error",
     "latentmoe_resolved_path",
@@ -83,6 +84,9 @@ def lib():
                                               ctypes.POINTER(lmoe_dims), P, P, P, P, ctypes.c_size_t, P, P]
         L.latentmoe_forward_ex.restype = ctypes.c_int
         L.latentmoe_forward_ex.argtypes = [ctypes.POINTER(lmoe_args), ctypes.c_int32, ctypes.POINTER(lmoe_dims)]
+        L.latentmoe_forward_noalloc.restype = ctypes.c_int
+        L.latentmoe_forward_noalloc.argtypes = [P, P, P, P, P, P, ctypes.c_int32, P, ctypes.POINTER(lmoe_dims),
+                                                P, P, P, P]
         L.latentmoe_status_string.restype = ctypes.c_char_p
         L.latentmoe_status_string.argtypes = [ctypes.c_int]
         L.latentmoe_last_error.restype = ctypes.c_char_p
@@ -187,6 +191,29 @@ def latentmoe_forward(x, W_down, W_router, W1, W2, W_up, K: int, out, dims: lmoe
         rc = lib().latentmoe_forward_shared(*head, *shared, *tail)
     else:
         rc = lib().latentmoe_forward(*head, *tail)
+    if check:
+        _check(rc)
+    return rc
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def latentmoe_forward_noalloc(x, W_down, W_router, W1, W2, W_up, K: int, out, dims: lmoe_dims,
+                              router_bias=None, topk_ids=None, topk_gates=None, stream=None,
+                              check: bool = True) -> int:
+    """The no-workspace entry point (the library's own static scratch).
+    `stream` as in latentmoe_forward.  Returns the status (raises on failure
+    when check=True)."""
+    if stream is None:
+        stream_ptr = torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
+    elif isinstance(stream, int):
+        stream_ptr = stream
+    else:
+        stream_ptr = stream.cuda_stream
+    rc = lib().latentmoe_forward_noalloc(_ptr(x), _ptr(W_down), _ptr(W_router), _ptr(W1), _ptr(W2), _ptr(W_up),
+                                         int(K), _ptr(out), ctypes.byref(dims), _ptr(router_bias), _ptr(topk_ids),
+                                         _ptr(topk_gates), stream_ptr)
     if check:
         _check(rc)
     return rc

@@ -543,6 +543,39 @@ int check_aliasing(const Plan& p, const lmoe_dims& d, int K, bool standard, cons
     return LMOE_OK;
 }
 
+// Device memory of latentmoe_forward_noalloc, for callers that cannot
+// allocate: one copy of this array per device, held until the process ends.
+// In host code `scratch` names a host-side stand-in, not the device array:
+// host code uses only the address hipGetSymbolAddress gives for the current
+// device (scratch_address()).
+constexpr size_t kScratchBytes = LMOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// The device address of `scratch` on the current device, taken once per
+// device (with that device current), or NULL with the failure recorded.
+void* scratch_address() {
+    constexpr int kMaxDevices = 64;
+    static std::once_flag flags[kMaxDevices];
+    static void* addr[kMaxDevices];
+    static hipError_t err[kMaxDevices];
+    int dev = -1;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        fail(LMOE_EHIP, "hipGetDevice failed or device %d is out of range: %s", dev, hipGetErrorString(e));
+        return nullptr;
+    }
+    std::call_once(flags[dev], [dev] {
+        void* p = nullptr;
+        err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        addr[dev] = err[dev] == hipSuccess ? p : nullptr;
+    });
+    if (err[dev] != hipSuccess || !addr[dev]) {
+        fail(LMOE_EHIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(err[dev]));
+        return nullptr;
+    }
+    return addr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -718,6 +751,24 @@ int latentmoe_forward_timed(const void* x, const void* W_down, const void* W_rou
     if (const int rc = plain_options_only(dims)) return rc;
     return forward_impl(x, W_down, W_router, W1, W2, W_up, W_shared1, W_shared2, nullptr, nullptr, nullptr, K, out, dims,
                         router_bias, topk_ids, topk_gates, workspace, workspace_bytes, stream, events);
+}
+
+int latentmoe_forward_noalloc(const void* x, const void* W_down, const void* W_router, const void* W1,
+                              const void* W2, const void* W_up, int32_t K, void* out, const lmoe_dims* dims,
+                              const float* router_bias, int32_t* topk_ids, float* topk_gates, void* stream) {
+    if (dims && dims->m_shared != 0)
+        return fail(LMOE_EINVAL, "m_shared=%d: a shared expert goes through latentmoe_forward_shared",
+                    dims->m_shared);
+    if (const int rc = plain_options_only(dims)) return rc;
+    const Plan p = make_plan(dims, K);
+    if (p.status != LMOE_OK) return p.status;
+    if (p.total > kScratchBytes)
+        return fail(LMOE_EUNSUPPORTED, "these dims need %zu bytes of workspace; latentmoe_forward_noalloc has %zu",
+                    p.total, kScratchBytes);
+    void* ws = scratch_address();
+    if (!ws) return LMOE_EHIP;
+    return forward_impl(x, W_down, W_router, W1, W2, W_up, nullptr, nullptr, nullptr, nullptr, nullptr, K, out, dims,
+                        router_bias, topk_ids, topk_gates, ws, kScratchBytes, stream, nullptr);
 }
 
 int latentmoe_forward_ex(const lmoe_args* g, int32_t K, const lmoe_dims* dims) {
