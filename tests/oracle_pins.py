@@ -367,6 +367,45 @@ def pin_selection_and_forced_ids(o):
     assert np.array_equal(rf["out"], r["out"][sel])
 
 
+def pin_forced_ids_reroute(o):
+    """Forcing other ids routes the token to them: the gates are the
+    softmax of the token's own logits renormalised over the forced set, in
+    the forced order, and the output uses the forced experts; compared with
+    a numpy float64 evaluation of the forced routing."""
+    T, d, l, N, K, m = 6, 32, 8, 9, 3, 8
+    L = rand_layer(17, T, d, l, N, m, bias=True)
+    r = run(o, L, K)
+    rng = _rng(18)
+    forced = np.empty((T, K), np.int32)
+    for t in range(T):
+        own = set(r["ids"][t].tolist())
+        # K distinct ids, at least one the token would not pick, in a
+        # scrambled order
+        outside = int(rng.choice([e for e in range(N) if e not in own]))
+        rest = rng.choice([e for e in range(N) if e != outside], size=K - 1, replace=False)
+        forced[t] = rng.permutation(np.concatenate([[outside], rest])).astype(np.int32)
+        assert set(forced[t].tolist()) != own
+    sel = np.arange(T, dtype=np.int32)
+    rf = run(o, L, K, sel=sel, forced_ids=forced)
+    assert np.array_equal(rf["ids"], forced), "the forced ids are the ones reported"
+    x = f64(L["x"])
+    z = x @ f64(L["W_down"]).T
+    lg = np_logits(L)
+    for t in range(T):
+        S = forced[t]
+        g = softmax(lg[t, S])
+        assert np.allclose(rf["gates"][t], g, rtol=1e-12, atol=0), "gates: softmax over the forced set"
+        s = np.zeros(l)
+        for k in range(K):
+            e = S[k]
+            y = (np.maximum(z[t] @ f64(L["W1"][e]).T, 0.0) ** 2) @ f64(L["W2"][e]).T
+            s += g[k] * y
+        want = x[t] + s @ f64(L["W_up"]).T
+        assert np.allclose(rf["out"][t], want, rtol=1e-12, atol=1e-13), "output with the forced experts"
+        # the gap still describes the token's own selection
+        assert rf["gap"][t] == r["gap"][t]
+
+
 def pin_shared_expert(o):
     """The shared expert at full d: a dense FFN on x added to the layer."""
     for standard in (False, True):
@@ -588,6 +627,7 @@ ALL_PINS = [
     pin_homogeneity,
     pin_symmetries,
     pin_selection_and_forced_ids,
+    pin_forced_ids_reroute,
     pin_shared_expert,
     pin_fp8_experts,
     pin_zero_computation_experts,

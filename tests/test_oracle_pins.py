@@ -85,6 +85,19 @@ MUTANTS = {
     "zc_copy_gate_dropped": ("s[i] += g * z[i];", "s[i] += z[i];"),
     "zc_const_first_only": ("q -= D->n_copy; /* constant", "q = 0; /* constant"),
     "zc_const_gate_dropped": ("s[i] += g * widen(zc,", "s[i] += widen(zc,"),
+    "forced_ids_ignored": ("if (forced) for (int k = 0; k < K; ++k) ids_t[k] = forced[k];", "(void)forced;"),
+    "forced_ids_first_only": ("if (forced) for (int k = 0; k < K; ++k) ids_t[k] = forced[k];",
+                              "if (forced) ids_t[0] = forced[0];"),
+    "forced_gates_from_own_set": (
+        "    if (forced) for (int k = 0; k < K; ++k) ids_t[k] = forced[k];\n\n"
+        "    /* step 3c: renormalise the kept probabilities */\n"
+        "    double kept = 0.0;\n"
+        "    for (int k = 0; k < K; ++k) kept += p[ids_t[k]];\n"
+        "    for (int k = 0; k < K; ++k) gates_t[k] = p[ids_t[k]] / kept;\n",
+        "    double kept = 0.0;\n"
+        "    for (int k = 0; k < K; ++k) kept += p[ids_t[k]];\n"
+        "    for (int k = 0; k < K; ++k) gates_t[k] = p[ids_t[k]] / kept;\n"
+        "    if (forced) for (int k = 0; k < K; ++k) ids_t[k] = forced[k];\n"),
 }
 
 
