@@ -5,7 +5,10 @@
 //
 // The expert outputs sit in `nsplit` partial planes (the streaming FFN's
 // m-slices; 1 for the tiled FFN) of [T*K, l] each.  `gated`: multiply by the
-// gate here (streaming FFN) or not (the tiled FFN already did).
+// gate here (streaming FFN) or not (the tiled FFN already did).  YT: float
+// (the streaming FFN's partials, the float32 layer) or f16, the tiled FFN's
+// gate-scaled outputs times kYScale (summed as they are, then scaled back
+// once: a power of two, so no extra rounding).
 // Zero-computation experts (ids >= n_ffn) have no expert output.  Their
 // slots are the last ones (ids sort after the FFN experts), so a rank is
 // theirs when its slot is at or past offsets[n_ffn]; such ranks read the
@@ -14,6 +17,8 @@
 // g * z for a copy expert, g * its vector for a constant expert (MoE++'s
 // three kinds: 10100.com article, section 3.2).
 #pragma once
+
+#include <type_traits>
 
 #include "layer.h"
 
@@ -69,12 +74,10 @@ __global__ __launch_bounds__(256) void combine_kernel(LayerArgs a, int nsplit, i
             uint4 raw = ldg16(yp);
             float part[VPC];
             if constexpr (VPC == 8) {
-                const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+                static_assert(std::is_same<YT, f16>::value, "2-byte expert outputs are scaled half precision");
+                const f32x8 f = __builtin_convertvector(__builtin_bit_cast(f16x8, raw), f32x8);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    part[2 * i] = __uint_as_float(w[i] << 16);
-                    part[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-                }
+                for (int i = 0; i < 8; ++i) part[i] = f[i];
             } else {
                 part[0] = __uint_as_float(raw.x);
                 part[1] = __uint_as_float(raw.y);
@@ -99,6 +102,10 @@ __global__ __launch_bounds__(256) void combine_kernel(LayerArgs a, int nsplit, i
             const float gk = gated ? gt[k] : 1.0f;
 #pragma unroll
             for (int i = 0; i < VPC; ++i) acc[i] = fmaf(gk, part[i], acc[i]);
+        }
+        if constexpr (std::is_same<YT, f16>::value) {
+#pragma unroll
+            for (int i = 0; i < VPC; ++i) acc[i] *= kYUnscale;
         }
         const int* idk = a.ids + (size_t)t * a.K;
         while (zranks) {

@@ -8,6 +8,9 @@ namespace lmoe {
 
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -95,6 +98,29 @@ __device__ __forceinline__ void st_nt16(void* p, uint4 v) {
 }
 
 constexpr uint4 kZero16 = {0u, 0u, 0u, 0u};
+
+// 4 floats as 4 bfloat16 (round to nearest even), packed in 8 bytes.
+__device__ __forceinline__ uint2 pack4_bf16(const f32x4& v) {
+    const bf16 b[4] = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+    return *reinterpret_cast<const uint2*>(b);
+}
+
+// The tiled path keeps the gate-scaled expert outputs g * y in HBM as
+// IEEE half precision scaled by 2^-8: 11 significant bits (a rounding error
+// of at most 2^-12 relative, 8x below bfloat16's) in the same two bytes.
+// The scale moves half precision's range to [2^-6, 1.7e7] for normal values
+// (below it the absolute error is at most 2^-17 / 2); larger magnitudes
+// saturate at 65504 * 2^8 instead of becoming infinite.  NaN stays NaN.
+constexpr float kYScale = 0x1p-8f, kYUnscale = 0x1p8f;
+__device__ __forceinline__ uint2 pack4_f16_sat(f32x4 v) {
+    f16 h[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float c = fabsf(v[i]) > 65504.0f ? copysignf(65504.0f, v[i]) : v[i];
+        h[i] = (f16)c;
+    }
+    return *reinterpret_cast<const uint2*>(h);
+}
 
 __host__ __device__ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
 

@@ -117,6 +117,12 @@ template <class R>
 struct NtStores<R, std::void_t<decltype(R::kNtStores)>> : std::integral_constant<bool, R::kNtStores> {};
 // RowCtx<P>::kColScale (a float per output column, applied first), false
 // where a problem does not define it
+// RowCtx<P>::kHalfOut: the 2-byte tile holds scaled half precision
+// (pack4_f16_sat) instead of bfloat16
+template <class R, class = void>
+struct HalfOut : std::false_type {};
+template <class R>
+struct HalfOut<R, std::void_t<decltype(R::kHalfOut)>> : std::integral_constant<bool, R::kHalfOut> {};
 template <class R, class = void>
 struct ColScale : std::false_type {};
 template <class R>
@@ -187,19 +193,20 @@ struct RowCtx<Ffn1<bf16>> {
 };
 
 template <>
-struct RowCtx<Ffn2<bf16, bf16>> {
-    static constexpr bool kRowVal = true;   // the slot's gate
+struct RowCtx<Ffn2<bf16, f16>> {
+    static constexpr bool kRowVal = true;   // the slot's gate (times kYScale)
     static constexpr bool kBf16Tile = true;
+    static constexpr bool kHalfOut = true;  // the tile is stored as scaled half precision
     __device__ static f32x4 tile_op(f32x4 v, float g) { return v * g; }
-    __device__ static bf16* tile_row(const LayerArgs& a, int slot) { return static_cast<bf16*>(a.ybuf) + (size_t)slot * a.l; }
-    __device__ static float row_value(const LayerArgs& a, int, int slot) { return a.gates[a.perm[slot]]; }
+    __device__ static f16* tile_row(const LayerArgs& a, int slot) { return static_cast<f16*>(a.ybuf) + (size_t)slot * a.l; }
+    __device__ static float row_value(const LayerArgs& a, int, int slot) { return a.gates[a.perm[slot]] * kYScale; }
     using ColPre = NoPre;
     __device__ static NoPre col_load(const LayerArgs&, int, int) { return NoPre{}; }
     using Pre = NoPre;
     __device__ static NoPre load(const LayerArgs&, int, int, int) { return NoPre{}; }
     __device__ static void store(const LayerArgs& a, int, int slot, int c0, f32x4 v, const NoPre&, const NoPre&,
                                  float g) {
-        store_cols<bf16, true>(static_cast<bf16*>(a.ybuf) + (size_t)slot * a.l + c0, c0, a.l, v * g);
+        st_nt8(static_cast<f16*>(a.ybuf) + (size_t)slot * a.l + c0, pack4_f16_sat(v * g));   // l % 64 == 0
     }
 };
 
@@ -242,7 +249,7 @@ struct RowCtx<Ffn1Q> : RowCtx<Ffn1<bf16>> {
 };
 
 template <>
-struct RowCtx<Ffn2Q> : RowCtx<Ffn2<bf16, bf16>> {
+struct RowCtx<Ffn2Q> : RowCtx<Ffn2<bf16, f16>> {
     static constexpr bool kColScale = true;
     __device__ static float col_scale(const LayerArgs& a, int e, int c) { return Ffn2Q::row_scale(a, e, c); }
 };
@@ -252,7 +259,7 @@ struct RowCtx<Ffn2Q> : RowCtx<Ffn2<bf16, bf16>> {
 template <>
 struct RowCtx<Ffn1X> : RowCtx<Ffn1<bf16>> {};
 template <>
-struct RowCtx<Ffn2X> : RowCtx<Ffn2<bf16, bf16>> {};
+struct RowCtx<Ffn2X> : RowCtx<Ffn2<bf16, f16>> {};
 
 template <>
 struct RowCtx<Shared2<bf16>> {
@@ -598,8 +605,8 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm2_kernel(LayerArgs a, int 
                             v[3] += __uint_as_float(u.y & 0xffff0000u);
                         }
                         v = RowCtx<P>::tile_op(v, g);
-                        const bf16 b[4] = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
-                        tg[rl * (BN / 4) + (q ^ x)] = *reinterpret_cast<const uint2*>(b);
+                        tg[rl * (BN / 4) + (q ^ x)] =
+                            HalfOut<RowCtx<P>>::value ? pack4_f16_sat(v) : pack4_bf16(v);
                     }
             }
             __syncthreads();

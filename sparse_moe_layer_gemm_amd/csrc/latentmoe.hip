@@ -701,7 +701,7 @@ static int forward_impl(const void* x, const void* W_down, const void* W_router,
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     const hipError_t launch_err =
-        p.bf16 ? launch_all<bf16, bf16>(p, a, st, events) : launch_all<float, float>(p, a, st, events);
+        p.bf16 ? launch_all<bf16, f16>(p, a, st, events) : launch_all<float, float>(p, a, st, events);
     const hipError_t last_err = hipGetLastError();
     const hipError_t err = launch_err != hipSuccess ? launch_err : last_err;
     if (err != hipSuccess) return fail(LMOE_EHIP, "HIP launch failed: %s", hipGetErrorString(err));

@@ -143,7 +143,9 @@ struct Ffn1 {
 };
 
 // Expert FFN, second product: y = W2[e] a, scaled by the slot's gate
-// (so the combine only sums).  YT: storage type of the expert outputs.
+// (so the combine only sums).  YT: storage type of the expert outputs
+// (float for the float32 layer; f16 scaled by kYScale for the bf16 layer's
+// tiled path, whose epilogue is RowCtx<Ffn2<bf16, f16>> in gemm2.h).
 template <class E, class YT>
 struct Ffn2 {
     using BElem = E;
@@ -274,7 +276,7 @@ struct Ffn1Q : Ffn1<bf16> {
     __device__ static float row_scale(const LayerArgs& a, int e, int c) { return a.w1s[(size_t)e * a.m + c]; }
 };
 
-struct Ffn2Q : Ffn2<bf16, bf16> {
+struct Ffn2Q : Ffn2<bf16, f16> {
     using BElem = uint8_t;
     __device__ static const uint8_t* b_row(const LayerArgs& a, int e, int c) {
         return static_cast<const uint8_t*>(a.W2) + ((size_t)e * a.l + c) * a.m;
@@ -297,7 +299,7 @@ struct Ffn1X : Ffn1<bf16> {
     __device__ static const uint8_t* x_scales(const LayerArgs& a, int e) { return a.w1x + (size_t)e * a.m * (a.l / 32); }
 };
 
-struct Ffn2X : Ffn2<bf16, bf16> {
+struct Ffn2X : Ffn2<bf16, f16> {
     using BElem = MxFp4;
     __device__ static const uint8_t* x_codes(const LayerArgs& a, int e) {
         return static_cast<const uint8_t*>(a.W2) + (size_t)e * a.l * (a.m / 2);

@@ -7,16 +7,20 @@ Comparison rules:
     there either selection is correct, so the oracle re-evaluates those
     tokens with the GPU's ids (gates still from its own fp64 logits);
   * gates: per (token, id), |gpu - oracle| <= 1e-5 (fp32 softmax);
-  * out: max |gpu - oracle| <= 1e-4 for float32 workloads; for the named
-    bf16 workloads max |gpu - oracle| <= 2e-2 * RMS(oracle out), the stated
-    bar.  Other bf16 shapes (edge cases with few experts per token, where the
-    MoE part is large next to x) use a per-element bar derived from the
-    arithmetic: half a bf16 ulp of the output (its final rounding) plus
-    n * 1e-2 * RMS(oracle MoE part), the MoE part being out - x and n the
-    number of intermediate bf16 roundings on the path taken, each of relative
-    size 2^-9 at up to ~5 RMS per element: 3 on the streaming path (z,
-    relu(h)^2, s) and 4 on the tiled path, which also stores the gate-scaled
-    expert outputs in bf16; one more with a shared expert (its relu(h)^2).  (A numpy emulation of these rounding points
+  * out: max |gpu - oracle| <= 1e-4 for float32 workloads; for bf16 max
+    |gpu - oracle| <= 2e-2 * RMS(oracle out), the stated bar, on every case
+    except the ones a test names as bar="derived": edge shapes whose MoE part
+    is large next to x (DERIVED_BAR: identity projections, all tokens on
+    two experts, MXFP4 codes at large scales ...), where the bf16 roundings
+    of the MFMA operands (z, relu(h)^2, s) and of the output reach the
+    stated figure.  Those use a per-element bar derived from the arithmetic: half a
+    bf16 ulp of the output (its final rounding) plus n * 1e-2 * RMS(oracle
+    MoE part), the MoE part being out - x and n the number of intermediate
+    bf16 roundings on the path taken, each of relative size 2^-9 at up to ~5
+    RMS per element: 3 on the streaming path (z, relu(h)^2, s) and 3 1/8 on
+    the tiled path, which also stores the gate-scaled expert outputs in half
+    precision (relative 2^-12); one more with a shared expert (its
+    relu(h)^2); the stated figure is still reported for them.  (A numpy emulation of these rounding points
     reproduces the GPU's worst elements exactly.);
   * dispatch arrays: bit-exact against a stable counting sort of the GPU's
     own ids (computed here with numpy).
@@ -36,6 +40,32 @@ from sparse_moe_layer_gemm_amd.inputs import Workload, as_numpy_bits, make_input
 TIE_BAND = 1e-3
 FP32_TOL = 1e-4
 BF16_REL_TOL = 2e-2
+
+# The bf16 comparisons (by tag) held to the derived bar instead of the
+# stated one, with the stated fraction each measured on an MI355X: edge
+# shapes whose MoE part is large next to x (one or two experts per token,
+# identity projections, every byte of MXFP4 codes at large block scales,
+# few experts on many rows), where the bf16 rounding of the output (up to
+# 0.0156 for |out| in [4, 8)) plus those of the MFMA operands z, relu(h)^2
+# and s pass 2e-2 * RMS(out).  Every other bf16 comparison asserts the
+# stated bar.
+DERIVED_BAR = {
+    "mxfp4_l256_every_byte/path1": 1.307,
+    "mxfp4_l256_every_byte/path2": 1.267,
+    "shared_latent/path2": 1.184,
+    "shared_latent/path0": 1.184,
+    "rand7_1/path2": 1.122,
+    "rand7_1/path1": 1.122,
+    "rand7_1/path0": 1.122,
+    "biased/path1": 1.106,
+    "concentrated/path2": 1.079,
+    "concentrated/path1": 1.079,
+    "fp8_large_tiles/path2": 1.067,
+    "fp8_large_tiles/path0": 1.067,
+    "identity/latent/bf16/path2": 1.065,
+    "mxfp4_l128_every_byte/path2": 1.031,
+    "mxfp4_l128_every_byte/path1": 1.031,
+}
 
 
 def log(msg: str) -> None:
@@ -82,22 +112,52 @@ def read_dispatch(ws: torch.Tensor, dims, K: int, T: int, N: int):
             int(arr(lay.n_active, 1)[0]))
 
 
-def compare(w: Workload, inp, K: int, path: int = B.LMOE_PATH_AUTO, sample: Optional[Sequence[int]] = None,
-            check_dispatch: bool = True, tag: str = "") -> dict:
-    """Run GPU and oracle on `inp` (CPU tensors) and assert parity."""
-    T, N = w.T, w.N + w.n_zc   # N: routed ids
-    zc = dict(n_zero=w.n_zero, n_copy=w.n_copy)
-    log(f"[parity] {tag or w.name}: T={T} d={w.d} l={w.l} N={w.N}+{w.n_zc} K={K} m={w.m} {w.dtype} path={path}")
-    dinp = to_device(inp)
-    dims = B.dims_for(dinp, K, path, **zc)
-    out, ids, gates, ws = B.forward(dinp, K, path=path, routing=True, **zc)
-    torch.cuda.synchronize()
-    out_g = out.float().cpu().numpy().astype(np.float64)
-    ids_g = ids.cpu().numpy()
-    gates_g = gates.cpu().numpy().astype(np.float64)
-    arr = oracle_arrays(inp)
-    sel = np.arange(T, dtype=np.int32) if sample is None else np.asarray(sample, np.int32)
-    ref = run_oracle(arr, K, sel=sel, **zc)
+class GpuRun:
+    """One forward of the HIP path through the C ABI, copied to the host."""
+
+    def __init__(self, w: Workload, inp, K: int, path: int = B.LMOE_PATH_AUTO, tag: str = ""):
+        self.w, self.K, self.path = w, K, path
+        self.T, self.N = w.T, w.N + w.n_zc   # N: routed ids
+        self.zc = dict(n_zero=w.n_zero, n_copy=w.n_copy)
+        self.tag = tag or w.name
+        log(f"[parity] {self.tag}: T={w.T} d={w.d} l={w.l} N={w.N}+{w.n_zc} K={K} m={w.m} {w.dtype} path={path}")
+        dinp = to_device(inp)
+        self.dims = B.dims_for(dinp, K, path, **self.zc)
+        self.resolved = B.latentmoe_resolved_path(self.dims, K)
+        out, ids, gates, ws = B.forward(dinp, K, path=path, routing=True, **self.zc)
+        torch.cuda.synchronize()
+        self.out_t = out
+        self.out = out.float().cpu().numpy().astype(np.float64)
+        self.ids = ids.cpu().numpy()
+        self.gates = gates.cpu().numpy().astype(np.float64)
+        self.dispatch = read_dispatch(ws, self.dims, K, self.T, self.N)
+        del ws, dinp
+
+    def check_dispatch(self) -> None:
+        counts, offsets, perm, slot_of, n_active = self.dispatch
+        ec, eo, ep, es = expected_dispatch(self.ids, self.N)
+        assert np.array_equal(counts, ec), "counts"
+        assert np.array_equal(offsets, eo), "offsets"
+        assert np.array_equal(perm, ep), "perm"
+        assert np.array_equal(slot_of, es), "slot_of"
+        assert n_active == int((ec[:self.w.N] > 0).sum())   # FFN experts only
+
+
+def check_tokens(g: GpuRun, inp, sel: np.ndarray, arr=None, bar: str = "stated", tag: str = "") -> dict:
+    """Compare the tokens `sel` of the GPU run g with the oracle.
+
+    bar: "stated" (bf16: max |gpu - oracle| <= 2e-2 * RMS(oracle out) over
+    the compared tokens; float32: <= 1e-4) or "derived" (bf16 shapes whose
+    MoE part is large next to x, the comparisons DERIVED_BAR names: half a
+    bf16 ulp of the output plus n * 1e-2 * RMS(MoE part) per element, n =
+    the path's bf16 roundings; the stated figure is still reported)."""
+    w, K, T = g.w, g.K, g.T
+    if bar == "stated" and g.tag in DERIVED_BAR:
+        bar = "derived"
+    arr = oracle_arrays(inp) if arr is None else arr
+    sel = np.asarray(sel, np.int32)
+    ref = run_oracle(arr, K, sel=sel, **g.zc)
+    ids_g, gates_g, out_g = g.ids, g.gates, g.out
 
     # ids: sets equal outside the tie band
     near = ref["gap"] < TIE_BAND
@@ -112,7 +172,7 @@ def compare(w: Workload, inp, K: int, path: int = B.LMOE_PATH_AUTO, sample: Opti
     ref_gates = {}
     if mism:
         mq = np.asarray(mism)
-        fr = run_oracle(arr, K, sel=sel[mq], forced=ids_g[sel[mq]], **zc)
+        fr = run_oracle(arr, K, sel=sel[mq], forced=ids_g[sel[mq]], **g.zc)
         ref_out[mq] = fr["out"]
         for i, q in enumerate(mq):
             ref_gates[q] = dict(zip(fr["ids"][i].tolist(), fr["gates"][i].tolist()))
@@ -128,46 +188,47 @@ def compare(w: Workload, inp, K: int, path: int = B.LMOE_PATH_AUTO, sample: Opti
     err = np.abs(out_g[sel] - ref_out)
     maxerr = float(err.max())
     rms = float(np.sqrt(np.mean(ref_out ** 2)))
+    stated = float(maxerr / (BF16_REL_TOL * rms)) if w.dtype != "f32" else maxerr / FP32_TOL
     if w.dtype == "f32":
         tol = np.full_like(err, FP32_TOL)
         rule = "abs 1e-4"
-    elif is_named(w):
+    elif bar == "stated":
         tol = np.full_like(err, BF16_REL_TOL * rms)
         rule = "2e-2*rms"
-    else:
+    elif bar == "derived":
         moe = ref_out - x64(inp["x"])[sel]
         moe_rms = float(np.sqrt(np.mean(moe ** 2)))
-        n_round = 3 if B.latentmoe_resolved_path(dims, K) == B.LMOE_PATH_STREAM else 4
+        # z, relu(h)^2 and s in bf16; on the tiled path also the gate-scaled
+        # expert outputs in half precision (2^-12: an eighth of a bf16 rounding)
+        n_round = 3 if g.resolved == B.LMOE_PATH_STREAM else 3.125
         n_round += 1 if inp.get("W_s1") is not None else 0   # the shared expert's relu(h)^2
         tol = half_ulp_bf16(np.maximum(np.abs(ref_out), np.abs(out_g[sel]))) + n_round * 1e-2 * moe_rms
         rule = f"ulp/2 + {n_round}e-2*rms(moe)"
+    else:
+        raise ValueError(f"bar {bar!r}")
     frac = float((err / tol).max())
-    rep = dict(maxerr=maxerr, rms=rms, rule=rule, frac_of_tol=frac, tie_tokens=int(near.sum()),
-               id_mismatch=len(mism), rank_order_equal=rank_equal, gate_err=gerr, n_checked=len(sel))
-    log(f"[parity] {tag or w.name}: {rep}")
+    rep = dict(maxerr=maxerr, rms=rms, rule=rule, frac_of_tol=frac, stated_frac=stated,
+               tie_tokens=int(near.sum()), id_mismatch=len(mism), rank_order_equal=rank_equal, gate_err=gerr,
+               n_checked=len(sel))
+    log(f"[parity] {tag or g.tag}: {rep}")
     bad = np.unravel_index(int(np.argmax(err / tol)), err.shape)
     assert frac <= 1.0, (f"error {err[bad]} > tol {tol[bad]} at token {sel[bad[0]]} col {bad[1]} "
                          f"(ref {ref_out[bad]}, gpu {out_g[sel][bad]}, rule {rule})")
-
-    if check_dispatch:
-        counts, offsets, perm, slot_of, n_active = read_dispatch(ws, dims, K, T, N)
-        ec, eo, ep, es = expected_dispatch(ids_g, N)
-        assert np.array_equal(counts, ec), "counts"
-        assert np.array_equal(offsets, eo), "offsets"
-        assert np.array_equal(perm, ep), "perm"
-        assert np.array_equal(slot_of, es), "slot_of"
-        assert n_active == int((ec[:w.N] > 0).sum())   # FFN experts only
-    rep["out"] = out
-    rep["ids"] = ids_g
     return rep
 
 
-def is_named(w: Workload) -> bool:
-    """True for the named workloads at their stated shapes."""
-    from sparse_moe_layer_gemm_amd.inputs import WORKLOADS
-
-    ref = WORKLOADS.get(w.name)
-    return ref is not None and ref == w
+def compare(w: Workload, inp, K: int, path: int = B.LMOE_PATH_AUTO, sample: Optional[Sequence[int]] = None,
+            check_dispatch: bool = True, tag: str = "", bar: str = "stated") -> dict:
+    """Run GPU and oracle on `inp` (CPU tensors) and assert parity (all
+    tokens, or the tokens in `sample`)."""
+    g = GpuRun(w, inp, K, path, tag)
+    sel = np.arange(w.T, dtype=np.int32) if sample is None else np.asarray(sample, np.int32)
+    rep = check_tokens(g, inp, sel, bar=bar)
+    if check_dispatch:
+        g.check_dispatch()
+    rep["out"] = g.out_t
+    rep["ids"] = g.ids
+    return rep
 
 
 def half_ulp_bf16(v: np.ndarray) -> np.ndarray:
