@@ -45,10 +45,16 @@ def parse():
     ap.add_argument("--weight-sets", type=int, default=2)
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget; 0 skips it")
     ap.add_argument("--no-events", action="store_true", help="time without stage events")
+    ap.add_argument("--extra", default=None,
+                    help="comma-separated workloads also measured in the same run and reported under "
+                         "extra_workloads (default: prefill,skewed with the decode workload, none otherwise)")
     ap.add_argument("--sweep", default="",
                     help="comma-separated token counts: one JSON line per count, the workload's shape with "
                          "T tokens (x = the first T rows of one draw), no CPU baseline")
-    return ap.parse_args()
+    a = ap.parse_args()
+    if a.extra is None:
+        a.extra = "prefill,skewed" if a.config == "decode" and not a.sweep else ""
+    return a
 
 
 class Hip:
@@ -123,9 +129,9 @@ def main():
     torch.cuda.set_device(dev)
     B.lib()
 
-    def draw_sets(wk):
+    def draw_sets(wk, n=None):
         sets = []
-        for s in range(max(1, args.weight_sets)):
+        for s in range(max(1, args.weight_sets if n is None else n)):
             inp = make_inputs(wk, seed=s)
             sets.append((inp, {k: (None if v is None else v.to(dev)) for k, v in inp.items()}))
         return sets
@@ -138,18 +144,40 @@ def main():
             sets = [({**c, "x": c["x"][:T]}, {**g, "x": g["x"][:T].contiguous()}) for c, g in base]
             print(json.dumps(measure(wt, sets, 0.0)), flush=True)
         return
-    print(json.dumps(measure(w, draw_sets(w), args.cpu_seconds)), flush=True)
+    line = measure(w, draw_sets(w), args.cpu_seconds)
+    # The MFMA-bound workloads, measured in the same run (shorter: one weight
+    # set, no oracle, no yardsticks), so that one JSON line carries their step
+    # time, tokens/s and roofline fractions too.
+    extra = [e.strip() for e in args.extra.split(",") if e.strip()]
+    if extra:
+        line["extra_workloads"] = {}
+    for name in extra:
+        we = WORKLOADS[name]
+        rec = measure(we, draw_sets(we, 1), 0.0, steps=min(args.steps, 10), warmup=min(args.warmup, 3),
+                      references=False)
+        line["extra_workloads"][name] = {
+            "tokens_per_s": rec["value"], "ms_per_step": rec["ms_per_step"], "steps": rec["steps"],
+            "ffn_path": rec["config"]["ffn_path"],
+            "roofline": {k: rec["roofline"][k] for k in ("kernel", "bound", "achieved", "peak", "unit", "frac",
+                                                          "kernel_us", "traffic", "layer_frac")},
+            "stage_us": rec["layer"]["stage_us"], "active_experts": rec["layer"]["active_experts"]}
+        torch.cuda.empty_cache()
+    print(json.dumps(line), flush=True)
 
 
-def measure(w, sets, cpu_seconds: float) -> dict:
+def measure(w, sets, cpu_seconds: float, steps=None, warmup=None, references: bool = True) -> dict:
     """One JSON record: w's forward timed over `sets` (CPU and device copies
-    of the inputs, alternating between steps)."""
+    of the inputs, alternating between steps); `steps` / `warmup` default to
+    the command line's.  references: also time the in-run HBM and MFMA
+    yardsticks (device copy, streaming read, library GEMM)."""
     import numpy as np
     import torch
 
     from sparse_moe_layer_gemm_amd import binding as B
 
     args = ARGS
+    steps = args.steps if steps is None else steps
+    warmup = args.warmup if warmup is None else warmup
     dev = torch.device("cuda:0")
     dims = B.dims_for(sets[0][1], w.K, args.path, w.n_zero, w.n_copy)
     path = B.latentmoe_resolved_path(dims, w.K)
@@ -178,7 +206,7 @@ def measure(w, sets, cpu_seconds: float) -> dict:
     A = float(np.mean(active))
     R = float(np.mean(rows))
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     # Timed region: the whole forward, with HIP events recorded on the launch
     # stream only around the expert FFN (the dominant kernel).
@@ -188,17 +216,17 @@ def measure(w, sets, cpu_seconds: float) -> dict:
     ev_ffn = None
     if not args.no_events:
         ev_ffn = []
-        for _ in range(args.steps):
+        for _ in range(steps):
             arr = (ctypes.c_void_p * nst)()
             arr[3], arr[ffn_end] = hip.event(), hip.event()
             ev_ffn.append(arr)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step(i, ev_ffn[i] if ev_ffn else None)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms = (t1 - t0) * 1e3 / args.steps
+    ms = (t1 - t0) * 1e3 / steps
     tok_s = w.T / (ms * 1e-3)
     ffn_us = float("nan")
     if ev_ffn:
@@ -207,14 +235,15 @@ def measure(w, sets, cpu_seconds: float) -> dict:
     # Stage breakdown (a separate pass with an event at every stage boundary).
     stages = {}
     if not args.no_events:
-        ev_all = [(ctypes.c_void_p * nst)(*[hip.event() for _ in range(nst)]) for _ in range(args.steps)]
-        for i in range(args.steps):
+        ev_all = [(ctypes.c_void_p * nst)(*[hip.event() for _ in range(nst)]) for _ in range(steps)]
+        for i in range(steps):
             step(i, ev_all[i])
         torch.cuda.synchronize()
         for si, name in enumerate(B.STAGES):
             stages[name] = float(np.mean([hip.elapsed_ms(ev[si], ev[si + 1]) for ev in ev_all])) * 1e3
-    copy_gbs = copy_bandwidth(torch, dev)
-    mm_tflops = matmul_rate(torch, dev) if w.dtype == "bf16" else None
+    copy_gbs = copy_bandwidth(torch, dev) if references else None
+    read_gbs = read_bandwidth(torch, dev) if references else None
+    mm_tflops = matmul_rate(torch, dev) if references and w.dtype == "bf16" else None
     lay_bytes, lay_flops = algorithmic(w, A, R)
 
     # dominant kernel: the expert FFN
@@ -249,9 +278,11 @@ def measure(w, sets, cpu_seconds: float) -> dict:
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["kernel_us"] = ffn_us
     roof["copy_GBps_measured"] = copy_gbs
+    roof["read_GBps_measured"] = read_gbs
     roof["matmul_TFLOPs_measured"] = mm_tflops
     flop_peak = FP32_VECTOR_PEAK_TFLOPS if w.dtype == "f32" else MFMA_BF16_PEAK_TFLOPS
     layer_frac = max(lay_bytes / (HBM_PEAK_GBS * 1e9), lay_flops / (flop_peak * 1e12)) / (ms * 1e-3)
+    roof["layer_frac"] = layer_frac
 
     cpu = None
     if cpu_seconds > 0:
@@ -262,8 +293,8 @@ def measure(w, sets, cpu_seconds: float) -> dict:
         "value": tok_s,
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": ms,
         "higher_is_better": True,
         "scaling": "weak",
@@ -335,6 +366,22 @@ def copy_bandwidth(torch, dev, nbytes: int = 1 << 30, reps: int = 10) -> float:
     torch.cuda.synchronize()
     gbs = 2 * nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9
     del src, dst
+    return gbs
+
+
+def read_bandwidth(torch, dev, nbytes: int = 1 << 30, reps: int = 10) -> float:
+    """In-run HBM reference: a streaming read of 1 GiB (a float32 sum of a
+    bf16 tensor: every byte read once, 4 bytes written), bytes read / s."""
+    src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
+    acc = src.sum(dtype=torch.float32)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        acc = src.sum(dtype=torch.float32)
+    b.record()
+    torch.cuda.synchronize()
+    gbs = nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, acc
     return gbs
 
 
