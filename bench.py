@@ -370,19 +370,34 @@ def copy_bandwidth(torch, dev, nbytes: int = 1 << 30, reps: int = 10) -> float:
 
 
 def read_bandwidth(torch, dev, nbytes: int = 1 << 30, reps: int = 10) -> float:
-    """In-run HBM reference: a streaming read of 1 GiB (a float32 sum of a
-    bf16 tensor: every byte read once, 4 bytes written), bytes read / s."""
-    src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
-    acc = src.sum(dtype=torch.float32)
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(reps):
-        acc = src.sum(dtype=torch.float32)
-    b.record()
-    torch.cuda.synchronize()
-    gbs = nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9
-    del src, acc
-    return gbs
+    """In-run HBM reference: the streaming-read kernel of libhbmread.so over
+    1 GiB (every byte read once, each workgroup a contiguous share with eight
+    16-byte loads in flight per thread, nothing written), the best of a few
+    grid sizes, bytes read / s."""
+    from sparse_moe_layer_gemm_amd import build as hipbuild
+
+    lib = ctypes.CDLL(hipbuild.PROBE_LIB)
+    lib.hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    best = 0.0
+    for per_cu in (2, 4, 8):
+        def run():
+            rc = lib.hbm_read(src.data_ptr(), nbytes, sink.data_ptr(), cus * per_cu, stream)
+            if rc != 0:
+                raise RuntimeError(f"hbm_read failed: {rc}")
+        run()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            run()
+        b.record()
+        torch.cuda.synchronize()
+        best = max(best, nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9)
+    del src, sink
+    return best
 
 
 def cpu_baseline(w, inp, budget_s: float):

@@ -1,4 +1,5 @@
-"""Build the HIP library liblatentmoe.so (gfx950) in-tree with hipcc."""
+"""Build the HIP library liblatentmoe.so (gfx950) in-tree with hipcc, and the
+benchmark's HBM read yardstick libhbmread.so."""
 from __future__ import annotations
 
 import os
@@ -31,15 +32,25 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
-    cmd = [hipcc(), *HIPCC_FLAGS, SRC, "-o", LIB + ".tmp"]
+# the benchmark's HBM streaming-read yardstick (not part of the layer)
+PROBE_SRC = os.path.join(PKG, "csrc", "hbm_read.hip")
+PROBE_LIB = os.path.join(PKG, "libhbmread.so")
+
+
+def _hipcc(src: str, lib: str, verbose: bool) -> None:
+    cmd = [hipcc(), *HIPCC_FLAGS, src, "-o", lib + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building liblatentmoe.so")
-    os.replace(LIB + ".tmp", LIB)
+        raise RuntimeError(f"hipcc failed building {os.path.basename(lib)}")
+    os.replace(lib + ".tmp", lib)
+
+
+def build(verbose: bool = False) -> str:
+    _hipcc(SRC, LIB, verbose)
+    _hipcc(PROBE_SRC, PROBE_LIB, verbose)
     return LIB
 
 
