@@ -280,8 +280,18 @@ struct RowCtx<Shared2<bf16>> {
 template <>
 struct RowCtx<UpCat<bf16>> : RowCtx<Up<bf16>> {};
 
+// Problems that map a logical tile index themselves (Tail<P>):
+// item(a, logical, grp, row0, row_end, col0).
+template <class P, class = void>
+struct HasItem : std::false_type {};
+template <class P>
+struct HasItem<P, decltype((void)P::item(std::declval<const LayerArgs&>(), 0, std::declval<int&>(),
+                                          std::declval<int&>(), std::declval<int&>(), std::declval<int&>()))>
+    : std::true_type {};
+
 template <class P, int BM, int BN, int NWM, int NWN>
-__global__ __launch_bounds__(64 * NWM * NWN) void gemm2_kernel(LayerArgs a, int nrow_tiles, int ncol_tiles) {
+__global__ __launch_bounds__(64 * NWM * NWN) void gemm2_kernel(LayerArgs a, int nrow_tiles, int ncol_tiles,
+                                                                int g_limit) {
     using S = G2Shape<BM, BN, NWM, NWN>;
     // Persistent workgroups.  Logical tiles (row-tile-major) are split into
     // 8 contiguous ranges, one per XCD (workgroup b runs on XCD b % 8); the
@@ -290,7 +300,9 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm2_kernel(LayerArgs a, int 
     // of one expert against all its weight columns) and share that XCD's
     // L2.  The actual tile count is read on the device for the FFN (the
     // host only knows a bound).
-    const int G = P::row_tiles(a, nrow_tiles) * ncol_tiles;
+    // logical tiles: the problem's row tiles x column tiles, the first g_limit
+    // of them (the rest, if any, run as a split-reduction tail)
+    const int G = min(P::row_tiles(a, nrow_tiles) * ncol_tiles, g_limit);
     const int per_xcd = (G + kXcds - 1) / kXcds;
     const int xcd = blockIdx.x % kXcds, nslot = gridDim.x / kXcds;
     const int ncols = P::ncols(a);
@@ -302,9 +314,13 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm2_kernel(LayerArgs a, int 
         if (slot >= per_xcd) return false;
         const int logical = xcd * per_xcd + slot;
         if (logical >= G) return false;
-        if (!P::tile(a, logical / ncol_tiles, BM, t.grp, t.row0, t.row_end)) return false;
-        t.col0 = (logical % ncol_tiles) * BN;
-        return t.col0 < ncols;
+        if constexpr (HasItem<P>::value) {
+            return P::item(a, logical, t.grp, t.row0, t.row_end, t.col0);
+        } else {
+            if (!P::tile(a, logical / ncol_tiles, BM, t.grp, t.row0, t.row_end)) return false;
+            t.col0 = (logical % ncol_tiles) * BN;
+            return t.col0 < ncols;
+        }
     };
 
     // Two LDS stages, each [A rows | B rows] contiguous; after a tile's last
@@ -717,6 +733,77 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm2_kernel(LayerArgs a, int 
             tile_loads();
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// Split-reduction tail.  A persistent launch of G tiles on R resident
+// workgroups runs ceil(G / R) rounds; when the last round is partly empty
+// (the projection at prefill: 384 tiles on 256 CUs), its r = G mod R tiles
+// instead run as s = R / r (>= 2) workgroups each, workgroup p reducing k-range
+// p of s into an fp32 partial tile (Tail<P>, a launch of its own after the
+// full rounds), and tail_fixup_kernel adds the s partials in order and
+// applies P's epilogue: ceil(G / R) rounds become floor(G / R) + 1/s.
+// P: a problem with one row group (grp 0) and a one-segment reduction
+// (ProjRouter, Up).
+template <class P, int BM, int BN>
+struct Tail {
+    using BElem = typename P::BElem;
+    __device__ static int kpart(const LayerArgs& a) { return P::kdim(a) / a.tail_s; }
+    __device__ static bool item(const LayerArgs& a, int logical, int& grp, int& row0, int& row_end, int& col0) {
+        const int t = a.tail_base + logical / a.tail_s;
+        grp = logical % a.tail_s;   // the k-range
+        int g;
+        if (!P::tile(a, t / a.tail_ncol, BM, g, row0, row_end)) return false;
+        col0 = (t % a.tail_ncol) * BN;
+        return col0 < P::ncols(a);
+    }
+    __device__ static int row_tiles(const LayerArgs&, int host_count) { return host_count; }
+    __device__ static int ncols(const LayerArgs& a) { return P::ncols(a); }
+    __device__ static int kdim(const LayerArgs& a) { return kpart(a); }
+    __device__ static const bf16* a_row(const LayerArgs& a, int p, int r) {
+        return P::a_row(a, 0, r) + (size_t)p * kpart(a);
+    }
+    __device__ static const bf16* b_row(const LayerArgs& a, int p, int c) {
+        return P::b_row(a, 0, c) + (size_t)p * kpart(a);
+    }
+    // partial tile of (row, column): [tile - tail_base][p][row - row0][column - col0]
+    __device__ static float* part(const LayerArgs& a, int p, int r, int c) {
+        const int t = (r / BM) * a.tail_ncol + c / BN - a.tail_base;
+        return a.tail_part + (((size_t)t * a.tail_s + p) * BM + r % BM) * BN + c % BN;
+    }
+};
+
+template <class P, int BM, int BN>
+struct RowCtx<Tail<P, BM, BN>> {
+    static constexpr bool kRowVal = false;
+    __device__ static float row_value(const LayerArgs&, int, int) { return 0.0f; }
+    using ColPre = NoPre;
+    __device__ static NoPre col_load(const LayerArgs&, int, int) { return NoPre{}; }
+    using Pre = NoPre;
+    __device__ static NoPre load(const LayerArgs&, int, int, int) { return NoPre{}; }
+    __device__ static void store(const LayerArgs& a, int p, int r, int c0, f32x4 v, const NoPre&, const NoPre&,
+                                 float) {
+        *reinterpret_cast<f32x4*>(Tail<P, BM, BN>::part(a, p, r, c0)) = v;   // BN, c0 multiples of 4
+    }
+};
+
+// One thread per 4 consecutive columns of a row of a split tile: the s
+// partials added in k-range order, then P's epilogue (its fp32-path
+// RowCtx: per-element operand, per-column operand, store).
+template <class P, int BM, int BN>
+__global__ __launch_bounds__(256) void tail_fixup_kernel(LayerArgs a, int ntail) {
+    const int item = blockIdx.x * 256 + threadIdx.x;
+    const int per_tile = BM * (BN / 4);
+    if (item >= ntail * per_tile) return;
+    const int t = a.tail_base + item / per_tile;
+    const int r = (t / a.tail_ncol) * BM + (item % per_tile) / (BN / 4);
+    const int c = (t % a.tail_ncol) * BN + 4 * (item % (BN / 4));
+    if (r >= a.T || c >= P::ncols(a)) return;
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < a.tail_s; ++p) v += *reinterpret_cast<const f32x4*>(Tail<P, BM, BN>::part(a, p, r, c));
+    const typename RowCtx<P>::Pre pre = RowCtx<P>::load(a, 0, r, c);
+    const typename RowCtx<P>::ColPre cp = RowCtx<P>::col_load(a, 0, c);
+    RowCtx<P>::store(a, 0, r, c, v, pre, cp, 0.0f);
 }
 
 }  // namespace lmoe

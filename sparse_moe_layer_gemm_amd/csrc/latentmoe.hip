@@ -61,10 +61,7 @@ using G2Small = G2Cfg<128, 128, 2, 2, 2>;   // 4 waves, 64 KB LDS
 // (the tile list, shared by both FFN GEMMs, is cut at that height); with few
 // rows per expert the 256-row tile would be mostly padding.
 constexpr int kFfnLargeMinMeanRows = 512;
-// The tiled projection takes the large tile when it still makes at least one
-// tile per CU (many rows and columns: the latent layer's [z | logits] at
-// prefill), else the small one (the standard layer's few router columns).
-constexpr long long kProjLargeMinTiles = 256;
+constexpr long long kProjLargeMinTiles = 256;   // see proj_uses_large()
 using UpTile = G2Large;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -111,10 +108,19 @@ struct Plan {
     long long max_tiles = 0;
     size_t es = 2;
     size_t z, logits, ids, gates, counts, offsets, perm, slot_of, blk_counts, blk_offsets, tiles, n_tiles,
-        active, n_active, abuf, ybuf, s, part, a_s, y_s, total;
+        active, n_active, abuf, ybuf, s, part, a_s, y_s, tail, total;
 };
 
 bool mult64(int v) { return v > 0 && v % 64 == 0; }
+
+size_t tiled_tail_bytes(const lmoe_dims& d, const Plan& p);
+
+// The tiled projection takes the large tile when it still makes at least one
+// tile per CU (many rows and columns: the latent layer's [z | logits] at
+// prefill), else the small one (the standard layer's few router columns).
+bool proj_uses_large(int T, int ncols) {
+    return (long long)cdiv(T, G2Large::BM) * cdiv(ncols, G2Large::BN) >= kProjLargeMinTiles;
+}
 
 Plan make_plan(const lmoe_dims* dm, int32_t K) {
     Plan p;
@@ -241,6 +247,7 @@ Plan make_plan(const lmoe_dims* dm, int32_t K) {
     p.part = take(part_bytes);
     p.a_s = take((size_t)d.T * d.m_shared * p.es);
     p.y_s = take(d.m_shared > 0 ? (size_t)d.T * d.d * 4 : 0);
+    p.tail = take(tiled_tail_bytes(d, p));
     p.total = o;
     return p;
 }
@@ -277,15 +284,86 @@ int device_cus() {
     return n;
 }
 
+// Resident workgroups of a tiled-GEMM configuration (a multiple of 8).
+template <class C>
+long long g2_resident() {
+    return (long long)device_cus() * C::PER_CU / kXcds * kXcds;
+}
+
 // Persistent launch: one wave of resident workgroups (a multiple of 8, one
-// range of tiles per XCD), or fewer when there are fewer tiles.
+// range of tiles per XCD), or fewer when there are fewer tiles.  g_limit:
+// only the first g_limit logical tiles (the rest run as a tail).
 template <class P, class C>
-void launch_g2(const LayerArgs& a, int nrow_tiles, int ncol_tiles, hipStream_t st) {
-    const long long tiles = (long long)nrow_tiles * ncol_tiles;
-    const long long resident = (long long)device_cus() * C::PER_CU / kXcds * kXcds;
+void launch_g2(const LayerArgs& a, int nrow_tiles, int ncol_tiles, hipStream_t st, int g_limit = INT_MAX) {
+    const long long tiles = std::min<long long>((long long)nrow_tiles * ncol_tiles, g_limit);
+    const long long resident = g2_resident<C>();
     const long long g = std::max<long long>(kXcds, std::min<long long>((tiles + kXcds - 1) / kXcds * kXcds, resident));
     gemm2_kernel<P, C::BM, C::BN, C::NWM, C::NWN>
-        <<<(unsigned)g, dim3(64 * C::NWM * C::NWN), 0, st>>>(a, nrow_tiles, ncol_tiles);
+        <<<(unsigned)g, dim3(64 * C::NWM * C::NWN), 0, st>>>(a, nrow_tiles, ncol_tiles, g_limit);
+}
+
+// Split-reduction tail of a product of G tiles on R resident workgroups
+// (Tail<P> in gemm2.h): when the last round would hold r = G mod R tiles
+// with r <= R / 2, those tiles are split over s = min(4, R / r) k-ranges
+// (s dividing the k-steps).  s = 1: no tail.
+constexpr int kMaxTailSplit = 4;
+struct TailPlan {
+    long long base = 0;   // tiles before the tail
+    int s = 1, ntail = 0;
+};
+TailPlan tail_plan(long long G, long long R, int ksteps) {
+    TailPlan t;
+    const long long r = G % R;
+    if (G <= 0 || r == 0) return t;
+    int s = (int)std::min<long long>(kMaxTailSplit, R / r);
+    while (s > 1 && ksteps % s != 0) --s;
+    if (s < 2) return t;
+    t.base = G - r;
+    t.s = s;
+    t.ntail = (int)r;
+    return t;
+}
+template <class C>
+size_t tail_bytes(long long G, int ksteps) {
+    const TailPlan t = tail_plan(G, g2_resident<C>(), ksteps);
+    return t.s > 1 ? (size_t)t.ntail * t.s * C::BM * C::BN * 4 : 0;
+}
+
+// Bytes of the tail partials the bf16 tiled path's projection and
+// up-projection may need (the projection's columns depend on the mode, only
+// known at the call: the larger of the two).  No tail with a shared expert's
+// two-part up-projection.
+size_t tiled_tail_bytes(const lmoe_dims& d, const Plan& p) {
+    if (!p.bf16 || p.skinny) return 0;
+    size_t t = 0;
+    for (int lz : {d.l, 0}) {
+        const int nc = lz + d.m_shared + p.nr;
+        t = std::max(t, proj_uses_large(d.T, nc)
+                            ? tail_bytes<G2Large>((long long)cdiv(d.T, G2Large::BM) * cdiv(nc, G2Large::BN), d.d / 64)
+                            : tail_bytes<G2Small>((long long)cdiv(d.T, G2Small::BM) * cdiv(nc, G2Small::BN), d.d / 64));
+    }
+    if (d.m_shared == 0)
+        t = std::max(t, tail_bytes<UpTile>((long long)cdiv(d.T, UpTile::BM) * cdiv(d.d, UpTile::BN), d.l / 64));
+    return t;
+}
+
+// A tiled product with its split-reduction tail, if any: the full rounds,
+// then the tail's partial tiles, then the fixup that adds them and applies
+// P's epilogue.  The workspace's tail buffer holds the partials.
+template <class P, class C>
+void launch_g2_tail(LayerArgs a, int nrow_tiles, int ncol_tiles, int ksteps, hipStream_t st) {
+    const TailPlan t = tail_plan((long long)nrow_tiles * ncol_tiles, g2_resident<C>(), ksteps);
+    if (t.s < 2) {
+        launch_g2<P, C>(a, nrow_tiles, ncol_tiles, st);
+        return;
+    }
+    a.tail_base = (int)t.base;
+    a.tail_s = t.s;
+    a.tail_ncol = ncol_tiles;
+    if (t.base > 0) launch_g2<P, C>(a, nrow_tiles, ncol_tiles, st, (int)t.base);
+    launch_g2<Tail<P, C::BM, C::BN>, C>(a, t.s * t.ntail, 1, st);
+    const long long items = (long long)t.ntail * C::BM * (C::BN / 4);
+    tail_fixup_kernel<P, C::BM, C::BN><<<(unsigned)((items + 255) / 256), dim3(256), 0, st>>>(a, t.ntail);
 }
 
 // Rank groups per combine item: enough threads to fill the GPU.
@@ -321,10 +399,12 @@ hipError_t launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* 
                 <<<dim3(cdiv(ncols_pr, 16), split, cdiv(a.T, 64)), b256, 0, st>>>(a, part, split, stride);
             pin = PartIn{part, split, stride, a.standard ? 0 : a.l};
         } else {
-            if ((long long)cdiv(a.T, G2Large::BM) * cdiv(ncols_pr, G2Large::BN) >= kProjLargeMinTiles)
-                launch_g2<ProjRouter<bf16>, G2Large>(a, cdiv(a.T, G2Large::BM), cdiv(ncols_pr, G2Large::BN), st);
+            if (proj_uses_large(a.T, ncols_pr))
+                launch_g2_tail<ProjRouter<bf16>, G2Large>(a, cdiv(a.T, G2Large::BM), cdiv(ncols_pr, G2Large::BN),
+                                                          a.d / 64, st);
             else
-                launch_g2<ProjRouter<bf16>, G2Small>(a, cdiv(a.T, G2Small::BM), cdiv(ncols_pr, G2Small::BN), st);
+                launch_g2_tail<ProjRouter<bf16>, G2Small>(a, cdiv(a.T, G2Small::BM), cdiv(ncols_pr, G2Small::BN),
+                                                          a.d / 64, st);
         }
     } else {
         gemm_simt_kernel<ProjRouter<float>><<<dim3(cdiv(a.T, kSimtM), cdiv(ncols_pr, kSimtN)), b256, 0, st>>>(a);
@@ -467,7 +547,7 @@ hipError_t launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* 
             if (p.skinny)
                 skinny_kernel<Up<bf16>><<<dim3(cdiv(a.d, 16), cdiv(a.T, 64)), b1024, 0, st>>>(a);
             else
-                launch_g2<Up<bf16>, UpTile>(a, cdiv(a.T, UpTile::BM), cdiv(a.d, UpTile::BN), st);
+                launch_g2_tail<Up<bf16>, UpTile>(a, cdiv(a.T, UpTile::BM), cdiv(a.d, UpTile::BN), a.l / 64, st);
         } else {
             gemm_simt_kernel<Up<float>><<<dim3(cdiv(a.T, kSimtM), cdiv(a.d, kSimtN)), b256, 0, st>>>(a);
         }
@@ -694,6 +774,7 @@ static int forward_impl(const void* x, const void* W_down, const void* W_router,
     // y_s (the shared expert's float32 output) only where it is kept apart:
     // float32 layers and standard mode
     a.y_s = (d.m_shared > 0 && (!p.bf16 || standard)) ? reinterpret_cast<float*>(ws + p.y_s) : nullptr;
+    a.tail_part = reinterpret_cast<float*>(ws + p.tail);
     a.tile_rows = p.tile_rows;
     a.y_planes = p.nsplit;
     a.y_row_bytes = d.l * (p.path == LMOE_PATH_STREAM ? 4 : (int)p.es);

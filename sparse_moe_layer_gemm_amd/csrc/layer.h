@@ -57,6 +57,11 @@ struct LayerArgs {
     void* part;            // split-reduction partial tiles of the skinny projection
     void* a_s;             // [T, m_s] relu(W_s1 x)^2 (shared expert)
     float* y_s;            // [T, d] W_s2 a_s, float32 (shared expert)
+    // split-reduction tail of a tiled product (gemm2.h, Tail<P>): its last
+    // tiles, from tile tail_base on, each reduced by tail_s workgroups into
+    // fp32 partial tiles that tail_fixup_kernel adds and finishes
+    float* tail_part;      // [tiles][tail_s][BM][BN]
+    int tail_base, tail_s, tail_ncol;   // first split tile, split count, column tiles
     int tile_rows;         // rows per grouped-GEMM tile
     int y_planes;          // partial planes of ybuf (the streaming FFN's m-slices; 1 for the tiled FFN)
     int y_row_bytes;       // bytes of one ybuf row (l elements)
