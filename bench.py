@@ -194,15 +194,21 @@ def measure(w, sets, cpu_seconds: float, steps=None, warmup=None, references: bo
                             W_shared1=d.get("W_s1"), W_shared2=d.get("W_s2"),
                             W1_scale=d.get("W1_scale"), W2_scale=d.get("W2_scale"), zc_const=d.get("zc_const"))
 
-    # active FFN experts and FFN rows per weight set (for the algorithmic counts)
-    lay = B.latentmoe_workspace_layout(dims, w.K)
+    # active FFN experts and FFN rows per weight set (for the algorithmic
+    # counts), from the routed ids
     active, rows = [], []
+    ids_t = torch.empty(w.T, w.K, dtype=torch.int32, device=out.device)
     for i in range(len(sets)):
-        step(i)
+        d = sets[i][1]
+        B.latentmoe_forward(d["x"], d["W_down"], d["W_router"], d["W1"], d["W2"], d["W_up"], w.K, out, dims,
+                            router_bias=d["bias"], topk_ids=ids_t, workspace=ws, stream=stream,
+                            W_shared1=d.get("W_s1"), W_shared2=d.get("W_s2"),
+                            W1_scale=d.get("W1_scale"), W2_scale=d.get("W2_scale"), zc_const=d.get("zc_const"))
         torch.cuda.synchronize()
-        raw = ws.cpu().numpy()
-        active.append(int(raw[lay.n_active:lay.n_active + 4].view(np.int32)[0]))
-        rows.append(int(raw[lay.offsets + 4 * w.N:lay.offsets + 4 * w.N + 4].view(np.int32)[0]))
+        ffn_ids = ids_t.cpu().numpy().ravel()
+        ffn_ids = ffn_ids[ffn_ids < w.N]   # FFN experts (zero-computation ids come after)
+        active.append(int(np.unique(ffn_ids).size))
+        rows.append(int(ffn_ids.size))
     A = float(np.mean(active))
     R = float(np.mean(rows))
 

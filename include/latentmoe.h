@@ -257,7 +257,10 @@ int latentmoe_resolved_path(const lmoe_dims* dims, int32_t K);
 /*
  * Where the dispatch arrays live inside the workspace after a forward (byte
  * offsets from the workspace base), so that callers and tests can inspect the
- * token -> expert permutation:
+ * token -> expert permutation.  `written` is 1 when a forward with these dims
+ * writes them, 0 when it does not: the streaming path with T <= 256 has no
+ * dispatch (each expert's workgroups find its rows from the top-K ids), and
+ * the arrays then hold whatever was there before.  The arrays:
  *   counts   [Nr]     int32  rows routed to each id (Nr = N without
  *                            zero-computation experts)
  *   offsets  [Nr + 1] int32  exclusive prefix sum of counts
@@ -268,6 +271,7 @@ int latentmoe_resolved_path(const lmoe_dims* dims, int32_t K);
  */
 typedef struct {
     size_t counts, offsets, perm, slot_of, n_active;
+    size_t written;
 } lmoe_ws_layout;
 
 int latentmoe_workspace_layout(const lmoe_dims* dims, int32_t K, lmoe_ws_layout* layout);

@@ -51,7 +51,7 @@ class lmoe_args(ctypes.Structure):
 
 
 class lmoe_ws_layout(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_size_t) for n in ("counts", "offsets", "perm", "slot_of", "n_active")]
+    _fields_ = [(n, ctypes.c_size_t) for n in ("counts", "offsets", "perm", "slot_of", "n_active", "written")]
 
 
 class LatentMoEError(RuntimeError):

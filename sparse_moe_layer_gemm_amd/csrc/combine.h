@@ -9,13 +9,17 @@
 // (the streaming FFN's partials, the float32 layer) or f16, the tiled FFN's
 // gate-scaled outputs times kYScale (summed as they are, then scaled back
 // once: a power of two, so no extra rounding).
-// Zero-computation experts (ids >= n_ffn) have no expert output.  Their
-// slots are the last ones (ids sort after the FFN experts), so a rank is
-// theirs when its slot is at or past offsets[n_ffn]; such ranks read the
-// planes' zero row (the loads of all ranks stay unconditional), and a second
-// pass over just those ranks adds their own g * y: nothing for a zero expert,
-// g * z for a copy expert, g * its vector for a constant expert (MoE++'s
-// three kinds: 10100.com article, section 3.2).
+// A rank's expert output is at its slot (slot_of, after a dispatch), or at
+// row t*K + k of each plane when the streaming FFN routed itself
+// (self_route).  Zero-computation experts (ids >= n_ffn) have no expert
+// output.  After a dispatch their slots are the last ones (ids sort after
+// the FFN experts), so a rank is theirs when its slot is at or past
+// offsets[n_ffn], and such ranks read the planes' zero row; self-routed, a
+// rank is theirs by its id, and its row (never written) is read and then
+// discarded.  Either way the loads of all ranks stay unconditional, and a
+// second pass over just those ranks adds their own g * y: nothing for a zero
+// expert, g * z for a copy expert, g * its vector for a constant expert
+// (MoE++'s three kinds: 10100.com article, section 3.2).
 #pragma once
 
 #include <type_traits>
@@ -61,16 +65,26 @@ __global__ __launch_bounds__(256) void combine_kernel(LayerArgs a, int nsplit, i
     for (int i = 0; i < VPC; ++i) acc[i] = 0.0f;
     if (live) {
         const int* so = a.slot_of + (size_t)t * a.K;
+        const int* idk = a.ids + (size_t)t * a.K;
         const float* gt = a.gates + (size_t)t * a.K;
-        const int nf = a.N > a.n_ffn ? a.offsets[a.n_ffn] : INT_MAX;   // FFN slots: [0, nf)
+        const bool has_zc = a.N > a.n_ffn;
+        const int nf = has_zc && !a.self_route ? a.offsets[a.n_ffn] : INT_MAX;   // FFN slots: [0, nf)
         const size_t zrow = (size_t)a.T * a.K;
         unsigned long long zranks = 0;   // ranks of zero-computation experts (K <= 64)
 #pragma unroll 4
         for (int k = g; k < a.K; k += RS) {
-            const int sl = so[k];
-            const bool z = sl >= nf;
+            size_t row;
+            bool z;
+            if (a.self_route) {
+                row = (size_t)t * a.K + k;
+                z = has_zc && idk[k] >= a.n_ffn;
+            } else {
+                const int sl = so[k];
+                z = sl >= nf;
+                row = z ? zrow : (size_t)sl;
+            }
             zranks |= (unsigned long long)z << k;
-            const YT* yp = Y + (z ? zrow : (size_t)sl) * a.l;
+            const YT* yp = Y + row * a.l;
             uint4 raw = ldg16(yp);
             float part[VPC];
             if constexpr (VPC == 8) {
@@ -101,13 +115,12 @@ __global__ __launch_bounds__(256) void combine_kernel(LayerArgs a, int nsplit, i
             }
             const float gk = gated ? gt[k] : 1.0f;
 #pragma unroll
-            for (int i = 0; i < VPC; ++i) acc[i] = fmaf(gk, part[i], acc[i]);
+            for (int i = 0; i < VPC; ++i) acc[i] = fmaf(gk, z ? 0.0f : part[i], acc[i]);
         }
         if constexpr (std::is_same<YT, f16>::value) {
 #pragma unroll
             for (int i = 0; i < VPC; ++i) acc[i] *= kYUnscale;
         }
-        const int* idk = a.ids + (size_t)t * a.K;
         while (zranks) {
             const int k = __builtin_ctzll(zranks);
             zranks &= zranks - 1;

@@ -62,6 +62,10 @@ using G2Small = G2Cfg<128, 128, 2, 2, 2>;   // 4 waves, 64 KB LDS
 // rows per expert the 256-row tile would be mostly padding.
 constexpr int kFfnLargeMinMeanRows = 512;
 constexpr long long kProjLargeMinTiles = 256;   // see proj_uses_large()
+// the self-routed streaming FFN (T <= kSkinnyMaxRows): one mask bit per FFN
+// expert, the T*K ids in at most 32 KB of dynamic LDS
+static_assert(kSelfRouteMaskWords * 32 >= kMaxExperts, "self-route mask too small");
+static_assert((size_t)kSkinnyMaxRows * kMaxK * 2 <= 32768, "self-route ids exceed 32 KB of LDS");
 using UpTile = G2Large;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -395,8 +399,15 @@ hipError_t launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* 
     if constexpr (sizeof(E) == 2) {
         if (p.skinny) {
             const int split = proj_split(ncols_pr, a.T), stride = proj_stride(ncols_pr);
-            skinny_part_kernel<ProjRouter<bf16>>
-                <<<dim3(cdiv(ncols_pr, 16), split, cdiv(a.T, 64)), b256, 0, st>>>(a, part, split, stride);
+            const dim3 grid(cdiv(ncols_pr, 16), split, cdiv(a.T, 64));
+            if (a.T <= 16)
+                skinny_part_kernel<ProjRouter<bf16>, 1><<<dim3(grid.x, split, cdiv(a.T, 16)), b256, 0, st>>>(
+                    a, part, split, stride);
+            else if (a.T <= 32)
+                skinny_part_kernel<ProjRouter<bf16>, 2><<<dim3(grid.x, split, cdiv(a.T, 32)), b256, 0, st>>>(
+                    a, part, split, stride);
+            else
+                skinny_part_kernel<ProjRouter<bf16>, 4><<<grid, b256, 0, st>>>(a, part, split, stride);
             pin = PartIn{part, split, stride, a.standard ? 0 : a.l};
         } else {
             if (proj_uses_large(a.T, ncols_pr))
@@ -452,7 +463,9 @@ hipError_t launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* 
     // 3. dispatch
     mark(2);
     const size_t lds = dispatch_lds_bytes(a.N);
-    if (p.nblk == 1) {
+    if (a.self_route) {
+        // none: the streaming FFN finds its rows from the ids
+    } else if (p.nblk == 1) {
         dispatch_one_block_kernel<<<1, b1024, lds, st>>>(a);
     } else {
         dispatch_count_kernel<<<p.nblk, b1024, lds, st>>>(a);
@@ -473,14 +486,16 @@ hipError_t launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* 
             if (ev0 && ev1 && hipStreamIsCapturing(st, &cap) != hipSuccess) cap = hipStreamCaptureStatusActive;
             const bool own = ev0 && ev1 && cap == hipStreamCaptureStatusNone;
             if (!own) mark(3);
+            // (self-routed: the routed ids staged in dynamic LDS)
+            const size_t dyn = self_route_lds_bytes(a.T, a.K, a.self_route != 0);
             auto launch = [&](auto kernel, dim3 grid) {
                 if (own) {
                     void* args[] = {&a};
-                    const hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, b256, args, 0,
-                                                            st, ev0, ev1, 0);
+                    const hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, b256, args,
+                                                            dyn, st, ev0, ev1, 0);
                     if (e != hipSuccess) ext_err = e;
                 } else {
-                    kernel<<<grid, b256, 0, st>>>(a);
+                    kernel<<<grid, b256, dyn, st>>>(a);
                 }
             };
             // (MXFP4 pairs slices across the grid in chunks of 16 workgroups:
@@ -679,6 +694,7 @@ int latentmoe_workspace_layout(const lmoe_dims* dims, int32_t K, lmoe_ws_layout*
     layout->perm = p.perm;
     layout->slot_of = p.slot_of;
     layout->n_active = p.n_active;
+    layout->written = p.skinny ? 0 : 1;
     return LMOE_OK;
 }
 
@@ -778,6 +794,7 @@ static int forward_impl(const void* x, const void* W_down, const void* W_router,
     a.tile_rows = p.tile_rows;
     a.y_planes = p.nsplit;
     a.y_row_bytes = d.l * (p.path == LMOE_PATH_STREAM ? 4 : (int)p.es);
+    a.self_route = p.skinny ? 1 : 0;
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();

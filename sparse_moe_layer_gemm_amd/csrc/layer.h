@@ -65,11 +65,16 @@ struct LayerArgs {
     int tile_rows;         // rows per grouped-GEMM tile
     int y_planes;          // partial planes of ybuf (the streaming FFN's m-slices; 1 for the tiled FFN)
     int y_row_bytes;       // bytes of one ybuf row (l elements)
+    // The streaming FFN for T <= 256 finds each expert's rows from ids
+    // itself (no dispatch arrays): expert outputs are then stored at row
+    // t*K + k of each plane, which the combine reads directly.
+    int self_route;
 };
 
-// Elements of one ybuf plane: a row per slot and one more (row T*K), kept at
-// zero when there are zero-computation experts, whose ranks read it in place
-// of an expert output.
+// Elements of one ybuf plane: a row per slot (per pair t*K + k when
+// self_route) and one more (row T*K), kept at zero when there are
+// zero-computation experts and a dispatch, whose ranks read it in place of an
+// expert output.
 __device__ inline size_t y_plane_elems(const LayerArgs& a) { return ((size_t)a.T * a.K + 1) * a.l; }
 
 // ---------------------------------------------------------------------------

@@ -10,7 +10,7 @@
 //   skinny_kernel<P>: a product with T <= 256 rows.  One workgroup of 16
 //     waves owns 16 output columns of a group of 64 rows; the waves split the
 //     reduction and add their partial tiles through LDS.
-//   skinny_part_kernel<P>: the same, with the reduction also split over
+//   skinny_part_kernel<P, NRB>: the same, with the reduction also split over
 //     workgroups (fp32 partial tiles added by the consumer).
 //   ffn_stream_kernel<MS, F>: the expert FFN.  Workgroup (s, a) takes
 //     active expert a and the m-slice [s*MS, (s+1)*MS) (MS = 64, 128, or 256
@@ -125,16 +125,22 @@ __global__ __launch_bounds__(1024) void skinny_kernel(LayerArgs a) {
 
 // z and the router logits for T <= 256 rows, split over the reduction so
 // that enough workgroups stream the weights: workgroup (g, s, q) takes the
-// 16 columns of group g, k-range s of `nsplit` and rows 64q .. 64q+63; its 4 waves split that
-// range further and add their partial tiles through LDS, and the fp32
-// partial tile goes to part[s][T][stride].  The top-K kernel adds the
-// partials in split order (then the bias) and writes z.
-template <class P>
+// 16 columns of group g, k-range s of `nsplit` and the NRB * 16 rows from
+// q * NRB * 16 (NRB = 1, 2 or 4 row blocks, the fewest that hold min(T, 64)
+// rows: no registers or MFMAs for row blocks that cannot hold a row); its 4
+// waves split that range further and add their partial tiles through LDS,
+// and the fp32 partial tile goes to part[s][T][stride].  A wave issues the
+// loads of UB = 8 k-steps (4 with 4 row blocks) before their MFMAs, so the
+// usual decode split (7 k-steps per wave) takes one round trip to memory.
+// The top-K kernel adds the partials in split order (then the bias) and
+// writes z.
+template <class P, int NRB>
 __global__ __launch_bounds__(256) void skinny_part_kernel(LayerArgs a, float* part, int nsplit, int stride) {
-    const int c0 = blockIdx.x * 16, s = blockIdx.y, r0 = blockIdx.z * 64;
+    constexpr int UB = NRB <= 2 ? 8 : 4;
+    const int c0 = blockIdx.x * 16, s = blockIdx.y, r0 = blockIdx.z * (16 * NRB);
     const int ncols = P::ncols(a), K = P::kdim(a);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int nrb = min(4, cdiv(a.T - r0, 16));
+    const int nrb = min(NRB, cdiv(a.T - r0, 16));
     const int ksteps = K / 32;
     const int kc = cdiv(ksteps, nsplit);
     const int kb = s * kc, ke = min(ksteps, kb + kc);
@@ -143,34 +149,34 @@ __global__ __launch_bounds__(256) void skinny_part_kernel(LayerArgs a, float* pa
     const int c = c0 + (lane & 15);
     const int koff = 8 * (lane >> 4);
     const bf16* bp = c < ncols ? P::b_row(a, 0, c) + koff : nullptr;
-    const bf16* ap[4];
+    const bf16* ap[NRB];
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
+    for (int rb = 0; rb < NRB; ++rb) {
         const int r = r0 + rb * 16 + (lane & 15);
         ap[rb] = (rb < nrb && r < a.T) ? P::a_row(a, 0, r) + koff : nullptr;
     }
-    f32x4 acc[4];
+    f32x4 acc[NRB];
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int ks = ks0; ks < ks1; ks += 4) {
-        uint4 bv[4], av[4][4];
+    for (int rb = 0; rb < NRB; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ks = ks0; ks < ks1; ks += UB) {
+        uint4 bv[UB], av[UB][NRB];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < UB; ++u) {
             const int k0 = (ks + u) * 32;
             const bool ok = ks + u < ks1;
             bv[u] = (ok && bp) ? ldg16(bp + k0) : kZero16;
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb) av[u][rb] = (ok && ap[rb]) ? ldg16(ap[rb] + k0) : kZero16;
+            for (int rb = 0; rb < NRB; ++rb) av[u][rb] = (ok && ap[rb]) ? ldg16(ap[rb] + k0) : kZero16;
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < UB; ++u)
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb)
+            for (int rb = 0; rb < NRB; ++rb)
                 if (rb < nrb) acc[rb] = mfma16(as_bf16x8(av[u][rb]), as_bf16x8(bv[u]), acc[rb]);
     }
-    __shared__ f32x4 red[4][4][64];
+    __shared__ f32x4 red[4][NRB][64];
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
+    for (int rb = 0; rb < NRB; ++rb)
         if (rb < nrb) red[wave][rb][lane] = acc[rb];
     __syncthreads();
     const int rb = threadIdx.x >> 6;
@@ -252,6 +258,122 @@ __device__ inline void paired_slices(int& slice, int& ai) {
     }
 }
 
+// The rows of one streaming-FFN workgroup's expert.  With a dispatch: the
+// expert is active expert ai (active experts in ascending id order), its
+// rows the slots offsets[e] .. offsets[e+1] (perm gives each slot's pair
+// t*K + k, and the output row is the slot).
+// Self-routed (T <= 256, no dispatch): the workgroup reads all T*K routed ids
+// (coalesced, into LDS) and finds the same active-expert order itself: a bit
+// per FFN expert that any token names, then the ai-th set bit.  So the grid
+// maps to active experts exactly as after a dispatch (workgroups past the
+// active count return at once, and every XCD gets an even share of the real
+// work).  A token names an expert at most once, so list[t] = the pair t*K + k
+// naming e (or none) gives the expert's rows in token order; compacted with
+// a ballot per wave, the pair indices are both the row's token (pair / K)
+// and its output row.
+struct ExpertRows {
+    int e, n, base;
+    const int* list;   // self-routed: n pair indices in LDS; else nullptr
+    __device__ int pair(const LayerArgs& a, int i) const { return list ? list[i] : a.perm[base + i]; }
+    __device__ int out_row(int i) const { return list ? list[i] : base + i; }
+};
+
+constexpr int kSelfRouteMaskWords = 64;   // FFN experts / 32 (at most 2048 experts)
+
+struct SelfRouteLds {
+    uint32_t amask[kSelfRouteMaskWords];   // FFN experts named by any token
+    int list[kSkinnyMaxRows];
+    int wcnt[4];
+    int e, n_active;
+};
+
+// Dynamic LDS bytes of a streaming-FFN launch: the routed ids as 16-bit
+// values when self-routed.
+inline size_t self_route_lds_bytes(int T, int K, bool self_route) {
+    return self_route ? ((size_t)T * K * 2 + 15) / 16 * 16 : 0;
+}
+
+// false: the workgroup has no rows (the same in every thread: return).
+// L: LDS; ids16: dynamic LDS of T*K 16-bit ids (self-routed).  256 threads.
+__device__ inline bool expert_rows(const LayerArgs& a, int ai, SelfRouteLds& L, uint16_t* ids16,
+                                   ExpertRows& r) {
+    if (!a.self_route) {
+        if (ai >= *a.n_active) return false;
+        r.e = a.active[ai];
+        r.base = a.offsets[r.e];
+        r.n = a.offsets[r.e + 1] - r.base;
+        r.list = nullptr;
+        return true;
+    }
+    if (ai >= a.n_ffn) return false;
+    const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+    const int tk = a.T * a.K, nw = cdiv(a.n_ffn, 32);
+    if (t < kSelfRouteMaskWords) L.amask[t] = 0u;
+    L.list[t] = -1;
+    __syncthreads();
+    // the ids, 8 coalesced loads per thread in flight at a time
+    for (int p0 = t; p0 < tk; p0 += 8 * 256) {
+        int v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = a.ids[min(p0 + 256 * u, tk - 1)];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int p = p0 + 256 * u;
+            if (p < tk) {
+                ids16[p] = (uint16_t)v[u];
+                if (v[u] < a.n_ffn) atomicOr(&L.amask[v[u] >> 5], 1u << (v[u] & 31));
+            }
+        }
+    }
+    __syncthreads();
+    // wave 0: the ai-th set bit of the mask (prefix count of set bits over
+    // the words, one word per lane)
+    if (wave == 0) {
+        const uint32_t w = lane < nw ? L.amask[lane] : 0u;
+        const int c = __popc(w);
+        int incl = c;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(incl, off);
+            if (lane >= off) incl += y;
+        }
+        if (lane == 63) L.n_active = incl;
+        if (ai >= incl - c && ai < incl) {
+            uint32_t x = w;
+            for (int i = incl - c; i < ai; ++i) x &= x - 1;   // drop the lower set bits
+            L.e = lane * 32 + __builtin_ctz(x);
+        }
+    }
+    __syncthreads();
+    if (ai >= L.n_active) return false;
+    const int e = L.e;
+    for (int p = t; p < tk; p += 256)
+        if (ids16[p] == e) L.list[p / a.K] = p;
+    __syncthreads();
+    const int pair = L.list[t];
+    __syncthreads();
+    const unsigned long long m = __ballot(pair >= 0);
+    if (lane == 0) L.wcnt[wave] = __popcll(m);
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const int c = L.wcnt[w];
+        before += w < wave ? c : 0;
+        total += c;
+    }
+    if (pair >= 0) {
+        const unsigned long long below = lane ? (~0ull >> (64 - lane)) : 0ull;
+        L.list[before + __popcll(m & below)] = pair;
+    }
+    __syncthreads();
+    r.e = e;
+    r.n = total;
+    r.base = 0;
+    r.list = L.list;
+    return true;
+}
+
 // F: the expert weights' format (0 bf16, 1 FP8 E4M3 with one float32 scale
 // per weight row applied to that row's fp32 result, 2 MXFP4 -- the shapes
 // ffn_stream_mx_kernel does not take).
@@ -263,10 +385,12 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(LayerArgs a) {
         paired_slices(slice, ai);
     else
         slice = blockIdx.x, ai = blockIdx.y;
-    if (ai >= *a.n_active) return;
-    const int e = a.active[ai];
+    __shared__ SelfRouteLds srl;
+    extern __shared__ uint16_t ids16[];
+    ExpertRows er;
+    if (!expert_rows(a, ai, srl, ids16, er)) return;
+    const int e = er.e;
     const int j0 = slice * MS;
-    const int r_begin = a.offsets[e], r_end = a.offsets[e + 1];
     const int l = a.l, m = a.m;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int lr = lane & 15, k16 = 16 * (lane >> 4);
@@ -281,11 +405,12 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(LayerArgs a) {
     constexpr int NKB = F == 2 ? 4 : 2;
     __shared__ bf16 As[16 * AST];
 
-    for (int rc = r_begin; rc < r_end; rc += 16) {
-        const int nr = min(16, r_end - rc);
+    for (int rc = 0; rc < er.n; rc += 16) {
+        const int nr = min(16, er.n - rc);
         // ---- phase 1: H[16 x MS] = Z[rows] . W1[e][j0 : j0+MS]^T, reduce over l
-        const int my_slot = rc + min(lr, nr - 1);
-        const bf16* zp = Z + (size_t)(a.perm[my_slot] / a.K) * l + k16;
+        const int my_row = rc + min(lr, nr - 1);
+        const size_t orow = (size_t)er.out_row(my_row) * l;   // the lane's output row (lanes lr < nr)
+        const bf16* zp = Z + (size_t)(er.pair(a, my_row) / a.K) * l + k16;
         size_t w1o[NBW];   // element offset of the lane's W1 row, at its k16
 #pragma unroll
         for (int b = 0; b < NBW; ++b) w1o[b] = ((size_t)e * m + j0 + (wave + 4 * b) * 16 + lr) * l + k16;
@@ -407,8 +532,7 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(LayerArgs a) {
                     for (int u = 0; u < NU; ++u) {
                         const int ib = ib0 + 4 * (NU * it + u);
                         if (ib < nblk)
-                            *reinterpret_cast<f32x4*>(&Yp[(size_t)(rc + lr) * l + ib * 16 + 4 * (lane >> 4)]) =
-                                yb[it][u];
+                            *reinterpret_cast<f32x4*>(&Yp[orow + ib * 16 + 4 * (lane >> 4)]) = yb[it][u];
                     }
             }
         }
@@ -435,10 +559,12 @@ __global__ __launch_bounds__(256) void ffn_stream_mx_kernel(LayerArgs a) {
     constexpr int NSB = 2;   // 128-wide k blocks per batch of phase-1 loads
     int slice, ai;
     paired_slices(slice, ai);
-    if (ai >= *a.n_active) return;
-    const int e = a.active[ai];
+    __shared__ SelfRouteLds srl;
+    extern __shared__ uint16_t ids16[];
+    ExpertRows er;
+    if (!expert_rows(a, ai, srl, ids16, er)) return;
+    const int e = er.e;
     const int j0 = slice * MS;
-    const int r_begin = a.offsets[e], r_end = a.offsets[e + 1];
     const int l = a.l, m = a.m;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int lr = lane & 15, g = lane >> 4;
@@ -451,11 +577,12 @@ __global__ __launch_bounds__(256) void ffn_stream_mx_kernel(LayerArgs a) {
         return as_bf16x8(fp4x8_to_bf16x8(word, e8m0_to_f32(scale_byte & 0xffu)));
     };
 
-    for (int rc = r_begin; rc < r_end; rc += 16) {
-        const int nr = min(16, r_end - rc);
+    for (int rc = 0; rc < er.n; rc += 16) {
+        const int nr = min(16, er.n - rc);
         // ---- phase 1: H[16 x MS] = Z[rows] . W1[e][j0 : j0+MS]^T, reduce over l
-        const int my_slot = rc + min(lr, nr - 1);
-        const bf16* zp = Z + (size_t)(a.perm[my_slot] / a.K) * l + 32 * g;
+        const int my_row = rc + min(lr, nr - 1);
+        const size_t orow = (size_t)er.out_row(my_row) * l;   // the lane's output row (lanes lr < nr)
+        const bf16* zp = Z + (size_t)(er.pair(a, my_row) / a.K) * l + 32 * g;
         size_t w1e[NBW];   // element offset of the lane's W1 row
 #pragma unroll
         for (int b = 0; b < NBW; ++b) w1e[b] = ((size_t)e * m + j0 + (wave + 4 * b) * 16 + lr) * l;
@@ -540,7 +667,7 @@ __global__ __launch_bounds__(256) void ffn_stream_mx_kernel(LayerArgs a) {
                 for (int u = 0; u < NU; ++u) {
                     const int ib = ib0 + 4 * u;
                     if (ib < nblk)
-                        *reinterpret_cast<f32x4*>(&Yp[(size_t)(rc + lr) * l + ib * 16 + 4 * (lane >> 4)]) = yb[u];
+                        *reinterpret_cast<f32x4*>(&Yp[orow + ib * 16 + 4 * (lane >> 4)]) = yb[u];
                 }
             }
         }

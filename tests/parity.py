@@ -102,7 +102,11 @@ def expected_dispatch(ids: np.ndarray, N: int):
 
 
 def read_dispatch(ws: torch.Tensor, dims, K: int, T: int, N: int):
+    """The dispatch arrays of the last forward, or None where the forward
+    writes none (the streaming path at T <= 256 routes inside the FFN)."""
     lay = B.latentmoe_workspace_layout(dims, K)
+    if not lay.written:
+        return None
     raw = ws.cpu().numpy()
 
     def arr(off, n):
@@ -134,6 +138,10 @@ class GpuRun:
         del ws, dinp
 
     def check_dispatch(self) -> None:
+        if self.dispatch is None:
+            # no dispatch arrays: only the self-routed streaming path
+            assert self.resolved == B.LMOE_PATH_STREAM and self.T <= 256, "dispatch arrays not written"
+            return
         counts, offsets, perm, slot_of, n_active = self.dispatch
         ec, eo, ep, es = expected_dispatch(self.ids, self.N)
         assert np.array_equal(counts, ec), "counts"

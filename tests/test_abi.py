@@ -74,6 +74,20 @@ def test_resolved_paths(lib):
     assert B.latentmoe_resolved_path(dims_of(WORKLOADS["tiny_f32"], S), 4) == B.LMOE_EUNSUPPORTED
 
 
+def test_dispatch_written_flag(lib):
+    # the streaming path with T <= 256 routes inside the expert FFN and
+    # writes no dispatch arrays; every other path does
+    S, Tl = B.LMOE_PATH_STREAM, B.LMOE_PATH_TILED
+    dec = WORKLOADS["decode"]
+    assert B.latentmoe_workspace_layout(dims_of(dec), 22).written == 0
+    assert B.latentmoe_workspace_layout(dims_of(dec, Tl), 22).written == 1
+    assert B.latentmoe_workspace_layout(dims_of(WORKLOADS["prefill"]), 22).written == 1
+    big = B.make_dims(300, dec.d, dec.l, dec.N, dec.m, dec.dtype, S)
+    assert B.latentmoe_workspace_layout(big, 22).written == 1
+    small = B.make_dims(256, dec.d, dec.l, dec.N, dec.m, dec.dtype, S)
+    assert B.latentmoe_workspace_layout(small, 22).written == 0
+
+
 @pytest.mark.parametrize("field,value,K", [
     ("T", 0, 4), ("d", 100, 4), ("l", 0, 4), ("m", 65, 4), ("N", 0, 4), ("N", 4096, 4),
     ("dtype", 7, 4), ("path", 9, 4), ("m_shared", 96, 4), ("m_shared", -64, 4),
