@@ -110,9 +110,11 @@ struct Plan {
     int ms = 128;                 // streaming FFN m-slice
     int nsplit = 1;               // streaming FFN partial planes
     long long max_tiles = 0;
+    int tall_rows = 0;            // > 0: experts over tile_rows rows take G2Large tiles (tiles_tall)
+    long long max_tiles_tall = 0;
     size_t es = 2;
     size_t z, logits, ids, gates, counts, offsets, perm, slot_of, blk_counts, blk_offsets, tiles, n_tiles,
-        active, n_active, abuf, ybuf, s, part, a_s, y_s, tail, total;
+        tiles_tall, n_tiles_tall, active, n_active, abuf, ybuf, s, part, a_s, y_s, tail, total;
 };
 
 bool mult64(int v) { return v > 0 && v % 64 == 0; }
@@ -212,6 +214,14 @@ Plan make_plan(const lmoe_dims* dm, int32_t K) {
     }
     p.nblk = cdiv(d.T, kRouteTok);
     p.max_tiles = TK / p.tile_rows + std::min<long long>(d.N, TK);
+    // On the 128-row FFN tiles, experts with more than 128 rows (possible
+    // only when T > 128) take 256-row tiles on the large GEMM tile instead:
+    // with skewed routing most rows belong to a few heavy experts, whose
+    // weights are then read by half as many row tiles.
+    if (p.bf16 && p.path == LMOE_PATH_TILED && !p.ffn_large && d.T > G2Small::BM) {
+        p.tall_rows = G2Large::BM;
+        p.max_tiles_tall = TK / p.tall_rows + std::min<long long>(d.N, TK);
+    }
 
     size_t o = 0;
     auto take = [&](size_t bytes) {
@@ -231,6 +241,8 @@ Plan make_plan(const lmoe_dims* dm, int32_t K) {
     p.blk_offsets = take((size_t)p.nblk * p.nr * 4);
     p.tiles = take((size_t)p.max_tiles * 8);
     p.n_tiles = take(4);
+    p.tiles_tall = take((size_t)p.max_tiles_tall * 8);
+    p.n_tiles_tall = take(4);
     p.active = take((size_t)d.N * 4);
     p.n_active = take(4);
     if (p.path == LMOE_PATH_STREAM) {
@@ -530,6 +542,18 @@ hipError_t launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* 
                     launch_g2<F1, G2Large>(a, (int)mt, cdiv(a.m, G2Large::BN), st);
                     mark(4);
                     launch_g2<F2, G2Large>(a, (int)mt, cdiv(a.l, G2Large::BN), st);
+                } else if (p.tall_rows > 0) {
+                    // each product: the heavy experts' tall tiles, then the
+                    // light experts' tiles
+                    LayerArgs at = a;
+                    at.tiles = a.tiles_tall;
+                    at.n_tiles = a.n_tiles_tall;
+                    const int mtt = (int)p.max_tiles_tall;
+                    launch_g2<F1, G2Large>(at, mtt, cdiv(a.m, G2Large::BN), st);
+                    launch_g2<F1, G2Small>(a, (int)mt, cdiv(a.m, G2Small::BN), st);
+                    mark(4);
+                    launch_g2<F2, G2Large>(at, mtt, cdiv(a.l, G2Large::BN), st);
+                    launch_g2<F2, G2Small>(a, (int)mt, cdiv(a.l, G2Small::BN), st);
                 } else {
                     launch_g2<F1, G2Small>(a, (int)mt, cdiv(a.m, G2Small::BN), st);
                     mark(4);
@@ -780,6 +804,9 @@ static int forward_impl(const void* x, const void* W_down, const void* W_router,
     a.blk_offsets = reinterpret_cast<int32_t*>(ws + p.blk_offsets);
     a.tiles = reinterpret_cast<int2*>(ws + p.tiles);
     a.n_tiles = reinterpret_cast<int32_t*>(ws + p.n_tiles);
+    a.tiles_tall = reinterpret_cast<int2*>(ws + p.tiles_tall);
+    a.n_tiles_tall = reinterpret_cast<int32_t*>(ws + p.n_tiles_tall);
+    a.tall_rows = p.tall_rows;
     a.active = reinterpret_cast<int32_t*>(ws + p.active);
     a.n_active = reinterpret_cast<int32_t*>(ws + p.n_active);
     a.abuf = ws + p.abuf;

@@ -49,6 +49,13 @@ struct LayerArgs {
     int32_t* blk_offsets;  // [nblk, N]
     int2* tiles;           // grouped-GEMM row tiles: (expert, first slot)
     int32_t* n_tiles;
+    // tall_rows > 0: `tiles` lists only the experts with at most tile_rows
+    // rows; the others get row tiles of tall_rows rows in tiles_tall, run on
+    // the larger GEMM tile (their weights and gathered rows are then read by
+    // half as many tiles)
+    int2* tiles_tall;
+    int32_t* n_tiles_tall;
+    int tall_rows;
     int32_t* active;       // experts with rows, ascending
     int32_t* n_active;
     void* abuf;            // [T*K, m] relu(h)^2

@@ -316,14 +316,35 @@ __device__ inline void finish_scan(const LayerArgs& a, const int* cnt, int* off,
         *a.n_active = n_act;
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < N; e += blockDim.x) tmp[e] = e < a.n_ffn ? cdiv(cnt[e], a.tile_rows) : 0;
-    __syncthreads();
-    const int ntiles = block_excl_scan(tmp, N, wsum);
-    for (int e = threadIdx.x; e < N; e += blockDim.x) {
-        const int nt = e < a.n_ffn ? cdiv(cnt[e], a.tile_rows) : 0, base = tmp[e], o = off[e];
-        for (int i = 0; i < nt; ++i) a.tiles[base + i] = make_int2(e, o + i * a.tile_rows);
+    // The row tiles of the experts `sel` picks, `rows` rows each, into
+    // list[first ...] in expert order; returns their count.
+    auto emit = [&](int rows, auto sel, int2* list, int first) {
+        for (int e = threadIdx.x; e < N; e += blockDim.x) tmp[e] = sel(e) ? cdiv(cnt[e], rows) : 0;
+        __syncthreads();
+        const int n = block_excl_scan(tmp, N, wsum);
+        for (int e = threadIdx.x; e < N; e += blockDim.x) {
+            const int nt = sel(e) ? cdiv(cnt[e], rows) : 0, base = first + tmp[e], o = off[e];
+            for (int i = 0; i < nt; ++i) list[base + i] = make_int2(e, o + i * rows);
+        }
+        __syncthreads();
+        return n;
+    };
+    auto ffn = [&](int e) { return e < a.n_ffn; };
+    if (a.tall_rows == 0) {
+        const int n = emit(a.tile_rows, ffn, a.tiles, 0);
+        if (threadIdx.x == 0) *a.n_tiles = n;
+    } else {
+        // experts with at most tile_rows rows: tile_rows-row tiles; the
+        // others: tall_rows-row tiles, in the second list
+        auto light = [&](int e) { return e < a.n_ffn && cnt[e] <= a.tile_rows; };
+        auto heavy = [&](int e) { return e < a.n_ffn && cnt[e] > a.tile_rows; };
+        const int nl = emit(a.tile_rows, light, a.tiles, 0);
+        const int nt = emit(a.tall_rows, heavy, a.tiles_tall, 0);
+        if (threadIdx.x == 0) {
+            *a.n_tiles = nl;
+            *a.n_tiles_tall = nt;
+        }
     }
-    if (threadIdx.x == 0) *a.n_tiles = ntiles;
     // the zero row of every expert-output plane (row T*K), read by the
     // combine for zero-computation experts
     if (a.N > a.n_ffn) {
