@@ -744,7 +744,7 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm2_kernel(LayerArgs a, int 
 // full rounds), and tail_fixup_kernel adds the s partials in order and
 // applies P's epilogue: ceil(G / R) rounds become floor(G / R) + 1/s.
 // P: a problem with one row group (grp 0) and a one-segment reduction
-// (ProjRouter, Up).
+// (the projection ProjRouter).
 template <class P, int BM, int BN>
 struct Tail {
     using BElem = typename P::BElem;

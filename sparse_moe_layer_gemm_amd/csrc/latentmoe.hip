@@ -345,10 +345,11 @@ size_t tail_bytes(long long G, int ksteps) {
     return t.s > 1 ? (size_t)t.ntail * t.s * C::BM * C::BN * 4 : 0;
 }
 
-// Bytes of the tail partials the bf16 tiled path's projection and
-// up-projection may need (the projection's columns depend on the mode, only
-// known at the call: the larger of the two).  No tail with a shared expert's
-// two-part up-projection.
+// Bytes of the tail partials the bf16 tiled path's projection may need (its
+// columns depend on the mode, only known at the call: the larger of the
+// two).  The up-projection has no tail: its reduction (l) is short, and the
+// half tiles' fp32 partials and the fixup cost what the shorter last round
+// saves (skewed workload: 249 -> 258 us with a tail).
 size_t tiled_tail_bytes(const lmoe_dims& d, const Plan& p) {
     if (!p.bf16 || p.skinny) return 0;
     size_t t = 0;
@@ -358,8 +359,6 @@ size_t tiled_tail_bytes(const lmoe_dims& d, const Plan& p) {
                             ? tail_bytes<G2Large>((long long)cdiv(d.T, G2Large::BM) * cdiv(nc, G2Large::BN), d.d / 64)
                             : tail_bytes<G2Small>((long long)cdiv(d.T, G2Small::BM) * cdiv(nc, G2Small::BN), d.d / 64));
     }
-    if (d.m_shared == 0)
-        t = std::max(t, tail_bytes<UpTile>((long long)cdiv(d.T, UpTile::BM) * cdiv(d.d, UpTile::BN), d.l / 64));
     return t;
 }
 
@@ -586,7 +585,7 @@ hipError_t launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* 
             if (p.skinny)
                 skinny_kernel<Up<bf16>><<<dim3(cdiv(a.d, 16), cdiv(a.T, 64)), b1024, 0, st>>>(a);
             else
-                launch_g2_tail<Up<bf16>, UpTile>(a, cdiv(a.T, UpTile::BM), cdiv(a.d, UpTile::BN), a.l / 64, st);
+                launch_g2<Up<bf16>, UpTile>(a, cdiv(a.T, UpTile::BM), cdiv(a.d, UpTile::BN), st);
         } else {
             gemm_simt_kernel<Up<float>><<<dim3(cdiv(a.T, kSimtM), cdiv(a.d, kSimtN)), b256, 0, st>>>(a);
         }
