@@ -536,6 +536,23 @@ def test_all_tokens_on_few_experts():
         assert set(np.unique(rep["ids"])) == {3, 7}
 
 
+def test_heavy_and_light_experts_tiled():
+    """Two experts that nearly every token names (a bias of +3) beside 62
+    light ones, on the 128-row FFN tiles: the two heavy experts (over 500
+    rows each: two full 256-row tiles and a ragged one) run on the large GEMM
+    tile from their own tile list, the light ones (at most 128 rows) on
+    128-row tiles."""
+    w = Workload("heavy_light", T=600, d=256, l=128, N=64, K=4, m=128, dtype="bf16", bias=True)
+    inp = make_inputs(w, 8)
+    inp["bias"] = torch.zeros(w.N)
+    inp["bias"][5] = 3.0
+    inp["bias"][40] = 3.0
+    rep = P.compare(w, inp, w.K, path=TL, tag="heavy_light/path2")
+    counts = np.bincount(np.asarray(rep["ids"]).ravel(), minlength=w.N)
+    assert counts[5] > 512 and counts[40] > 512
+    assert np.sort(counts)[-3] <= 128
+
+
 # --- exact properties ----------------------------------------------------------
 
 @pytest.mark.parametrize("path", [S, TL])
