@@ -509,9 +509,13 @@ hipError_t launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* 
                     kernel<<<grid, b256, dyn, st>>>(a);
                 }
             };
-            // (MXFP4 pairs slices across the grid in chunks of 16 workgroups:
-            // a multiple of 8 experts keeps every chunk whole)
-            const dim3 g(p.nsplit, p.wfmt == 2 ? (unsigned)(cdiv(a.n_ffn, 8) * 8) : (unsigned)a.n_ffn);
+            // One grid row per possibly active expert: at most min(n_ffn,
+            // T*K) experts receive rows, so small batches launch no
+            // workgroups that could only return.  (MXFP4 pairs slices across
+            // the grid in chunks of 16 workgroups: a multiple of 8 experts
+            // keeps every chunk whole.)
+            const int rows_g = (int)std::min<long long>(a.n_ffn, (long long)a.T * a.K);
+            const dim3 g(p.nsplit, p.wfmt == 2 ? (unsigned)(cdiv(rows_g, 8) * 8) : (unsigned)rows_g);
             auto stream = [&](auto fmt) {
                 constexpr int F = decltype(fmt)::value;
                 if (F <= 1 && p.ms == 256)
