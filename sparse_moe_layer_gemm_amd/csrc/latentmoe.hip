@@ -3,7 +3,9 @@
 // One forward enqueues, on the caller's stream:
 //   1. z = W_down x and the router logits   (skinny / tiled MFMA / SIMT GEMM)
 //   2. top-K + softmax renormalisation      (one wavefront per token)
-//   3. dispatch: counting sort by expert    (1 or 3 launches)
+//   3. dispatch: counting sort by expert    (1 or 3 launches; none on the
+//                                            streaming path at T <= 256,
+//                                            whose FFN routes itself)
 //   4. expert FFN                           (streaming kernel, or two grouped
 //                                            GEMMs with ReLU^2 and the gate
 //                                            fused into their epilogues)

@@ -13,8 +13,10 @@
 //   skinny_part_kernel<P, NRB>: the same, with the reduction also split over
 //     workgroups (fp32 partial tiles added by the consumer).
 //   ffn_stream_kernel<MS, F>: the expert FFN.  Workgroup (s, a) takes
-//     active expert a and the m-slice [s*MS, (s+1)*MS) (MS = 64, 128, or 256
-//     when there are enough workgroups to go round): it computes
+//     active expert a (from the dispatch, or, at T <= 256, found by the
+//     workgroup itself from the top-K ids: expert_rows()) and the m-slice
+//     [s*MS, (s+1)*MS) (MS = 64, 128, or 256 when there are enough
+//     workgroups to go round): it computes
 //     relu(W1[e][slice] z)^2 for up to 16 routed rows at a time, keeps it in
 //     LDS, and multiplies it by the matching column slice of W2[e], writing
 //     an fp32 partial expert output per slice.  Every weight byte of an
