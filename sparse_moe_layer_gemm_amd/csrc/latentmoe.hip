@@ -72,11 +72,14 @@ using UpTile = G2Large;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 // The skinny projection's reduction is split into enough k-ranges that the
-// (16-column group, k-range) workgroups cover the CUs; its partial tiles
-// are part[split][T][stride], stride = columns rounded up to 4 floats.
+// (16-column group, k-range) workgroups fill the CUs once: 768 for T <= 32
+// (the kernel with at most two row blocks fits three workgroups per CU),
+// else 512; its partial tiles are part[split][T][stride], stride = columns
+// rounded up to 4 floats.
 constexpr int kMaxProjSplit = kMaxSplit;   // the top-K kernel adds at most this many partials
 int proj_split(int ncols, int T) {
-    return std::max(1, std::min(kMaxProjSplit, 512 / (cdiv(ncols, 16) * cdiv(T, 64))));
+    const int target = T <= 32 ? 768 : 512;
+    return std::max(1, std::min(kMaxProjSplit, target / (cdiv(ncols, 16) * cdiv(T, 64))));
 }
 int proj_stride(int ncols) { return (ncols + 3) / 4 * 4; }
 size_t proj_part_floats(int ncols, int T) {  // per token row
@@ -445,7 +448,7 @@ hipError_t launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* 
         auto launch_topk = [&](auto npl) {
             constexpr int NPL = decltype(npl)::value;
             if (pin.nsplit > 0)
-                topk_part_kernel<NPL><<<dim3(a.T), b256, 0, st>>>(a, pin);
+                topk_part_kernel<NPL><<<dim3(a.T, 2), b256, 0, st>>>(a, pin);
             else
                 topk_kernel<NPL><<<dim3(cdiv(a.T, 4)), b256, 0, st>>>(a);
         };

@@ -141,9 +141,11 @@ __global__ __launch_bounds__(256) void topk_kernel(LayerArgs a) {
     topk_token<NPL>(a, t, a.logits + (size_t)t * a.N, s_key[wave], s_idx[wave], s_val[wave]);
 }
 
-// One workgroup per token, after the split projection: its 256 threads add
-// the partial tiles in split order (logits: then the bias, into LDS; z:
-// rounded once to bf16, to global memory), then wave 0 selects the top K.
+// Two workgroups per token, after the split projection, each adding partial
+// tiles in split order: blockIdx.y = 0 the logits (then the bias, into LDS),
+// after which wave 0 selects the top K; blockIdx.y = 1 z and the shared
+// expert's h_s (relu(h_s)^2), rounded once to bf16, to global memory.  The
+// selecting workgroup thus waits only for the logits' partials.
 template <int NPL>
 __global__ __launch_bounds__(256) void topk_part_kernel(LayerArgs a, PartIn pin) {
     const int t = blockIdx.x;
@@ -155,13 +157,13 @@ __global__ __launch_bounds__(256) void topk_part_kernel(LayerArgs a, PartIn pin)
     const float* pt = pin.part + (size_t)t * pin.stride;
     const int le = pin.lz + a.m_s;   // first logit column
     // The partials of a value are all loaded before they are added (in split
-    // order), so their latencies overlap; the first group of 4 z columns and
-    // the first two logits of each thread are loaded together, so the usual
-    // sizes (le <= 1024, N <= 512) take one round trip to memory.  The loads
-    // are unconditional (indices past the end and splits past nsplit are
-    // clamped to valid ones inside the partial rows, and their values not
-    // used): conditional loads
-    // compile to branches that each wait for the loads before them.
+    // order), so their latencies overlap; a thread's first two logits (or
+    // first group of 4 z columns) are loaded together, so the usual sizes
+    // (le <= 1024, N <= 512) take one round trip to memory.  The loads are
+    // unconditional (indices past the end and splits past nsplit are clamped
+    // to valid ones inside the partial rows, and their values not used):
+    // conditional loads compile to branches that each wait for the loads
+    // before them.
     const int s_last = pin.nsplit - 1;
     auto load_lg = [&](int e, float* v, float& b) {
         const int ec = min(e, a.N - 1);
@@ -204,14 +206,19 @@ __global__ __launch_bounds__(256) void topk_part_kernel(LayerArgs a, PartIn pin)
         const bf16 b[4] = {(bf16)zs[0], (bf16)zs[1], (bf16)zs[2], (bf16)zs[3]};
         *reinterpret_cast<uint2*>((c < pin.lz ? zo : so) + c) = *reinterpret_cast<const uint2*>(b);
     };
+    if (blockIdx.y == 1) {
+        for (int c = 4 * (int)threadIdx.x; c < le; c += 1024) {
+            f32x4 v[kMaxSplit];
+            load_z(c, v);
+            add_z(c, v);
+        }
+        return;
+    }
     {
-        f32x4 zv[kMaxSplit];
         float v0[kMaxSplit], v1[kMaxSplit], b0, b1;
-        const int c = 4 * (int)threadIdx.x, e = (int)threadIdx.x;
-        load_z(c, zv);
+        const int e = (int)threadIdx.x;
         load_lg(e, v0, b0);
         load_lg(e + 256, v1, b1);
-        add_z(c, zv);
         add_lg(e, v0, b0);
         add_lg(e + 256, v1, b1);
     }
@@ -219,11 +226,6 @@ __global__ __launch_bounds__(256) void topk_part_kernel(LayerArgs a, PartIn pin)
         float v[kMaxSplit], b;
         load_lg(e, v, b);
         add_lg(e, v, b);
-    }
-    for (int c = 4 * (int)threadIdx.x + 1024; c < le; c += 1024) {
-        f32x4 v[kMaxSplit];
-        load_z(c, v);
-        add_z(c, v);
     }
     __syncthreads();
     if (threadIdx.x < 64) topk_token<NPL>(a, t, lg, s_key, s_idx, s_val);
