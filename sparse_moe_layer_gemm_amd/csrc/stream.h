@@ -478,10 +478,15 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(LayerArgs a) {
         // columns i0 + 4 (l / 16) .. +3 of row l % 16: one 16-byte store.
         // A pass loads NU blocks of 16 output columns; the results of NP
         // passes are stored together, since a load issued behind pending
-        // stores waits for them to complete.
-        // passes per batch of stores (fewer for FP8 and MXFP4, whose decode
-        // registers would otherwise cut the waves per SIMD: 2 and 4 of them)
-        constexpr int NP = F == 0 ? 4 : (F == 1 ? 2 : 1);
+        // stores waits for them to complete (the stores cost the kernel more
+        // time than their bytes: without them the decode FFN ran 17 µs
+        // faster).  bf16 weights in 256-wide slices: 8 passes, a wave's 16
+        // blocks of the usual l = 1024 in one batch, so that its stores come
+        // after all of its loads; 128-wide slices: 4 (their 4 blocks per pass
+        // would need 128 more registers); fewer for FP8 (4 at 256-wide
+        // slices, else 2) and MXFP4, whose decode registers would otherwise
+        // cut the waves per SIMD.
+        constexpr int NP = F == 0 ? (MS == 256 ? 8 : 4) : (F == 1 ? (MS == 256 ? 4 : 2) : 1);
         bf16x8 af[KB][2];
 #pragma unroll
         for (int q = 0; q < KB; ++q)
