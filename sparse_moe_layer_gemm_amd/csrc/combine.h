@@ -6,9 +6,9 @@
 // The expert outputs sit in `nsplit` partial planes (the streaming FFN's
 // m-slices; 1 for the tiled FFN) of [T*K, l] each.  `gated`: multiply by the
 // gate here (streaming FFN) or not (the tiled FFN already did).  YT: float
-// (the streaming FFN's partials, the float32 layer) or f16, the tiled FFN's
-// gate-scaled outputs times kYScale (summed as they are, then scaled back
-// once: a power of two, so no extra rounding).
+// (the float32 layer) or f16 times kYScale (the bf16 layer: the streaming
+// FFN's partials, the tiled FFN's gate-scaled outputs; summed as they are,
+// then scaled back once: a power of two, so no extra rounding).
 // A rank's expert output is at its slot (slot_of, after a dispatch), or at
 // row t*K + k of each plane when the streaming FFN routed itself
 // (self_route).  Zero-computation experts (ids >= n_ffn) have no expert
@@ -92,6 +92,20 @@ __global__ __launch_bounds__(256) void combine_kernel(LayerArgs a, int nsplit, i
                 const f32x8 f = __builtin_convertvector(__builtin_bit_cast(f16x8, raw), f32x8);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) part[i] = f[i];
+                // the other planes, loaded 8 at a time before they are added
+                // (in plane order)
+                for (int sp0 = 1; sp0 < nsplit; sp0 += 8) {
+                    uint4 q[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) q[i] = sp0 + i < nsplit ? ldg16(yp + (sp0 + i) * plane) : kZero16;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        if (sp0 + i < nsplit) {
+                            const f32x8 g8 = __builtin_convertvector(__builtin_bit_cast(f16x8, q[i]), f32x8);
+#pragma unroll
+                            for (int c = 0; c < 8; ++c) part[c] += g8[c];
+                        }
+                }
             } else {
                 part[0] = __uint_as_float(raw.x);
                 part[1] = __uint_as_float(raw.y);

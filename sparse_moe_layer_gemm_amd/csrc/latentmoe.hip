@@ -93,7 +93,7 @@ constexpr int kStreamMaxMeanRows = 16;
 // ffn_stream_mx_kernel) when the expected (active expert, slice)
 // workgroups under uniform routing number at least kWideSliceMinWgs (four
 // per CU) and the active experts average at most kWideSliceMaxRows rows.
-// Wider slices halve the fp32 partial planes (the FFN's stores, the
+// Wider slices halve the partial planes (the FFN's stores, the
 // combine's reads) but also the workgroups that stream the weights.  With
 // bf16 experts and fewer than kNarrowSliceMaxWgs such workgroups at 128
 // (a few tokens on few, large experts) the slice is 64 wide: twice the
@@ -252,7 +252,7 @@ Plan make_plan(const lmoe_dims* dm, int32_t K) {
     p.n_active = take(4);
     if (p.path == LMOE_PATH_STREAM) {
         p.abuf = take(0);
-        p.ybuf = take((size_t)p.nsplit * (TK + 1) * d.l * 4);   // + the zero row of each plane
+        p.ybuf = take((size_t)p.nsplit * (TK + 1) * d.l * 2);   // fp16 partials, + the zero row of each plane
     } else {
         p.abuf = take((size_t)TK * d.m * p.es);
         p.ybuf = take((size_t)(TK + 1) * d.l * p.es);
@@ -583,10 +583,14 @@ hipError_t launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* 
     }
     // 5. combine
     mark(5);
-    if (p.path == LMOE_PATH_STREAM)
-        launch_combine<E, float>(a, p.nsplit, 1, st);
-    else
-        launch_combine<E, YT>(a, 1, 0, st);
+    if constexpr (sizeof(E) == 2) {
+        if (p.path == LMOE_PATH_STREAM)
+            launch_combine<E, f16>(a, p.nsplit, 1, st);   // the streaming FFN's fp16 partials
+        else
+            launch_combine<E, YT>(a, 1, 0, st);
+    } else {
+        launch_combine<E, YT>(a, 1, 0, st);   // (the float32 layer has no streaming path)
+    }
     // 6. back to d with the residual
     mark(6);
     if (!a.standard && a.m_s == 0) {
@@ -828,7 +832,7 @@ static int forward_impl(const void* x, const void* W_down, const void* W_router,
     a.tail_part = reinterpret_cast<float*>(ws + p.tail);
     a.tile_rows = p.tile_rows;
     a.y_planes = p.nsplit;
-    a.y_row_bytes = d.l * (p.path == LMOE_PATH_STREAM ? 4 : (int)p.es);
+    a.y_row_bytes = d.l * (int)p.es;   // fp16 (scaled) outputs or partials, or float32
     a.self_route = p.skinny ? 1 : 0;
 
     hipStream_t st = static_cast<hipStream_t>(stream);

@@ -59,7 +59,9 @@ struct LayerArgs {
     int32_t* active;       // experts with rows, ascending
     int32_t* n_active;
     void* abuf;            // [T*K, m] relu(h)^2
-    void* ybuf;            // expert outputs (layout depends on the path)
+    void* ybuf;            // expert outputs: fp16 times kYScale in the bf16 layer (the streaming
+                           // FFN's per-slice partials, the tiled FFN's gate-scaled outputs),
+                           // float32 in the float32 layer
     void* s;               // [T, l] gate-weighted latent sum (latent mode)
     void* part;            // split-reduction partial tiles of the skinny projection
     void* a_s;             // [T, m_s] relu(W_s1 x)^2 (shared expert)

@@ -19,7 +19,8 @@
 //     workgroups to go round): it computes
 //     relu(W1[e][slice] z)^2 for up to 16 routed rows at a time, keeps it in
 //     LDS, and multiplies it by the matching column slice of W2[e], writing
-//     an fp32 partial expert output per slice.  Every weight byte of an
+//     a partial expert output per slice (fp16 scaled by kYScale, like the
+//     tiled path's outputs: half the bytes of fp32, 11 significant bits).  Every weight byte of an
 //     active expert is read once per 16 rows; no atomics: the combine adds
 //     the slices in a fixed order.  F: bf16, FP8 or MXFP4 weights.
 //   ffn_stream_mx_kernel<MS>: the same for MXFP4 weights with 16-byte code
@@ -397,7 +398,7 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(LayerArgs a) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int lr = lane & 15, k16 = 16 * (lane >> 4);
     const bf16* Z = static_cast<const bf16*>(a.z);
-    float* Yp = static_cast<float*>(a.ybuf) + (size_t)slice * y_plane_elems(a);
+    f16* Yp = static_cast<f16*>(a.ybuf) + (size_t)slice * y_plane_elems(a);   // scaled by kYScale
 
     constexpr int NB = MS / 16;        // 16-column blocks of the slice
     constexpr int NBW = NB / 4;        // per wave
@@ -539,7 +540,8 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(LayerArgs a) {
                     for (int u = 0; u < NU; ++u) {
                         const int ib = ib0 + 4 * (NU * it + u);
                         if (ib < nblk)
-                            *reinterpret_cast<f32x4*>(&Yp[orow + ib * 16 + 4 * (lane >> 4)]) = yb[it][u];
+                            *reinterpret_cast<uint2*>(&Yp[orow + ib * 16 + 4 * (lane >> 4)]) =
+                                pack4_f16_sat(yb[it][u] * kYScale);
                     }
             }
         }
@@ -578,7 +580,7 @@ __global__ __launch_bounds__(256) void ffn_stream_mx_kernel(LayerArgs a) {
     const uint8_t* W1 = static_cast<const uint8_t*>(a.W1);
     const uint8_t* W2 = static_cast<const uint8_t*>(a.W2);
     const bf16* Z = static_cast<const bf16*>(a.z);
-    float* Yp = static_cast<float*>(a.ybuf) + (size_t)slice * y_plane_elems(a);
+    f16* Yp = static_cast<f16*>(a.ybuf) + (size_t)slice * y_plane_elems(a);   // scaled by kYScale
     __shared__ bf16 As[16 * AST];
     auto decode = [](uint32_t word, uint32_t scale_byte) {
         return as_bf16x8(fp4x8_to_bf16x8(word, e8m0_to_f32(scale_byte & 0xffu)));
@@ -674,7 +676,8 @@ __global__ __launch_bounds__(256) void ffn_stream_mx_kernel(LayerArgs a) {
                 for (int u = 0; u < NU; ++u) {
                     const int ib = ib0 + 4 * u;
                     if (ib < nblk)
-                        *reinterpret_cast<f32x4*>(&Yp[orow + ib * 16 + 4 * (lane >> 4)]) = yb[u];
+                        *reinterpret_cast<uint2*>(&Yp[orow + ib * 16 + 4 * (lane >> 4)]) =
+                            pack4_f16_sat(yb[u] * kYScale);
                 }
             }
         }

@@ -284,8 +284,10 @@ def test_fp8_every_code(path):
 def test_fp8_layer_is_the_bf16_layer_on_decoded_weights(path):
     """With power-of-two row scales every decoded weight code * scale is a
     bfloat16 value and scaling a float32 dot product by the scale is exact,
-    so the FP8 layer equals, bit for bit, the bf16 layer on those weights."""
-    w = Workload("fp8_pow2", T=120, d=256, l=128, N=16, K=4, m=128, dtype="bf16", experts="fp8")
+    so the FP8 layer equals, bit for bit, the bf16 layer on those weights
+    (with as many active experts as here both take the same m-slices on the
+    streaming path, whose per-slice partials are rounded to fp16)."""
+    w = Workload("fp8_pow2", T=120, d=256, l=128, N=128, K=4, m=256, dtype="bf16", experts="fp8")
     inp = every_code_inputs(w, 13)
     dense = dict(inp)
     for name in ("W1", "W2"):
@@ -334,8 +336,10 @@ def every_byte_mxfp4(w: Workload, seed: int):
 
 # l = 128: the streaming FFN shared with bf16 and FP8 (8-byte code loads, a
 # scale byte per block); l = 256, m = 256: the MXFP4 streaming kernel with
-# 16-byte code loads
-MX_POW2 = [Workload("mxfp4_l128", T=120, d=256, l=128, N=16, K=4, m=128, dtype="bf16", experts="mxfp4"),
+# 16-byte code loads.  At l = 128, 160 experts keep enough of them active that
+# a bf16 layer of this shape also streams 128-wide m-slices, so both store the
+# same fp16 partial planes.
+MX_POW2 = [Workload("mxfp4_l128", T=120, d=256, l=128, N=160, K=4, m=128, dtype="bf16", experts="mxfp4"),
            Workload("mxfp4_l256", T=60, d=256, l=256, N=16, K=4, m=256, dtype="bf16", experts="mxfp4")]
 
 
