@@ -3,12 +3,14 @@
 // projection back: 10100.com article, section 2.2).  Latent mode writes s
 // [T, l]; standard mode adds the residual and writes out [T, d] directly.
 //
-// The expert outputs sit in `nsplit` partial planes (the streaming FFN's
-// m-slices; 1 for the tiled FFN) of [T*K, l] each.  `gated`: multiply by the
-// gate here (streaming FFN) or not (the tiled FFN already did).  YT: float
-// (the float32 layer) or f16 times kYScale (the bf16 layer: the streaming
-// FFN's partials, the tiled FFN's gate-scaled outputs; summed as they are,
-// then scaled back once: a power of two, so no extra rounding).
+// PL: the streaming FFN's outputs, `nsplit` partial planes (its m-slices)
+// of [T*K, l] each, multiplied by the gate here; otherwise the tiled FFN's
+// single plane, already gate-scaled.  (A separate instantiation: the plane
+// loop in the rank loop keeps the compiler from batching the ranks' loads.)
+// YT: float (the float32 layer, tiled only) or f16 times kYScale (the bf16
+// layer: the streaming FFN's partials, the tiled FFN's gate-scaled outputs;
+// summed as they are, then scaled back once: a power of two, so no extra
+// rounding).
 // A rank's expert output is at its slot (slot_of, after a dispatch), or at
 // row t*K + k of each plane when the streaming FFN routed itself
 // (self_route).  Zero-computation experts (ids >= n_ffn) have no expert
@@ -49,8 +51,9 @@ __device__ inline void zc_add(const LayerArgs& a, int q, int t, int c0, float g,
 // 4 or 16 for decode-sized batches.  The rank loop is unrolled so the loads
 // of several ranks (and partial planes) are in flight together; no store
 // happens before the last load.
-template <class E, class YT, int RS>
-__global__ __launch_bounds__(256) void combine_kernel(LayerArgs a, int nsplit, int gated) {
+template <class E, class YT, int RS, bool PL>
+__global__ __launch_bounds__(256) void combine_kernel(LayerArgs a, int nsplit) {
+    static_assert(!PL || std::is_same<YT, f16>::value, "the streaming FFN's partials are scaled half precision");
     constexpr int VPC = 16 / (int)sizeof(YT);
     constexpr int IPB = 256 / RS;
     const int cpt = a.l / VPC;
@@ -92,42 +95,30 @@ __global__ __launch_bounds__(256) void combine_kernel(LayerArgs a, int nsplit, i
                 const f32x8 f = __builtin_convertvector(__builtin_bit_cast(f16x8, raw), f32x8);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) part[i] = f[i];
-                // the other planes, loaded 8 at a time before they are added
-                // (in plane order)
-                for (int sp0 = 1; sp0 < nsplit; sp0 += 8) {
-                    uint4 q[8];
+                if constexpr (PL) {
+                    // the other planes, loaded 8 at a time before they are
+                    // added (in plane order)
+                    for (int sp0 = 1; sp0 < nsplit; sp0 += 8) {
+                        uint4 q[8];
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) q[i] = sp0 + i < nsplit ? ldg16(yp + (sp0 + i) * plane) : kZero16;
+                        for (int i = 0; i < 8; ++i)
+                            q[i] = sp0 + i < nsplit ? ldg16(yp + (sp0 + i) * plane) : kZero16;
 #pragma unroll
-                    for (int i = 0; i < 8; ++i)
-                        if (sp0 + i < nsplit) {
-                            const f32x8 g8 = __builtin_convertvector(__builtin_bit_cast(f16x8, q[i]), f32x8);
+                        for (int i = 0; i < 8; ++i)
+                            if (sp0 + i < nsplit) {
+                                const f32x8 g8 = __builtin_convertvector(__builtin_bit_cast(f16x8, q[i]), f32x8);
 #pragma unroll
-                            for (int c = 0; c < 8; ++c) part[c] += g8[c];
-                        }
+                                for (int c = 0; c < 8; ++c) part[c] += g8[c];
+                            }
+                    }
                 }
             } else {
                 part[0] = __uint_as_float(raw.x);
                 part[1] = __uint_as_float(raw.y);
                 part[2] = __uint_as_float(raw.z);
                 part[3] = __uint_as_float(raw.w);
-                // the other planes, loaded 8 at a time before they are added
-                // (in plane order)
-                for (int sp0 = 1; sp0 < nsplit; sp0 += 8) {
-                    uint4 q[8];
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) q[i] = sp0 + i < nsplit ? ldg16(yp + (sp0 + i) * plane) : kZero16;
-#pragma unroll
-                    for (int i = 0; i < 8; ++i)
-                        if (sp0 + i < nsplit) {
-                            part[0] += __uint_as_float(q[i].x);
-                            part[1] += __uint_as_float(q[i].y);
-                            part[2] += __uint_as_float(q[i].z);
-                            part[3] += __uint_as_float(q[i].w);
-                        }
-                }
             }
-            const float gk = gated ? gt[k] : 1.0f;
+            const float gk = PL ? gt[k] : 1.0f;
 #pragma unroll
             for (int i = 0; i < VPC; ++i) acc[i] = fmaf(gk, z ? 0.0f : part[i], acc[i]);
         }

@@ -387,15 +387,15 @@ void launch_g2_tail(LayerArgs a, int nrow_tiles, int ncol_tiles, int ksteps, hip
 }
 
 // Rank groups per combine item: enough threads to fill the GPU.
-template <class E, class YT>
-void launch_combine(const LayerArgs& a, int nsplit, int gated, hipStream_t st) {
+template <class E, class YT, bool PL>
+void launch_combine(const LayerArgs& a, int nsplit, hipStream_t st) {
     const long long items = (long long)a.T * (a.l / (16 / (int)sizeof(YT)));
     if (items >= 131072) {
-        combine_kernel<E, YT, 1><<<(unsigned)((items + 255) / 256), dim3(256), 0, st>>>(a, nsplit, gated);
+        combine_kernel<E, YT, 1, PL><<<(unsigned)((items + 255) / 256), dim3(256), 0, st>>>(a, nsplit);
     } else if (items >= 16384) {
-        combine_kernel<E, YT, 4><<<(unsigned)((items + 63) / 64), dim3(256), 0, st>>>(a, nsplit, gated);
+        combine_kernel<E, YT, 4, PL><<<(unsigned)((items + 63) / 64), dim3(256), 0, st>>>(a, nsplit);
     } else {
-        combine_kernel<E, YT, 16><<<(unsigned)((items + 15) / 16), dim3(256), 0, st>>>(a, nsplit, gated);
+        combine_kernel<E, YT, 16, PL><<<(unsigned)((items + 15) / 16), dim3(256), 0, st>>>(a, nsplit);
     }
 }
 
@@ -585,11 +585,11 @@ hipError_t launch_all(const Plan& p, LayerArgs& a, hipStream_t st, void* const* 
     mark(5);
     if constexpr (sizeof(E) == 2) {
         if (p.path == LMOE_PATH_STREAM)
-            launch_combine<E, f16>(a, p.nsplit, 1, st);   // the streaming FFN's fp16 partials
+            launch_combine<E, f16, true>(a, p.nsplit, st);   // the streaming FFN's fp16 partials
         else
-            launch_combine<E, YT>(a, 1, 0, st);
+            launch_combine<E, YT, false>(a, 1, st);
     } else {
-        launch_combine<E, YT>(a, 1, 0, st);   // (the float32 layer has no streaming path)
+        launch_combine<E, YT, false>(a, 1, st);   // (the float32 layer has no streaming path)
     }
     // 6. back to d with the residual
     mark(6);

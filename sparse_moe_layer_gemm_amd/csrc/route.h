@@ -6,7 +6,8 @@
 // register, find the K-th largest key tau exactly; the selection is every
 // key > tau plus the lowest-index keys == tau, which is exactly the first K
 // in (larger logit, then lower expert index) order.  The K winners are
-// compacted through LDS and each ranks itself against the others.  The gates
+// compacted through LDS and each ranks itself against the others
+// (reading them back 8 at a time).  The gates
 // are the softmax over the K selected logits, which equals the full softmax
 // renormalised over them.
 //
@@ -50,7 +51,7 @@ constexpr int kMaxSplit = 16;
 
 // Top-K of token t by one wavefront, from its N logits at lg (global
 // memory or LDS).  s_key / s_idx / s_val: 64 entries of LDS private to the
-// calling wave.
+// calling wave (s_key and s_idx 16-byte aligned).
 template <int NPL>
 __device__ inline void topk_token(const LayerArgs& a, int t, const float* lg, uint32_t* s_key, int* s_idx,
                                   float* s_val) {
@@ -83,6 +84,11 @@ __device__ inline void topk_token(const LayerArgs& a, int t, const float* lg, ui
     const int need = K - gt;  // keys equal to tau still to take, lowest index first
     const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     int eq_seen = 0, base = 0;
+    // entries past the K winners: key 0, below every real key (the ranking
+    // below reads the first multiple of 8 entries)
+    s_key[lane] = 0u;
+    s_idx[lane] = 0x7fffffff;
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int j = 0; j < NPL; ++j) {
         const bool eq = key[j] == tau;
@@ -101,8 +107,9 @@ __device__ inline void topk_token(const LayerArgs& a, int t, const float* lg, ui
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // winner `lane` ranks itself against the others, whose keys and indices
-    // it reads from their lanes (v_readlane: no LDS round trip per winner)
+    // winner `lane` ranks itself against all K winners, reading their keys
+    // and indices 8 at a time (the same LDS address in every lane: one
+    // broadcast read each, all of a batch in flight together)
     float my_v = -INFINITY;
     uint32_t mk = 0u;
     int my_rank = 0, my_idx = 0;
@@ -111,10 +118,15 @@ __device__ inline void topk_token(const LayerArgs& a, int t, const float* lg, ui
         my_idx = s_idx[lane];
         my_v = s_val[lane];
     }
-    for (int q = 0; q < K; ++q) {
-        const uint32_t qk = __builtin_amdgcn_readlane(mk, q);
-        const int qi = __builtin_amdgcn_readlane(my_idx, q);
-        my_rank += (qk > mk || (qk == mk && qi < my_idx)) ? 1 : 0;
+    for (int q0 = 0; q0 < K; q0 += 8) {
+        const uint4 ka = *reinterpret_cast<const uint4*>(s_key + q0);
+        const uint4 kb = *reinterpret_cast<const uint4*>(s_key + q0 + 4);
+        const int4 ia = *reinterpret_cast<const int4*>(s_idx + q0);
+        const int4 ib = *reinterpret_cast<const int4*>(s_idx + q0 + 4);
+        const uint32_t qk[8] = {ka.x, ka.y, ka.z, ka.w, kb.x, kb.y, kb.z, kb.w};
+        const int qi[8] = {ia.x, ia.y, ia.z, ia.w, ib.x, ib.y, ib.z, ib.w};
+#pragma unroll
+        for (int u = 0; u < 8; ++u) my_rank += (qk[u] > mk || (qk[u] == mk && qi[u] < my_idx)) ? 1 : 0;
     }
     float mx = my_v;
 #pragma unroll
@@ -134,8 +146,8 @@ template <int NPL>
 __global__ __launch_bounds__(256) void topk_kernel(LayerArgs a) {
     const int wave = threadIdx.x >> 6;
     const int t = blockIdx.x * 4 + wave;
-    __shared__ uint32_t s_key[4][64];
-    __shared__ int s_idx[4][64];
+    __shared__ __align__(16) uint32_t s_key[4][64];
+    __shared__ __align__(16) int s_idx[4][64];
     __shared__ float s_val[4][64];
     if (t >= a.T) return;
     topk_token<NPL>(a, t, a.logits + (size_t)t * a.N, s_key[wave], s_idx[wave], s_val[wave]);
@@ -150,8 +162,8 @@ template <int NPL>
 __global__ __launch_bounds__(256) void topk_part_kernel(LayerArgs a, PartIn pin) {
     const int t = blockIdx.x;
     __shared__ float lg[64 * NPL];
-    __shared__ uint32_t s_key[64];
-    __shared__ int s_idx[64];
+    __shared__ __align__(16) uint32_t s_key[64];
+    __shared__ __align__(16) int s_idx[64];
     __shared__ float s_val[64];
     const size_t ps = (size_t)a.T * pin.stride;
     const float* pt = pin.part + (size_t)t * pin.stride;
