@@ -74,6 +74,47 @@ __global__ __launch_bounds__(256) void combine_kernel(LayerArgs a, int nsplit) {
         const int nf = has_zc && !a.self_route ? a.offsets[a.n_ffn] : INT_MAX;   // FFN slots: [0, nf)
         const size_t zrow = (size_t)a.T * a.K;
         unsigned long long zranks = 0;   // ranks of zero-computation experts (K <= 64)
+        if constexpr (!PL) {
+            // (after a dispatch) the slots of a batch of 8 ranks are loaded
+            // first, then their outputs: loads that alternated with the
+            // slot loads would each wait for all the loads before them.
+            // Ranks past K take the last rank's row (a cached re-read) and
+            // are not added.
+            constexpr int B = 8;
+            for (int k0 = g; k0 < a.K; k0 += RS * B) {
+                size_t row[B];
+                bool z[B];
+#pragma unroll
+                for (int u = 0; u < B; ++u) {
+                    const int sl = so[min(k0 + u * RS, a.K - 1)];
+                    z[u] = sl >= nf;
+                    row[u] = z[u] ? zrow : (size_t)sl;
+                }
+                uint4 raw[B];
+#pragma unroll
+                for (int u = 0; u < B; ++u) raw[u] = ldg16(Y + row[u] * a.l);
+#pragma unroll
+                for (int u = 0; u < B; ++u) {
+                    const int k = k0 + u * RS;
+                    if (k < a.K) {
+                        zranks |= (unsigned long long)z[u] << k;
+                        float part[VPC];
+                        if constexpr (VPC == 8) {
+                            const f32x8 f = __builtin_convertvector(__builtin_bit_cast(f16x8, raw[u]), f32x8);
+#pragma unroll
+                            for (int i = 0; i < 8; ++i) part[i] = f[i];
+                        } else {
+                            part[0] = __uint_as_float(raw[u].x);
+                            part[1] = __uint_as_float(raw[u].y);
+                            part[2] = __uint_as_float(raw[u].z);
+                            part[3] = __uint_as_float(raw[u].w);
+                        }
+#pragma unroll
+                        for (int i = 0; i < VPC; ++i) acc[i] += z[u] ? 0.0f : part[i];
+                    }
+                }
+            }
+        } else
 #pragma unroll 4
         for (int k = g; k < a.K; k += RS) {
             size_t row;
