@@ -92,14 +92,19 @@ constexpr int kStreamMaxMeanRows = 16;
 // or 256 (bf16, FP8, and MXFP4 experts with l % 256 == 0, which take
 // ffn_stream_mx_kernel) when the expected (active expert, slice)
 // workgroups under uniform routing number at least kWideSliceMinWgs (four
-// per CU) and the active experts average at most kWideSliceMaxRows rows.
+// per CU) and the active experts average at most kWideSliceMaxRows rows
+// (one 16-row pass, as a rule), or when the 256-wide workgroups fill most
+// of one round of the GPU's kOneRoundWgs (two per CU), which the 128-wide
+// ones would overflow (decode at 8 tokens: 462 against 924).
 // Wider slices halve the partial planes (the FFN's stores, the
 // combine's reads) but also the workgroups that stream the weights.  With
 // bf16 experts and fewer than kNarrowSliceMaxWgs such workgroups at 128
 // (a few tokens on few, large experts) the slice is 64 wide: twice the
 // workgroups, each streaming half as much.
 constexpr double kWideSliceMinWgs = 1024;
-constexpr double kWideSliceMaxRows = 8;
+constexpr double kWideSliceMaxRows = 16;
+constexpr double kOneRoundWgs = 512;
+constexpr double kOneRoundMinFill = 0.8;
 constexpr double kNarrowSliceMaxWgs = 128;
 
 struct Plan {
@@ -209,8 +214,10 @@ Plan make_plan(const lmoe_dims* dm, int32_t K) {
         p.ms = (d.m % 128 == 0) ? 128 : 64;
         const double ffn_slots = (double)TK * d.N / p.nr;   // routed rows of FFN experts
         const double active = d.N * (1.0 - std::pow(1.0 - (double)K / p.nr, (double)d.T));   // expected
-        if ((p.wfmt <= 1 || d.l % 256 == 0) && d.m % 256 == 0 && active * (d.m / 256) >= kWideSliceMinWgs &&
-            ffn_slots <= kWideSliceMaxRows * active)
+        const double wide_wgs = active * (d.m / 256);
+        const bool many = wide_wgs >= kWideSliceMinWgs && ffn_slots <= kWideSliceMaxRows * active;
+        const bool one_round = wide_wgs >= kOneRoundMinFill * kOneRoundWgs && wide_wgs <= kOneRoundWgs;
+        if ((p.wfmt <= 1 || d.l % 256 == 0) && d.m % 256 == 0 && (many || one_round))
             p.ms = 256;
         else if (p.wfmt == 0 && p.ms == 128 && active * (d.m / 128) < kNarrowSliceMaxWgs)
             p.ms = 64;

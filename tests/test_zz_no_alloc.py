@@ -65,7 +65,7 @@ def test_noalloc_tiled_path_twice():
 
 
 def test_noalloc_rejects_dims_beyond_its_scratch():
-    w = WORKLOADS["decode"].replace(T=256)
+    w = WORKLOADS["decode"].replace(T=1024)   # a workspace of ~107 MiB
     d = P.to_device(make_inputs(w.replace(T=1), 35))
     dims = B.dims_for(d, w.K)
     dims.T = w.T
