@@ -100,7 +100,7 @@ def test_full_size_every_token(full_run, name, chunk):
 # (x = the first T rows of one draw; the path and kernels change with T: the
 # split skinny projection up to 64 tokens, the tiled projection above)
 
-SWEEP_T = [1, 2, 4, 8, 16, 64, 128, 256]
+SWEEP_T = [1, 2, 4, 8, 16, 64, 128, 192, 256]
 
 
 @pytest.fixture(scope="module")
@@ -123,15 +123,16 @@ def test_standard_decode_batch_sweep(T):
 
 
 # FP8 and MXFP4 experts across the batch sizes where the decode FFN's m-slice
-# changes: 128 wide at T = 16, 256 wide at T = 64 and 128 (one draw per
-# format, x = its first T rows)
+# changes: 256 wide at T = 8 (the workgroups fill one round of the GPU), 128
+# wide at T = 16, 256 wide at T = 64 and 128 (one draw per format, x = its
+# first T rows)
 @pytest.fixture(scope="module", params=["fp8", "mxfp4"])
 def sweep_low_precision(request):
     w = WORKLOADS[f"decode_{request.param}"].replace(T=128)
     return w, make_inputs(w, 9)
 
 
-@pytest.mark.parametrize("T", [16, 64, 128])
+@pytest.mark.parametrize("T", [8, 16, 64, 128])
 def test_low_precision_decode_batch_sweep(sweep_low_precision, T):
     w0, inp = sweep_low_precision
     w = w0.replace(name=f"{w0.name}_T{T}", T=T)
