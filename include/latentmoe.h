@@ -231,7 +231,7 @@ int latentmoe_forward_ex(const lmoe_args* args, int32_t K, const lmoe_dims* dims
  * until the process ends; the call allocates nothing.  Dims whose
  * latentmoe_workspace_bytes() exceeds that size are rejected with
  * LMOE_EUNSUPPORTED (at d = 4096, l = 1024, 512 experts, top-22 that is
- * T > 128).  Every call on one device uses the same array and leaves the
+ * T > 600).  Every call on one device uses the same array and leaves the
  * last call's routing data in it: calls that may overlap on one device --
  * on two streams, or from two threads -- race and must be serialised by
  * the caller.  Arguments, results, errors and the stream rules are those of
