@@ -16,10 +16,14 @@
 // and a per-column bias, applied in the store layout).
 //
 // Pipeline: global -> registers two k-tiles ahead, registers -> LDS one
-// k-tile ahead (two LDS buffers).  In MFMA groups 0 and 1 of a k-tile,
-// group g writes parts 2g and 2g+1 of the next k-tile to LDS and then loads
-// the same parts of the k-tile after it into the freed registers, so each
-// load is at least two groups old when the next k-tile starts.
+// k-tile ahead (two LDS buffers).  A k-tile is four MFMA groups (16 deep
+// each); group q writes part q of the next k-tile to LDS and then loads
+// part q of the k-tile after it into the freed registers, so every group
+// carries the same LDS work (fragment reads plus a quarter of the staging
+// writes) beside its MFMAs.  Within a group the MFMAs are interleaved with
+// the LDS reads (two per MFMA) and then the writes and loads
+// (sched_group_barrier), so each wave keeps the matrix cores and the LDS
+// busy at once instead of alternating between them.
 //
 // LDS rows are 64 bf16 = 8 units of 16 bytes; unit c of row r is stored at
 // c ^ sw(r), sw(r) = (r & 7) ^ ((r >> 3) & 1).  A 16-byte fragment read
@@ -431,16 +435,23 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm2_kernel(LayerArgs a, int 
     BStage rb[S::LB];
     // Staged loads are split in 4 parts (load index i belongs to part i % 4),
     // so that part q of the next k-step can go to LDS, and part q of the
-    // k-step after it can be loaded, right after MFMA group q.
+    // k-step after it can be loaded, in MFMA group q.
     auto in_part = [](int i, int n, int q) { return n >= 4 ? (i % 4 == q) : (q == 0); };
-    auto gload_group = [&](int g) {
+    // loads of the parts in `mask` (bit q: part q)
+    auto gload_parts = [&](int mask) {
+        auto in_mask = [&](int i, int n) {
+            bool r = false;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) r = r || (((mask >> q) & 1) && in_part(i, n, q));
+            return r;
+        };
         const int k0 = lkt * kG2K;
 #pragma unroll
         for (int i = 0; i < S::LA; ++i)
-            if (in_part(i, S::LA, 2 * g) || in_part(i, S::LA, 2 * g + 1)) ra[i] = ldg16(ap[i] + k0);
+            if (in_mask(i, S::LA)) ra[i] = ldg16(ap[i] + k0);
 #pragma unroll
         for (int i = 0; i < S::LB; ++i)
-            if (in_part(i, S::LB, 2 * g) || in_part(i, S::LB, 2 * g + 1)) {
+            if (in_mask(i, S::LB)) {
                 if constexpr (kFmt == 2) {
                     const uint32_t o = bo[i] + k0 / 2;
                     rb[i] = uint2{ldg4(xc + o), ldg1(xs + (o >> 4))};
@@ -487,14 +498,12 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm2_kernel(LayerArgs a, int 
     zero_acc();
 
     // prologue: k-step 0 into stage 0, k-step 1 into the registers
-    gload_group(0);
-    gload_group(1);
+    gload_parts(15);
     advance_load();
 #pragma unroll
     for (int q = 0; q < 4; ++q) swrite_part(0, q);
     __syncthreads();
-    gload_group(0);
-    gload_group(1);
+    gload_parts(15);
     advance_load();
 
     // Fragments of MFMA group kk+1 are read from LDS before the MFMAs of
@@ -701,29 +710,60 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm2_kernel(LayerArgs a, int 
         __syncthreads();  // the stage is free for the k-step after next
     };
 
+    // One barrier per k-step, in the last MFMA group: by then every wave
+    // has written the next k-step to the other stage (parts 0-2 in groups
+    // 0-2, part 3 just before the barrier) and read its last fragments of
+    // this stage (in group 2).  After the barrier group 3 reads the next
+    // k-step's first fragments from the other stage, so the next k-step
+    // starts its MFMAs without waiting for the LDS.  After a tile's last
+    // k-step those fragments are read again after the epilogue (which uses
+    // only this stage), so that no fragment is live across the epilogue.
+    bf16x8 a0[S::FM], b0[S::FN], a1[S::FM], b1[S::FN];
+    read_frags(0, 0, a0, b0);
     for (int step = 0, ckt = 0;; ++step) {
         const int st = step & 1;
-        bf16x8 a0[S::FM], b0[S::FN], a1[S::FM], b1[S::FN];
-        read_frags(st, 0, a0, b0);
 #pragma unroll
         for (int kk = 0; kk < kG2K / 16; ++kk) {
             bf16x8* ac = (kk & 1) ? a1 : a0;
             bf16x8* bc = (kk & 1) ? b1 : b0;
             bf16x8* an = (kk & 1) ? a0 : a1;
             bf16x8* bn = (kk & 1) ? b0 : b1;
-            if (kk + 1 < kG2K / 16) read_frags(st, kk + 1, an, bn);
-            if (kk < 2) {
-                // parts 2kk, 2kk+1 of the next k-step go to LDS, then the
-                // same registers take parts 2kk, 2kk+1 of the k-step after
-                swrite_part(st ^ 1, 2 * kk);
-                swrite_part(st ^ 1, 2 * kk + 1);
-                gload_group(kk);
+            // part kk of the next k-step goes to LDS, then the same
+            // registers take part kk of the k-step after
+            if (kk + 1 < kG2K / 16) {
+                read_frags(st, kk + 1, an, bn);
+                swrite_part(st ^ 1, kk);
+                gload_parts(1 << kk);
+            } else {
+                swrite_part(st ^ 1, kk);
+                gload_parts(1 << kk);
+                __syncthreads();
+                read_frags(st ^ 1, 0, an, bn);
             }
             mfma_group(ac, bc);
+            // Issue order of the group: each MFMA followed by two fragment
+            // reads until they are all issued, then by one staging write and
+            // one global load (masks: 0x008 MFMA, 0x100 LDS read, 0x200 LDS
+            // write, 0x020 global load).  Group 3's write and load sit before
+            // its barrier, outside this region.
+            {
+                constexpr int NM = S::FM * S::FN, NR = S::FM + S::FN;
+#pragma unroll
+                for (int i = 0; i < NM; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if (2 * i + 1 < NR) {
+                        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                    } else if (2 * i < NR) {
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    } else if (kk < 3) {
+                        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                    }
+                }
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
         advance_load();
-        __syncthreads();
         if (++ckt == nk) {
             epilogue(st);
             cslot += nslot;
@@ -731,6 +771,7 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm2_kernel(LayerArgs a, int 
             ckt = 0;
             zero_acc();
             tile_loads();
+            read_frags(st ^ 1, 0, a0, b0);   // the next tile's first k-step
         }
     }
 }
