@@ -506,7 +506,7 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm2_kernel(LayerArgs a, int 
     gload_parts(15);
     advance_load();
 
-    // Fragments of MFMA group kk+1 are read from LDS before the MFMAs of
+    // Fragments of MFMA group kk+1 are read from LDS while the MFMAs of
     // group kk are issued (two register sets), so LDS latency overlaps them.
     auto read_frags = [&](int st, int kk, bf16x8* af, bf16x8* bfr) {
         const int chunk = kk * 2 + (lane >> 5);
