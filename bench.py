@@ -114,7 +114,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; the layer is not sharded "
-                                   "across GPUs (see DESIGN.md for how it would shard)",
+                                   "across GPUs",
                           "n_gpus_requested": max(args.gpus, world)}), flush=True)
         sys.exit(2)
 
