@@ -90,7 +90,7 @@ def test_dispatch_written_flag(lib):
 
 @pytest.mark.parametrize("field,value,K", [
     ("T", 0, 4), ("d", 100, 4), ("l", 0, 4), ("m", 65, 4), ("N", 0, 4), ("N", 4096, 4),
-    ("dtype", 7, 4), ("path", 9, 4), ("m_shared", 96, 4), ("m_shared", -64, 4),
+    ("dtype", 7, 4), ("path", 9, 4), ("m_shared", 96, 4), ("m_shared", -64, 4), ("T", (1 << 24) + 1, 4),
     (None, None, 0), (None, None, 33), (None, None, 65),
 ])
 def test_invalid_dims_rejected(lib, field, value, K):
@@ -285,6 +285,35 @@ def test_zero_computation_argument_checks(lib):
     assert B.latentmoe_workspace_bytes(dims_of(small), 20) > 0
     assert B.latentmoe_workspace_bytes(dims_of(small), 21) == 0
     assert call_ex(d, w.K, zc_const=ZC, workspace_bytes=64, **nofp8) == B.LMOE_EWORKSPACE
+
+
+def test_entry_point_option_checks(lib):
+    """Each entry point other than latentmoe_forward_ex rejects the options it
+    does not take before touching the device; the no-allocation entry point
+    rejects dims whose workspace exceeds its static scratch."""
+    P = ctypes.c_void_p
+    w = WORKLOADS["decode"]
+    ptrs = [P(FAKE + (i << 30)) for i in range(6)]
+    out = P(FAKE + (6 << 30))
+
+    def noalloc(d, K=w.K):
+        return B.lib().latentmoe_forward_noalloc(*ptrs, K, out, ctypes.byref(d), None, None, None, None)
+
+    big = dims_of(w.replace(T=1024))
+    assert B.latentmoe_workspace_bytes(big, w.K) > B.NOALLOC_SCRATCH_BYTES
+    assert noalloc(big) == B.LMOE_EUNSUPPORTED and "latentmoe_forward_noalloc" in B.latentmoe_last_error()
+    assert noalloc(dims_of(w.replace(m_shared=64))) == B.LMOE_EINVAL
+    assert "latentmoe_forward_shared" in B.latentmoe_last_error()
+    assert noalloc(dims_of(WORKLOADS["decode_fp8"])) == B.LMOE_EINVAL
+    assert noalloc(dims_of(WORKLOADS["decode_zc"])) == B.LMOE_EINVAL
+    assert noalloc(dims_of(w), K=0) == B.LMOE_EINVAL
+    assert call_shared(dims_of(w), w.K) == B.LMOE_EINVAL                  # m_shared = 0
+    assert "m_shared > 0" in B.latentmoe_last_error()
+    d = dims_of(w)
+    rc = B.lib().latentmoe_forward_timed(*ptrs, None, None, w.K, out, ctypes.byref(d), None, None, None,
+                                         P(FAKE + (7 << 30)), ctypes.c_size_t(B.latentmoe_workspace_bytes(d, w.K)),
+                                         None, None)
+    assert rc == B.LMOE_EINVAL and "events" in B.latentmoe_last_error()
 
 
 def test_status_strings(lib):
